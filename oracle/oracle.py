@@ -1,0 +1,146 @@
+"""ctypes wrapper of liboracle.so (built from haste_oracle.c with gcc).
+
+Test infrastructure only.  Every function takes numpy arrays: bf16 tensors as
+uint16 bit patterns, index sets and labels as int32, and returns fp64 numpy
+arrays.  Shapes are checked here; the C code assumes them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "haste_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2, IEEE fp64, OpenMP)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *extra_flags, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) and declare the C signatures."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if not os.path.exists(p) or (path is None and os.path.getmtime(p) < os.path.getmtime(_SRC)):
+        build(out=p)
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    for name in ("oracle_fwd", "oracle_bwd_w", "oracle_bwd_w_f64", "oracle_bwd_h", "oracle_bwd_h_f64"):
+        getattr(lib, name).argtypes = [P, P, P, P, I, I, I, I, I]
+        getattr(lib, name).restype = None
+    lib.oracle_bce.argtypes = [P, I, I, P, P, ctypes.c_double, P, P]
+    lib.oracle_bce.restype = None
+    lib.oracle_step.argtypes = [P, P, P, P, P, ctypes.c_double, P, P, P, P, P, I, I, I, I, I]
+    lib.oracle_step.restype = None
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(name, a, dtype, shape):
+    if a.dtype != dtype or not a.flags.c_contiguous or tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected C-contiguous {np.dtype(dtype)} {tuple(shape)}, "
+                         f"got {a.dtype} {a.shape}")
+
+
+def _dims(idx, G, h=None, B=None, H=None):
+    K, F = idx.shape
+    return K, F, K * G
+
+
+def oracle_fwd(h, idx, W, G, lib=None):
+    """Z (B x L fp64) = forward logits."""
+    lib = lib or load()
+    B, H = h.shape
+    K, F, L = _dims(idx, G)
+    _check("h", h, np.uint16, (B, H)); _check("idx", idx, np.int32, (K, F)); _check("W", W, np.uint16, (L, F))
+    Z = np.empty((B, L), dtype=np.float64)
+    lib.oracle_fwd(_p(h), _p(idx), _p(W), _p(Z), B, H, K, G, F)
+    return Z
+
+
+def oracle_bwd_w(h, idx, dZ, G, lib=None):
+    """dW (L x F fp64).  dZ is bf16 bits (uint16) or fp64."""
+    lib = lib or load()
+    B, H = h.shape
+    K, F, L = _dims(idx, G)
+    _check("h", h, np.uint16, (B, H)); _check("idx", idx, np.int32, (K, F))
+    dW = np.empty((L, F), dtype=np.float64)
+    if dZ.dtype == np.float64:
+        _check("dZ", dZ, np.float64, (B, L))
+        lib.oracle_bwd_w_f64(_p(h), _p(idx), _p(dZ), _p(dW), B, H, K, G, F)
+    else:
+        _check("dZ", dZ, np.uint16, (B, L))
+        lib.oracle_bwd_w(_p(h), _p(idx), _p(dZ), _p(dW), B, H, K, G, F)
+    return dW
+
+
+def oracle_bwd_h(dZ, idx, W, G, H, lib=None):
+    """dh (B x H fp64).  dZ is bf16 bits (uint16) or fp64."""
+    lib = lib or load()
+    B = dZ.shape[0]
+    K, F, L = _dims(idx, G)
+    _check("idx", idx, np.int32, (K, F)); _check("W", W, np.uint16, (L, F))
+    dh = np.empty((B, H), dtype=np.float64)
+    if dZ.dtype == np.float64:
+        _check("dZ", dZ, np.float64, (B, L))
+        lib.oracle_bwd_h_f64(_p(dZ), _p(idx), _p(W), _p(dh), B, H, K, G, F)
+    else:
+        _check("dZ", dZ, np.uint16, (B, L))
+        lib.oracle_bwd_h(_p(dZ), _p(idx), _p(W), _p(dh), B, H, K, G, F)
+    return dh
+
+
+def oracle_bce(Z, y_rowptr, y_col, scale, lib=None):
+    """(dZ fp64 B x L, loss float) of BCE(sigmoid(Z), Y) with Y from CSR."""
+    lib = lib or load()
+    B, L = Z.shape
+    _check("Z", Z, np.float64, (B, L))
+    _check("y_rowptr", y_rowptr, np.int32, (B + 1,))
+    _check("y_col", y_col, np.int32, (int(y_rowptr[-1]),))
+    if y_col.size and (y_col.min() < 0 or y_col.max() >= L):
+        raise ValueError("label id out of range")
+    dZ = np.empty((B, L), dtype=np.float64)
+    loss = np.zeros(1, dtype=np.float64)
+    lib.oracle_bce(_p(Z), B, L, _p(y_rowptr), _p(y_col), float(scale), _p(dZ), _p(loss))
+    return dZ, float(loss[0])
+
+
+def oracle_step(h, idx, W, y_rowptr, y_col, scale, G, want_dW=True, want_dh=True, lib=None):
+    """Full training pass: returns dict with Z, dZ (fp64), dW, dh, loss."""
+    lib = lib or load()
+    B, H = h.shape
+    K, F, L = _dims(idx, G)
+    _check("h", h, np.uint16, (B, H)); _check("idx", idx, np.int32, (K, F)); _check("W", W, np.uint16, (L, F))
+    _check("y_rowptr", y_rowptr, np.int32, (B + 1,))
+    _check("y_col", y_col, np.int32, (int(y_rowptr[-1]),))
+    if y_col.size and (y_col.min() < 0 or y_col.max() >= L):
+        raise ValueError("label id out of range")
+    Z = np.empty((B, L), dtype=np.float64)
+    dZ = np.empty((B, L), dtype=np.float64)
+    dW = np.empty((L, F), dtype=np.float64) if want_dW else None
+    dh = np.empty((B, H), dtype=np.float64) if want_dh else None
+    loss = np.zeros(1, dtype=np.float64)
+    lib.oracle_step(_p(h), _p(idx), _p(W), _p(y_rowptr), _p(y_col), float(scale),
+                    _p(Z), _p(dZ), _p(dW), _p(dh), _p(loss), B, H, K, G, F)
+    return {"Z": Z, "dZ": dZ, "dW": dW, "dh": dh, "loss": float(loss[0])}

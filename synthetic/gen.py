@@ -1,0 +1,150 @@
+"""Seeded input generators (no layer arithmetic lives here).
+
+Every tensor is drawn from ``np.random.SeedSequence([seed_no, tensor_no,
+chunk])`` so the result does not depend on the number of worker threads.
+Tensor numbers: 0 group index sets, 1 features h, 2 weights W, 3 upstream
+gradient dZ, 4 label-rank permutation, 5 positive labels, 6 per-label index
+sets of the G=1 fixed fan-in baseline.
+
+bf16 values are carried as their uint16 bit patterns, rounded from float32
+to nearest with ties to even.
+"""
+
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+T_IDX, T_H, T_W, T_DZ, T_PERM, T_POS, T_IDX1 = range(7)
+
+_CHUNK = 1 << 22  # elements per independently seeded chunk
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _rng(seed_no: int, tensor_no: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed_no, tensor_no, chunk]))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if np.any((u & 0x7F800000) == 0x7F800000):
+        raise ValueError("bf16_bits: NaN/Inf inputs are not generated here")
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_value(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact widening)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(n: int, std: float, seed_no: int, tensor_no: int) -> np.ndarray:
+    """n draws of N(0, std^2), rounded to bf16 bit patterns."""
+    out = np.empty(n, dtype=np.uint16)
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def work(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        x = _rng(seed_no, tensor_no, c).standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[lo:hi] = bf16_bits(x)
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def sorted_subsets(rows: int, F: int, H: int, seed_no: int, tensor_no: int = T_IDX) -> np.ndarray:
+    """rows x F int32: each row an F-subset of [0, H) drawn uniformly without
+    replacement, sorted ascending.
+
+    Draw H random 53-bit keys per row, keep the F columns with the smallest
+    keys (a uniformly random F-subset), then sort the kept column ids.
+    """
+    if not (0 < F <= H <= 1024):
+        raise ValueError("need 0 < F <= H <= 1024")
+    out = np.empty((rows, F), dtype=np.int32)
+    per = max(1, _CHUNK // H)
+    nchunks = (rows + per - 1) // per
+    col = np.arange(H, dtype=np.uint64)
+
+    def work(c):
+        lo, hi = c * per, min(rows, (c + 1) * per)
+        keys = _rng(seed_no, tensor_no, c).integers(0, 2**63, size=(hi - lo, H), dtype=np.int64)
+        keys = ((keys.view(np.uint64) >> np.uint64(10)) << np.uint64(10)) | col
+        if F < H:
+            keys = np.partition(keys, F - 1, axis=1)[:, :F]
+        out[lo:hi] = np.sort((keys & np.uint64(1023)).astype(np.int32), axis=1)
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def zipf_labels(B: int, L: int, m: int, seed_no: int, s: float = 1.1):
+    """0/1 label matrix B x L as CSR (rowptr int32 [B+1], col int32 [B*m]).
+
+    Every sample gets exactly m distinct labels.  A label is drawn by rank r
+    from a Zipf(s) law truncated at L (p(r) proportional to r^-s, inverse-CDF
+    sampling), duplicates are redrawn, and rank r maps to label id perm[r-1]
+    for a seeded permutation perm of [0, L).  Column ids are sorted within a
+    row.
+    """
+    if m > L:
+        raise ValueError("m > L")
+    ranks = np.arange(1, L + 1, dtype=np.float64)
+    cdf = np.cumsum(ranks ** (-s))
+    cdf /= cdf[-1]
+    perm = _rng(seed_no, T_PERM).permutation(L).astype(np.int64)
+    rng = _rng(seed_no, T_POS)
+    rowptr = np.arange(B + 1, dtype=np.int64) * m
+    col = np.empty(B * m, dtype=np.int32)
+    for b in range(B):
+        chosen: list[int] = []
+        seen: set[int] = set()
+        while len(chosen) < m:
+            u = rng.random(2 * m)
+            r = np.minimum(np.searchsorted(cdf, u, side="right"), L - 1)
+            for x in r.tolist():
+                if x not in seen:
+                    seen.add(x)
+                    chosen.append(x)
+                    if len(chosen) == m:
+                        break
+        col[b * m:(b + 1) * m] = np.sort(perm[np.asarray(chosen)])
+    return rowptr.astype(np.int32), col
+
+
+def make_inputs(w, *, dZ: bool = True, labels: bool = True, idx1: bool = False) -> dict:
+    """All inputs of one workload `w` (a synthetic.configs.Workload).
+
+    Returns a dict of numpy arrays: idx (K x F int32), h (B x H bf16 bits),
+    W (L x F bf16 bits), optionally dZ (B x L bf16 bits), y_rowptr / y_col
+    (CSR 0/1 labels) and idx1 (L x F int32 per-label index sets for the G=1
+    baseline).
+    """
+    out = {
+        "idx": sorted_subsets(w.K, w.F, w.H, w.seed_no, T_IDX),
+        "h": normal_bf16(w.B * w.H, 1.0, w.seed_no, T_H).reshape(w.B, w.H),
+        "W": normal_bf16(w.L * w.F, float(1.0 / np.sqrt(w.F)), w.seed_no, T_W).reshape(w.L, w.F),
+    }
+    if dZ:
+        out["dZ"] = normal_bf16(w.B * w.L, 1.0, w.seed_no, T_DZ).reshape(w.B, w.L)
+    if labels:
+        out["y_rowptr"], out["y_col"] = zipf_labels(w.B, w.L, w.m, w.seed_no, w.zipf_s)
+    if idx1:
+        out["idx1"] = sorted_subsets(w.L, w.F, w.H, w.seed_no, T_IDX1)
+    return out

@@ -1,0 +1,306 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each pin_* function takes a loaded oracle library (ctypes) and raises
+AssertionError when the oracle disagrees with the fact it checks.  The pins
+are used twice: once on the real oracle (test_oracle_pins.py) and once on
+copies of the oracle with a planted mistake (test_oracle_mutants.py), which
+must each fail at least one pin.
+
+What pins what:
+  hand examples (tests/golden)  fwd, bwd_w, bwd_h, bce, loss: values computed by hand
+  dense special case F=H        fwd, bwd_w, bwd_h == numpy matmul
+  brute-force masked dense      fwd, bwd_w, bwd_h via an L x H matrix with zeros
+  one-hot probes                index handling, exact
+  all-ones integer case         closed forms Z=F, dW=B, dh=G*count(j)
+  finite differences            bwd_w, bwd_h == exact differences of <dZ, fwd>
+  permutation invariance        group order and slot order conventions
+  torch autograd                dZ, dW, dh, loss == autograd of forward+BCE
+  BCE closed form (W = 0)       dZ = s(1/2 - Y), loss = s*B*L*ln 2
+  G=1 special case              per-label fixed fan-in dot products
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import oracle as O
+from synthetic import bf16_bits, bf16_value, normal_bf16, sorted_subsets
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+EXACT = 0.0
+
+
+def _f(bits):
+    return bf16_value(bits).astype(np.float64)
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.abs(a - b)
+    ok = err <= atol + rtol * np.abs(b)
+    assert ok.all(), f"{what}: max abs err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
+def _rand_case(B, H, K, G, F, seed):
+    h = normal_bf16(B * H, 1.0, seed, 1).reshape(B, H)
+    W = normal_bf16(K * G * F, 0.5, seed, 2).reshape(K * G, F)
+    dZ = normal_bf16(B * K * G, 1.0, seed, 3).reshape(B, K * G)
+    idx = sorted_subsets(K, F, H, seed, 0)
+    return h, idx, W, dZ
+
+
+def _small_int_bf16(shape, rng, lo=-3, hi=4):
+    return bf16_bits(rng.integers(lo, hi, size=shape).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+
+def pin_hand_example(lib):
+    with open(os.path.join(GOLDEN, "hand_example_b2_h4_k2_g2_f2.json")) as fh:
+        g = json.load(fh)
+    s = g["shape"]
+    h = bf16_bits(np.array(g["h"], np.float32))
+    W = bf16_bits(np.array(g["W"], np.float32))
+    dZ = bf16_bits(np.array(g["dZ"], np.float32))
+    idx = np.array(g["idx"], np.int32)
+    Z = O.oracle_fwd(h, idx, W, s["G"], lib=lib)
+    dW = O.oracle_bwd_w(h, idx, dZ, s["G"], lib=lib)
+    dh = O.oracle_bwd_h(dZ, idx, W, s["G"], s["H"], lib=lib)
+    _close(Z, g["Z"], 0, EXACT, "hand Z")
+    _close(dW, g["dW"], 0, EXACT, "hand dW")
+    _close(dh, g["dh"], 0, EXACT, "hand dh")
+
+
+def pin_bce_hand_example(lib):
+    with open(os.path.join(GOLDEN, "bce_hand_example_b2_l2.json")) as fh:
+        g = json.load(fh)
+    Z = np.array(g["Z"], np.float64)
+    dZ, loss = O.oracle_bce(Z, np.array(g["y_rowptr"], np.int32), np.array(g["y_col"], np.int32),
+                            g["scale"], lib=lib)
+    _close(dZ, g["dZ"], 1e-14, 1e-15, "bce hand dZ")
+    assert abs(loss - g["loss"]) < 1e-12, f"bce hand loss {loss} vs {g['loss']}"
+
+
+def pin_dense_special_case(lib):
+    """F = H and every I_k = [0, H): the layer is a dense linear map."""
+    B, H, K, G = 5, 24, 3, 4
+    F = H
+    h, _, W, dZ = _rand_case(B, H, K, G, F, 11)
+    idx = np.tile(np.arange(H, dtype=np.int32), (K, 1))
+    hf, Wf, dZf = _f(h), _f(W), _f(dZ)
+    _close(O.oracle_fwd(h, idx, W, G, lib=lib), hf @ Wf.T, what="dense Z")
+    _close(O.oracle_bwd_w(h, idx, dZ, G, lib=lib), dZf.T @ hf, what="dense dW")
+    _close(O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib), dZf @ Wf, what="dense dh")
+
+
+def pin_brute_force_masked_dense(lib):
+    """Materialise the sparse layer as an L x H matrix and use matmul."""
+    B, H, K, G, F = 6, 40, 5, 3, 7
+    h, idx, W, dZ = _rand_case(B, H, K, G, F, 12)
+    L = K * G
+    hf, Wf, dZf = _f(h), _f(W), _f(dZ)
+    Wd = np.zeros((L, H))
+    M = np.zeros((L, H), dtype=np.int64)
+    for l in range(L):
+        for f in range(F):
+            Wd[l, idx[l // G, f]] = Wf[l, f]
+            M[l, idx[l // G, f]] += 1
+    assert (M.sum(1) == F).all() and (M <= 1).all()
+    for k in range(K):
+        assert (M[k * G:(k + 1) * G] == M[k * G]).all()
+    dWd = dZf.T @ hf
+    dW_ref = np.array([[dWd[l, idx[l // G, f]] for f in range(F)] for l in range(L)])
+    _close(O.oracle_fwd(h, idx, W, G, lib=lib), hf @ Wd.T, what="brute Z")
+    _close(O.oracle_bwd_w(h, idx, dZ, G, lib=lib), dW_ref, what="brute dW")
+    _close(O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib), dZf @ Wd, what="brute dh")
+
+
+def pin_one_hot_probes(lib):
+    """A one-hot feature column or gradient entry selects single products."""
+    B, H, K, G, F = 4, 32, 6, 2, 5
+    _, idx, W, _ = _rand_case(B, H, K, G, F, 13)
+    L = K * G
+    Wf = _f(W)
+    one = bf16_bits(np.array([1.0], np.float32))[0]
+    for j in (0, 7, H - 1):
+        h = np.zeros((B, H), np.uint16)
+        h[:, j] = one
+        Z = O.oracle_fwd(h, idx, W, G, lib=lib)
+        exp = np.zeros((B, L))
+        for l in range(L):
+            hit = np.nonzero(idx[l // G] == j)[0]
+            if hit.size:
+                exp[:, l] = Wf[l, hit[0]]
+        _close(Z, exp, 0, EXACT, f"one-hot Z j={j}")
+    rng = np.random.default_rng(5)
+    h = _small_int_bf16((B, H), rng)
+    hf = _f(h)
+    for (b, l) in ((0, 0), (B - 1, L - 1), (2, 5)):
+        dZ = np.zeros((B, L), np.uint16)
+        dZ[b, l] = one
+        k = l // G
+        dW = O.oracle_bwd_w(h, idx, dZ, G, lib=lib)
+        expw = np.zeros((L, F))
+        expw[l] = hf[b, idx[k]]
+        _close(dW, expw, 0, EXACT, f"one-hot dW {(b, l)}")
+        dh = O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib)
+        exph = np.zeros((B, H))
+        exph[b, idx[k]] = Wf[l]
+        _close(dh, exph, 0, EXACT, f"one-hot dh {(b, l)}")
+
+
+def pin_all_ones(lib):
+    """h = W = dZ = 1: Z = F, dW = B, dh[b, j] = G * #{k : j in I_k}."""
+    B, H, K, G, F = 3, 50, 9, 4, 6
+    _, idx, _, _ = _rand_case(B, H, K, G, F, 14)
+    L = K * G
+    one = bf16_bits(np.array([1.0], np.float32))[0]
+    h = np.full((B, H), one, np.uint16)
+    W = np.full((L, F), one, np.uint16)
+    dZ = np.full((B, L), one, np.uint16)
+    cnt = np.bincount(idx.ravel(), minlength=H).astype(np.float64)
+    _close(O.oracle_fwd(h, idx, W, G, lib=lib), np.full((B, L), F), 0, EXACT, "ones Z")
+    _close(O.oracle_bwd_w(h, idx, dZ, G, lib=lib), np.full((L, F), B), 0, EXACT, "ones dW")
+    _close(O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib), np.tile(G * cnt, (B, 1)), 0, EXACT, "ones dh")
+
+
+def pin_finite_differences(lib):
+    """S(h, W) = <dZ, fwd(h, W)> is bilinear, so S(h + e_bj) - S(h) = dh[b, j]
+    and S(W + e_lf) - S(W) = dW[l, f] exactly (integer-valued inputs, fp64)."""
+    B, H, K, G, F = 3, 20, 4, 3, 5
+    rng = np.random.default_rng(6)
+    _, idx, _, _ = _rand_case(B, H, K, G, F, 15)
+    L = K * G
+    h = _small_int_bf16((B, H), rng)
+    W = _small_int_bf16((L, F), rng)
+    dZ = _small_int_bf16((B, L), rng)
+    dZf = _f(dZ)
+
+    def S(hh, WW):
+        return float((dZf * O.oracle_fwd(hh, idx, WW, G, lib=lib)).sum())
+
+    base = S(h, W)
+    dh = O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib)
+    dW = O.oracle_bwd_w(h, idx, dZ, G, lib=lib)
+    for (b, j) in ((0, int(idx[0, 0])), (B - 1, int(idx[K - 1, F - 1])), (1, int(idx[2, 2]))):
+        h2 = h.copy()
+        h2[b, j] = bf16_bits(np.array([_f(h[b:b + 1, j:j + 1])[0, 0] + 1.0], np.float32))[0]
+        assert S(h2, W) - base == dh[b, j], f"fd dh[{b},{j}]"
+    for (l, f) in ((0, 0), (L - 1, F - 1), (4, 3)):
+        W2 = W.copy()
+        W2[l, f] = bf16_bits(np.array([_f(W[l:l + 1, f:f + 1])[0, 0] + 1.0], np.float32))[0]
+        assert S(h, W2) - base == dW[l, f], f"fd dW[{l},{f}]"
+
+
+def pin_permutation_invariance(lib):
+    B, H, K, G, F = 4, 30, 5, 3, 6
+    h, idx, W, dZ = _rand_case(B, H, K, G, F, 16)
+    L = K * G
+    rng = np.random.default_rng(7)
+    Z = O.oracle_fwd(h, idx, W, G, lib=lib)
+    dW = O.oracle_bwd_w(h, idx, dZ, G, lib=lib)
+    dh = O.oracle_bwd_h(dZ, idx, W, G, H, lib=lib)
+    # group order
+    p = rng.permutation(K)
+    lp = (p[:, None] * G + np.arange(G)[None, :]).ravel()
+    idx2 = np.ascontiguousarray(idx[p])
+    W2 = np.ascontiguousarray(W[lp])
+    dZ2 = np.ascontiguousarray(dZ[:, lp])
+    _close(O.oracle_fwd(h, idx2, W2, G, lib=lib), Z[:, lp], what="perm-group Z")
+    _close(O.oracle_bwd_w(h, idx2, dZ2, G, lib=lib), dW[lp], what="perm-group dW")
+    _close(O.oracle_bwd_h(dZ2, idx2, W2, G, H, lib=lib), dh, what="perm-group dh")
+    # slot order inside each group (index row and the G weight rows together)
+    sig = np.stack([rng.permutation(F) for _ in range(K)])
+    idx3 = np.ascontiguousarray(np.take_along_axis(idx, sig, 1))
+    W3 = np.ascontiguousarray(np.take_along_axis(W, np.repeat(sig, G, 0), 1))
+    _close(O.oracle_fwd(h, idx3, W3, G, lib=lib), Z, what="perm-slot Z")
+    _close(O.oracle_bwd_w(h, idx3, dZ, G, lib=lib), np.take_along_axis(dW, np.repeat(sig, G, 0), 1),
+           what="perm-slot dW")
+    _close(O.oracle_bwd_h(dZ, idx3, W3, G, H, lib=lib), dh, what="perm-slot dh")
+
+
+def pin_bce_zero_weights(lib):
+    """W = 0 gives Z = 0, sigmoid = 1/2, dZ = s(1/2 - Y), loss = s*B*L*ln 2."""
+    B, H, K, G, F = 4, 16, 3, 4, 5
+    h, idx, _, _ = _rand_case(B, H, K, G, F, 17)
+    L = K * G
+    W = np.zeros((L, F), np.uint16)
+    rowptr = np.array([0, 2, 2, 5, 6], np.int32)
+    col = np.array([1, 7, 0, 3, 11, 5], np.int32)
+    s = 1.0 / B
+    r = O.oracle_step(h, idx, W, rowptr, col, s, G, lib=lib)
+    Y = np.zeros((B, L))
+    for b in range(B):
+        Y[b, col[rowptr[b]:rowptr[b + 1]]] = 1
+    _close(r["Z"], np.zeros((B, L)), 0, EXACT, "bce0 Z")
+    _close(r["dZ"], s * (0.5 - Y), 0, EXACT, "bce0 dZ")
+    assert abs(r["loss"] - s * B * L * math.log(2.0)) < 1e-12, "bce0 loss"
+
+
+def pin_torch_autograd(lib):
+    """dZ, dW, dh and the loss equal torch autograd of forward + BCE (fp64, CPU)."""
+    import torch
+
+    B, H, K, G, F = 5, 36, 6, 4, 8
+    h, idx, W, _ = _rand_case(B, H, K, G, F, 18)
+    L = K * G
+    rowptr = np.array([0, 3, 4, 4, 7, 9], np.int32)
+    col = np.array([0, 5, 23, 9, 1, 2, 17, 8, 20], np.int32)
+    s = 1.0 / B
+    r = O.oracle_step(h, idx, W, rowptr, col, s, G, lib=lib)
+    ht = torch.tensor(_f(h), requires_grad=True)
+    Wt = torch.tensor(_f(W), requires_grad=True)
+    it = torch.tensor(idx.astype(np.int64))
+    Hg = ht[:, it]                                        # B x K x F
+    Zt = torch.einsum("bkf,kgf->bkg", Hg, Wt.reshape(K, G, F)).reshape(B, L)
+    Zt.retain_grad()
+    Y = torch.zeros(B, L, dtype=torch.float64)
+    for b in range(B):
+        Y[b, torch.tensor(col[rowptr[b]:rowptr[b + 1]].astype(np.int64))] = 1
+    loss = torch.nn.functional.binary_cross_entropy_with_logits(Zt, Y, reduction="sum") * s
+    loss.backward()
+    _close(r["Z"], Zt.detach().numpy(), 1e-12, 1e-12, "autograd Z")
+    _close(r["dZ"], Zt.grad.numpy(), 1e-10, 1e-14, "autograd dZ")
+    _close(r["dW"], Wt.grad.numpy(), 1e-10, 1e-13, "autograd dW")
+    _close(r["dh"], ht.grad.numpy(), 1e-10, 1e-13, "autograd dh")
+    assert abs(r["loss"] - loss.item()) < 1e-10 * abs(loss.item()), "autograd loss"
+
+
+def pin_g1_per_label(lib):
+    """G = 1: every label has its own index set; z = per-label dot product."""
+    B, H, L, F = 4, 25, 9, 6
+    h = normal_bf16(B * H, 1.0, 19, 1).reshape(B, H)
+    W = normal_bf16(L * F, 0.5, 19, 2).reshape(L, F)
+    dZ = normal_bf16(B * L, 1.0, 19, 3).reshape(B, L)
+    idx1 = sorted_subsets(L, F, H, 19, 6)
+    hf, Wf, dZf = _f(h), _f(W), _f(dZ)
+    gathered = hf[:, idx1]                                  # B x L x F
+    Z_ref = np.einsum("blf,lf->bl", gathered, Wf)
+    dW_ref = np.einsum("bl,blf->lf", dZf, gathered)
+    dh_ref = np.zeros((B, H))
+    for b in range(B):
+        np.add.at(dh_ref[b], idx1.ravel(), (dZf[b][:, None] * Wf).ravel())
+    _close(O.oracle_fwd(h, idx1, W, 1, lib=lib), Z_ref, what="G1 Z")
+    _close(O.oracle_bwd_w(h, idx1, dZ, 1, lib=lib), dW_ref, what="G1 dW")
+    _close(O.oracle_bwd_h(dZ, idx1, W, 1, H, lib=lib), dh_ref, what="G1 dh")
+
+
+ALL_PINS = [
+    pin_hand_example,
+    pin_bce_hand_example,
+    pin_dense_special_case,
+    pin_brute_force_masked_dense,
+    pin_one_hot_probes,
+    pin_all_ones,
+    pin_finite_differences,
+    pin_permutation_invariance,
+    pin_bce_zero_weights,
+    pin_torch_autograd,
+    pin_g1_per_label,
+]

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in a copy of the oracle; the pins must catch each.
+
+Each mutant replaces one exact piece of haste_oracle.c (asserted to occur
+exactly once), is compiled with gcc into a temporary directory, and is run
+against every pin in oracle_pins.ALL_PINS.  A mutant that passes all pins
+would mean the pins cannot tell that mistake from the definition.  CPU only.
+"""
+
+import os
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(O.__file__), "haste_oracle.c")
+
+FWD = "acc += bf16_to_double(h[b * H + idx[k * F + f]]) * bf16_to_double(W[l * F + f]);"
+BWW = "acc += dz_at(dz16, dz64, b * L + l) * bf16_to_double(h[b * H + idx[k * F + f]]);"
+BWH = "dh[b * H + idx[k * F + f]] += d * bf16_to_double(W[l * F + f]);"
+
+MUTANTS = {
+    "fwd_group_map_mod": ("        const int64_t k = l / G;\n        for (int64_t b = 0; b < B; ++b) {",
+                          "        const int64_t k = l % K;\n        for (int64_t b = 0; b < B; ++b) {"),
+    "fwd_slot_reversed": (FWD, FWD.replace("W[l * F + f]", "W[l * F + (F - 1 - f)]")),
+    "fwd_ignores_index": (FWD, FWD.replace("h[b * H + idx[k * F + f]]", "h[b * H + f]")),
+    "fwd_drops_last_slot": ("            for (int64_t f = 0; f < F; ++f)\n                acc += bf16_to_double(h",
+                            "            for (int64_t f = 0; f < F - 1; ++f)\n                acc += bf16_to_double(h"),
+    "bww_sign": (BWW, BWW.replace("acc +=", "acc -=")),
+    "bww_slot0_only": (BWW, BWW.replace("idx[k * F + f]", "idx[k * F]")),
+    "bww_drops_last_sample": ("            for (int64_t b = 0; b < B; ++b)\n                acc += dz_at",
+                              "            for (int64_t b = 0; b < B - 1; ++b)\n                acc += dz_at"),
+    "bww_transposed_dz": (BWW, BWW.replace("b * L + l", "(l % B) * L + (b % L)")),
+    "bwh_overwrite": (BWH, BWH.replace("+=", "=")),
+    "bwh_group_weight_row": (BWH, BWH.replace("W[l * F + f]", "W[k * F + f]")),
+    "bwh_plain_column": (BWH, BWH.replace("dh[b * H + idx[k * F + f]]", "dh[b * H + f]")),
+    "bce_label_sign": ("scale * (1.0 / (1.0 + exp(-z)) - yy)", "scale * (1.0 / (1.0 + exp(-z)) + yy)"),
+    "bce_no_scale": ("scale * (1.0 / (1.0 + exp(-z)) - yy)", "(1.0 / (1.0 + exp(-z)) - yy)"),
+    "bce_sigmoid_sign": ("scale * (1.0 / (1.0 + exp(-z)) - yy)", "scale * (1.0 / (1.0 + exp(z)) - yy)"),
+    "loss_drops_softplus": ("+ log1p(exp(-fabs(z))) - yy * z", "- yy * z"),
+    "loss_label_term_sign": ("+ log1p(exp(-fabs(z))) - yy * z", "+ log1p(exp(-fabs(z))) + yy * z"),
+}
+
+
+def _pins_fail(lib):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} must occur exactly once"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as fh:
+            fh.write(src.replace(old, new))
+        lib = O.load(O.build(src=path, out=os.path.join(d, f"lib{name}.so")))
+        failed = _pins_fail(lib)
+    assert failed, f"no pin detects mutant {name}"
+
+
+def test_pristine_oracle_passes_all_pins():
+    assert _pins_fail(O.load()) == []
