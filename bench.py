@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the group-shared fixed fan-in tail layer on one MI355X.
+
+A step is one fused training pass of the layer over one batch: forward
+logits, BCE gradient against the 0/1 labels, weight gradient and feature
+gradient (libhaste's haste_step), on the Amazon-3M-shaped workload
+(L = 2,999,936 labels in groups of G = 32, F = 64, H = 768, B = 128, ~36
+positives per sample; synthetic seeded inputs already resident in HBM).
+
+Prints ONE JSON line.  Besides the required fields it carries
+  roofline      dominant kernel (forward + BCE + dW) against HBM bandwidth,
+                from HIP events recorded around that kernel on its stream;
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same step;
+  kernels_us    per-phase averages from the same events;
+  extra         unfused calls and the G = 1 per-label baseline on the same
+                shapes (speedups are time ratios at equal useful work).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tail-layer fwd+bwd samples/s and useful TFLOP/s (% bf16 MFMA peak), L=3M G=32"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (timing enabled) through libamdhip64."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+        self.n = n
+
+    def block(self, i, k):
+        """ctypes array view of events [i, i + k)."""
+        return ctypes.cast(ctypes.addressof(self.ev) + i * ctypes.sizeof(ctypes.c_void_p),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(self.ev[i], stream) == 0
+
+    def ms(self, i, j):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[i], self.ev[j]) == 0
+        return out.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def bf16_dev(a, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def i32_dev(a, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def time_call(fn, reps, stream_handle, ev):
+    """Average ms of fn() over reps, from events on the call's stream."""
+    fn()
+    ev.record(0, stream_handle)
+    for _ in range(reps):
+        fn()
+    ev.record(1, stream_handle)
+    import torch
+    torch.cuda.synchronize()
+    return ev.ms(0, 1) / reps
+
+
+def cpu_baseline(w, d, seconds):
+    """The oracle (as is) on consecutive group slices, all batch rows, until
+    `seconds` of wall time are spent; extrapolated to the whole step."""
+    import numpy as np
+    from oracle import oracle as O
+
+    G, K, B = w.G, w.K, w.B
+    s = 1.0 / B
+    per = 4096
+    done = 0
+    t0 = time.perf_counter()
+    while done < K and time.perf_counter() - t0 < seconds:
+        k0, k1 = done, min(K, done + per)
+        lo, hi = k0 * G, k1 * G
+        rp = [0]
+        cols = []
+        for b in range(B):
+            c = d["y_col"][d["y_rowptr"][b]:d["y_rowptr"][b + 1]]
+            c = c[(c >= lo) & (c < hi)] - lo
+            cols.append(c)
+            rp.append(rp[-1] + c.size)
+        O.oracle_step(d["h"], np.ascontiguousarray(d["idx"][k0:k1]), np.ascontiguousarray(d["W"][lo:hi]),
+                      np.array(rp, np.int32), np.concatenate(cols).astype(np.int32), s, G)
+        done = k1
+    el = time.perf_counter() - t0
+    t_full = el * K / done
+    return {"value": round(B / t_full, 3), "unit": "samples/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle step (fwd+BCE+dW+dh) on label groups [0, {done}) of {K}, all {B} samples; "
+                      f"{el:.1f} s wall, extrapolated x{K / done:.2f} to the full step",
+            "seconds_per_step": round(t_full, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="amazon3m_shaped")
+    ap.add_argument("--mode", default="atomic", choices=["atomic", "det"], help="dh reduction")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip unfused calls and the G=1 baseline")
+    ap.add_argument("--report", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer is built and measured on a single MI355X; "
+              "multi-GPU runs are not supported (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import get_workload, make_inputs
+
+    w = get_workload(args.workload)
+    B, H, K, G, F, L = w.B, w.H, w.K, w.G, w.F, w.L
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: L={L} G={G} K={K} F={F} H={H} B={B}")
+    t0 = time.time()
+    d = make_inputs(w, dZ=not args.no_extra, idx1=not args.no_extra)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+
+    h, idx, W = bf16_dev(d["h"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev)
+    rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+    s = 1.0 / B
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = {"dW": torch.empty(L, F, dtype=torch.float32, device=dev),
+           "dh": torch.empty(B, H, dtype=torch.float32, device=dev), "Z": None, "loss": None}
+    ws = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, args.mode)), dtype=torch.uint8, device=dev)
+
+    nev = 5 * args.steps
+    ev = HipEvents(nev + 2)
+
+    def run(i=None):
+        hs.step(h, idx, W, rp, col, s, G, mode=args.mode, out=out, workspace=ws,
+                events=None if i is None else ev.block(5 * i, 5))
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+
+    def avg(a, b):
+        return sum(ev.ms(5 * i + a, 5 * i + b) for i in range(args.steps)) / args.steps
+
+    ph = {"prep_us": 1e3 * avg(0, 1), "fwd_bce_dw_us": 1e3 * avg(1, 2), "dh_us": 1e3 * avg(2, 3),
+          "dh_reduce_us": 1e3 * avg(3, 4), "step_events_us": 1e3 * avg(0, 4)}
+    nnz = int(d["y_rowptr"][-1])
+    # algorithmic bytes of the forward + BCE + dW kernel: W, idx, h, labels in; dW out
+    bytes_a = L * F * 2 + K * F * 4 + B * H * 2 + (B + 1) * 4 + nnz * 4 + L * F * 4
+    t_a = ph["fwd_bce_dw_us"] * 1e-6
+    flops_step = 6 * B * L * F
+    useful_tflops = flops_step / (ms_step * 1e-3) / 1e12
+    step_bytes = bytes_a + B * H * 4
+    res = {
+        "metric": METRIC,
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "L": L, "G": G, "K": K, "F": F, "H": H, "B": B,
+                   "positives_per_sample": w.m, "dh_mode": args.mode,
+                   "step": "haste_step: fused forward + BCE gradient + dW + dh"},
+        "useful_tflops": round(useful_tflops, 2),
+        "pct_bf16_peak": round(100 * useful_tflops / BF16_PEAK_TFLOPS, 2),
+        "step_hbm_floor_us": round(step_bytes / HBM_PEAK_GBS / 1e3, 1),
+        "roofline": {"kernel": "k_group_fwd<STEP_DW> (forward + BCE + dW)", "bound": "hbm",
+                     "achieved": round(bytes_a / t_a / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bytes_a / t_a / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": bytes_a, "avg_us": round(ph["fwd_bce_dw_us"], 2)},
+        "kernels_us": {k: round(v, 2) for k, v in ph.items()},
+    }
+    log(f"[bench] step {ms_step:.3f} ms  phases {res['kernels_us']}")
+
+    if not args.no_extra:
+        extra = {}
+        dZ = bf16_dev(d["dZ"], dev)
+        idx1 = i32_dev(d["idx1"], dev)
+        Z = torch.empty(B, L, dtype=torch.float32, device=dev)
+        dW = torch.empty(L, F, dtype=torch.float32, device=dev)
+        dh = torch.empty(B, H, dtype=torch.float32, device=dev)
+        wsx = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, "det")), dtype=torch.uint8, device=dev)
+        reps = 10
+        calls = {
+            "fwd": lambda: hs.fwd(h, idx, W, G, Z=Z, workspace=wsx),
+            "bwd_w": lambda: hs.bwd_w(h, idx, dZ, G, dW=dW, workspace=wsx),
+            "bwd_h_atomic": lambda: hs.bwd_h(dZ, idx, W, G, H, mode="atomic", dh=dh, workspace=wsx),
+            "bwd_h_det": lambda: hs.bwd_h(dZ, idx, W, G, H, mode="det", dh=dh, workspace=wsx),
+            "step_other_mode": lambda: hs.step(h, idx, W, rp, col, s, G,
+                                               mode="det" if args.mode == "atomic" else "atomic",
+                                               out=out, workspace=wsx),
+            "fixed_fwd": lambda: hs.fixed_fwd(h, idx1, W, Z=Z, workspace=wsx),
+            "fixed_bwd_w": lambda: hs.fixed_bwd_w(h, idx1, dZ, dW=dW, workspace=wsx),
+            "fixed_bwd_h_atomic": lambda: hs.fixed_bwd_h(dZ, idx1, W, H, mode="atomic", dh=dh, workspace=wsx),
+        }
+        for name, fn in calls.items():
+            extra[name + "_us"] = round(1e3 * time_call(fn, reps, sh, ev), 2)
+            log(f"[bench] {name}: {extra[name + '_us']} us")
+        t_fwd_bce = time_call(lambda: hs.fwd_bce(h, idx, W, rp, col, s, G, workspace=wsx), reps, sh, ev)
+        extra["fwd_bce_us"] = round(1e3 * t_fwd_bce, 2)
+        unf = extra["fwd_bce_us"] + extra["bwd_w_us"] + extra["bwd_h_atomic_us"]
+        extra["unfused_step_us"] = round(unf, 2)
+        extra["speedup_fwd_vs_G1"] = round(extra["fixed_fwd_us"] / extra["fwd_us"], 2)
+        extra["speedup_bwd_vs_G1"] = round((extra["fixed_bwd_w_us"] + extra["fixed_bwd_h_atomic_us"]) /
+                                           (extra["bwd_w_us"] + extra["bwd_h_atomic_us"]), 2)
+        bytes_fwd = L * F * 2 + K * F * 4 + B * H * 2 + B * L * 4
+        bytes_bwh = B * L * 2 + L * F * 2 + K * F * 4 + B * H * 4
+        extra["fwd_hbm_frac"] = round(bytes_fwd / (extra["fwd_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        extra["bwd_h_atomic_hbm_frac"] = round(bytes_bwh / (extra["bwd_h_atomic_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        res["extra"] = extra
+        del Z
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+    ev.close()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""MI355X-native group-shared fixed fan-in sparse output layer (HASTE).
+
+The compute lives in libhaste.so (HIP, gfx950) behind the C ABI declared in
+include/haste.h; `binding` is a thin ctypes layer over it.
+"""
+
+from . import binding  # noqa: F401
+from .binding import (  # noqa: F401
+    HasteError,
+    bwd_h,
+    bwd_w,
+    fixed_bwd_h,
+    fixed_bwd_w,
+    fixed_fwd,
+    fwd,
+    fwd_bce,
+    step,
+    validate_idx,
+    validate_labels,
+    workspace_size,
+)

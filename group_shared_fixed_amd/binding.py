@@ -1,0 +1,281 @@
+"""ctypes binding of libhaste.so (the C ABI in include/haste.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.  There is
+no fallback: when libhaste.so is missing or a call fails, a HasteError is
+raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhaste.so")
+
+HASTE_OK = 0
+STATUS = {
+    0: "HASTE_OK", -1: "HASTE_ERR_NULL", -2: "HASTE_ERR_DIM", -3: "HASTE_ERR_UNSUPPORTED",
+    -4: "HASTE_ERR_ALIGN", -5: "HASTE_ERR_WORKSPACE", -6: "HASTE_ERR_INDEX", -7: "HASTE_ERR_HIP",
+}
+OP = {"fwd": 0, "bwd_w": 1, "bwd_h": 2, "fwd_bce": 3, "step": 4, "fixed_fwd": 5, "fixed_bwd_w": 6,
+      "fixed_bwd_h": 7}
+DH_MODE = {"atomic": 0, "det": 1, "deterministic": 1, 0: 0, 1: 1}
+
+# name -> (restype, argtypes); P = pointer, I = int64, S = size_t, F = float, M = int
+_P, _I, _S, _F, _M = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_int
+SIGNATURES = {
+    "haste_workspace_size": (_S, [_M, _I, _I, _I, _I, _I, _M]),
+    "haste_fwd": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_bwd_w": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_bwd_h": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
+    "haste_fwd_bce": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_step": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
+    "haste_step_timed": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P, _P]),
+    "haste_fixed_fwd": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_fixed_bwd_w": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_fixed_bwd_h": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _M, _P, _S, _P]),
+    "haste_validate_idx": (_M, [_P, _I, _I, _I, _P, _P]),
+    "haste_validate_labels": (_M, [_P, _P, _I, _I, _P, _P]),
+    "haste_status_string": (ctypes.c_char_p, [_M]),
+    "haste_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class HasteError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} returned {code} ({STATUS.get(code, '?')})")
+
+
+def lib(path: str | None = None):
+    """Load libhaste.so; raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise HasteError("load", -7) from FileNotFoundError(
+            f"{p} is missing: build it with group_shared_fixed_amd/build.py (hipcc, gfx950)")
+    L = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(fn, code):
+    if code != HASTE_OK:
+        raise HasteError(fn, code)
+
+
+# ---------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bits(t):
+    """bf16 tensor (or its int16/uint16 bit view) as a bf16-bit tensor."""
+    torch = _torch()
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected bfloat16 (or its 16-bit patterns), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t
+
+
+def _i32(t):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError("index tensors must be contiguous int32")
+    return t
+
+
+def workspace_size(op: str, B, H, K, G, F, dh_mode="atomic") -> int:
+    return int(lib().haste_workspace_size(OP[op], B, H, K, G, F, DH_MODE[dh_mode]))
+
+
+def _workspace(op, B, H, K, G, F, dh_mode, device, workspace):
+    torch = _torch()
+    n = workspace_size(op, B, H, K, G, F, dh_mode)
+    if workspace is not None:
+        return workspace, n
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def fwd(h, idx, W, G, Z=None, workspace=None, stream=None):
+    """Z = forward logits (B x L fp32)."""
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx)
+    B, H = h.shape
+    K, F = idx.shape
+    if Z is None:
+        Z = torch.empty(B, K * G, dtype=torch.float32, device=h.device)
+    ws, n = _workspace("fwd", B, H, K, G, F, 0, h.device, workspace)
+    _check("haste_fwd", lib().haste_fwd(_ptr(h), _ptr(idx), _ptr(W), _ptr(Z), B, H, K, G, F,
+                                         _ptr(ws), ws.numel() if ws is not None else 0, _stream(h, stream)))
+    return Z
+
+
+def bwd_w(h, idx, dZ, G, dW=None, workspace=None, stream=None):
+    """dW (L x F fp32) from bf16 dZ."""
+    torch = _torch()
+    _bits(h); _bits(dZ); _i32(idx)
+    B, H = h.shape
+    K, F = idx.shape
+    if dW is None:
+        dW = torch.empty(K * G, F, dtype=torch.float32, device=h.device)
+    ws, n = _workspace("bwd_w", B, H, K, G, F, 0, h.device, workspace)
+    _check("haste_bwd_w", lib().haste_bwd_w(_ptr(h), _ptr(idx), _ptr(dZ), _ptr(dW), B, H, K, G, F,
+                                             _ptr(ws), ws.numel() if ws is not None else 0, _stream(h, stream)))
+    return dW
+
+
+def bwd_h(dZ, idx, W, G, H, mode="atomic", dh=None, workspace=None, stream=None):
+    """dh (B x H fp32) from bf16 dZ."""
+    torch = _torch()
+    _bits(dZ); _bits(W); _i32(idx)
+    B = dZ.shape[0]
+    K, F = idx.shape
+    if dh is None:
+        dh = torch.empty(B, H, dtype=torch.float32, device=dZ.device)
+    m = DH_MODE[mode]
+    ws, n = _workspace("bwd_h", B, H, K, G, F, m, dZ.device, workspace)
+    _check("haste_bwd_h", lib().haste_bwd_h(_ptr(dZ), _ptr(idx), _ptr(W), _ptr(dh), B, H, K, G, F, m,
+                                             _ptr(ws), ws.numel() if ws is not None else 0, _stream(dZ, stream)))
+    return dh
+
+
+def fwd_bce(h, idx, W, y_rowptr, y_col, scale, G, want_Z=False, want_loss=False, workspace=None, stream=None):
+    """(dZ bf16 B x L, Z fp32 or None, loss double tensor or None)."""
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    K, F = idx.shape
+    dZ = torch.empty(B, K * G, dtype=torch.bfloat16, device=h.device)
+    Z = torch.empty(B, K * G, dtype=torch.float32, device=h.device) if want_Z else None
+    loss = torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None
+    ws, n = _workspace("fwd_bce", B, H, K, G, F, 0, h.device, workspace)
+    _check("haste_fwd_bce", lib().haste_fwd_bce(
+        _ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(dZ), _ptr(Z), _ptr(loss),
+        B, H, K, G, F, _ptr(ws), ws.numel() if ws is not None else 0, _stream(h, stream)))
+    return dZ, Z, (loss[:1] if loss is not None else None)
+
+
+def step(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want_loss=False, out=None,
+         workspace=None, stream=None, events=None):
+    """Fused forward + BCE + dW + dh.  Returns dict(dW, dh, Z, loss).
+
+    events: optional ctypes array of 5 hipEvent_t handles (haste_step_timed)."""
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    K, F = idx.shape
+    if out is None:
+        out = {
+            "dW": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "Z": torch.empty(B, K * G, dtype=torch.float32, device=h.device) if want_Z else None,
+            "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
+        }
+    m = DH_MODE[mode]
+    ws, n = _workspace("step", B, H, K, G, F, m, h.device, workspace)
+    args = (_ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]),
+            _ptr(out["dh"]), _ptr(out.get("Z")), _ptr(out.get("loss")), B, H, K, G, F, m, _ptr(ws),
+            ws.numel() if ws is not None else 0, _stream(h, stream))
+    if events is None:
+        _check("haste_step", lib().haste_step(*args))
+    else:
+        _check("haste_step_timed", lib().haste_step_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+    return out
+
+
+def fixed_fwd(h, idx1, W, Z=None, workspace=None, stream=None):
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx1)
+    B, H = h.shape
+    L, F = idx1.shape
+    if Z is None:
+        Z = torch.empty(B, L, dtype=torch.float32, device=h.device)
+    ws, n = _workspace("fixed_fwd", B, H, L, 1, F, 0, h.device, workspace)
+    _check("haste_fixed_fwd", lib().haste_fixed_fwd(_ptr(h), _ptr(idx1), _ptr(W), _ptr(Z), B, H, L, F,
+                                                     _ptr(ws), ws.numel() if ws is not None else 0,
+                                                     _stream(h, stream)))
+    return Z
+
+
+def fixed_bwd_w(h, idx1, dZ, dW=None, workspace=None, stream=None):
+    torch = _torch()
+    _bits(h); _bits(dZ); _i32(idx1)
+    B, H = h.shape
+    L, F = idx1.shape
+    if dW is None:
+        dW = torch.empty(L, F, dtype=torch.float32, device=h.device)
+    ws, n = _workspace("fixed_bwd_w", B, H, L, 1, F, 0, h.device, workspace)
+    _check("haste_fixed_bwd_w", lib().haste_fixed_bwd_w(_ptr(h), _ptr(idx1), _ptr(dZ), _ptr(dW), B, H, L, F,
+                                                         _ptr(ws), ws.numel() if ws is not None else 0,
+                                                         _stream(h, stream)))
+    return dW
+
+
+def fixed_bwd_h(dZ, idx1, W, H, mode="atomic", dh=None, workspace=None, stream=None):
+    torch = _torch()
+    _bits(dZ); _bits(W); _i32(idx1)
+    B = dZ.shape[0]
+    L, F = idx1.shape
+    if dh is None:
+        dh = torch.empty(B, H, dtype=torch.float32, device=dZ.device)
+    m = DH_MODE[mode]
+    ws, n = _workspace("fixed_bwd_h", B, H, L, 1, F, m, dZ.device, workspace)
+    _check("haste_fixed_bwd_h", lib().haste_fixed_bwd_h(_ptr(dZ), _ptr(idx1), _ptr(W), _ptr(dh), B, H, L, F, m,
+                                                         _ptr(ws), ws.numel() if ws is not None else 0,
+                                                         _stream(dZ, stream)))
+    return dh
+
+
+def validate_idx(idx, H, stream=None) -> int:
+    """Number of index rows with an entry outside [0, H) or not increasing."""
+    torch = _torch()
+    _i32(idx)
+    bad = torch.empty(4, dtype=torch.int32, device=idx.device)
+    rows, F = idx.shape
+    _check("haste_validate_idx", lib().haste_validate_idx(_ptr(idx), rows, F, H, _ptr(bad), _stream(idx, stream)))
+    return int(bad[0].item())
+
+
+def validate_labels(y_rowptr, y_col, L, stream=None) -> int:
+    torch = _torch()
+    _i32(y_rowptr); _i32(y_col)
+    bad = torch.empty(4, dtype=torch.int32, device=y_rowptr.device)
+    B = y_rowptr.numel() - 1
+    _check("haste_validate_labels", lib().haste_validate_labels(_ptr(y_rowptr), _ptr(y_col), B, L, _ptr(bad),
+                                                                 _stream(y_rowptr, stream)))
+    return int(bad[0].item())
+
+
+def status_string(code: int) -> str:
+    return lib().haste_status_string(code).decode()
+
+
+def version() -> str:
+    return lib().haste_version().decode()

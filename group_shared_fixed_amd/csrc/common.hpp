@@ -1,0 +1,119 @@
+// Device helpers shared by the HIP kernels of libhaste (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace haste {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16x16x32 bf16 matrix-core product, fp32 accumulate.
+// Lane l supplies A row (l % 16) and B column (l % 16); the 32-deep
+// contraction is split over the four lane groups q = l / 16, eight values
+// per lane.  Any assignment of contraction indices to (q, element) works as
+// long as A and B use the same one.  The 16x16 result lands as: lane l holds
+// column (l % 16), rows 4*(l/16) + i for i = 0..3.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Split fp32 pairs into bf16 hi parts and bf16 residual (lo) parts so that
+// hi + lo carries about 16 significant bits of x.
+// Returns {hi, lo} packed pairs.
+__device__ __forceinline__ u32x2_t split_pair(float x0, float x1)
+{
+    const uint32_t hi = pack_bf16(x0, x1);
+    const uint32_t lo = pack_bf16(x0 - bf16lo_to_f32(hi), x1 - bf16hi_to_f32(hi));
+    return u32x2_t{hi, lo};
+}
+
+// Orders LDS accesses of one wavefront (LDS executes a wave's accesses in
+// issue order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const void* p)
+{
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// XOR swizzle of 16-byte chunks inside a row of an LDS tile so that the
+// transposing 2-byte writes and the 16-byte matrix-operand reads of one
+// instruction spread over distinct banks.
+__device__ __forceinline__ int swz(int r, int nchunks)
+{
+    int s = ((r & 3) | ((r >> 1) & 4)) ^ (((r >> 4) & 1) << 1);
+    return s & (nchunks - 1);
+}
+
+// Walks one sample's sorted positive-label list (a CSR row of the 0/1 label
+// matrix) alongside groups visited in increasing order.  take(lo, G) returns
+// the G-bit mask of positives with ids in [lo, lo + G) and skips ids below lo.
+struct LabelCursor {
+    int pos, end, next;
+
+    __device__ __forceinline__ void init(const int32_t* rowptr, const int32_t* col, int64_t b, int64_t B,
+                                         int64_t first)
+    {
+        pos = end = 0;
+        next = 0x7fffffff;
+        if (b < B) {
+            int lo = rowptr[b], hi = rowptr[b + 1];
+            end = hi;
+            while (lo < hi) {
+                int mid = (lo + hi) >> 1;
+                if ((int64_t)col[mid] < first) lo = mid + 1; else hi = mid;
+            }
+            pos = lo;
+            next = pos < end ? col[pos] : 0x7fffffff;
+        }
+    }
+
+    __device__ __forceinline__ uint64_t take(int64_t lo, int G, const int32_t* col)
+    {
+        uint64_t m = 0;
+        while ((int64_t)next < lo + G) {
+            if ((int64_t)next >= lo) m |= 1ull << (int)((int64_t)next - lo);
+            ++pos;
+            next = pos < end ? col[pos] : 0x7fffffff;
+        }
+        return m;
+    }
+};
+
+}  // namespace haste

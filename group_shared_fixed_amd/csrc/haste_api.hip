@@ -1,0 +1,317 @@
+// C ABI of libhaste: host-side validation, workspace layout and launches.
+// Every check runs before the first HIP call, so error paths behave the same
+// on a machine without a GPU.
+#include "haste.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+using namespace haste;
+
+namespace {
+
+constexpr int64_t kMaxLabels = 2147483647LL - 64;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+    int64_t Bp;          // batch padded to 32 (feature-major copy of h)
+    size_t hT_bytes;     // H x Bp bf16
+    size_t part_bytes;   // deterministic dh partials
+    int nchunks, ntiles; // dh split: label chunks x batch tiles
+    size_t total;
+};
+
+bool op_needs_hT(int op)
+{
+    return op == HASTE_OP_FWD || op == HASTE_OP_BWD_W || op == HASTE_OP_FWD_BCE || op == HASTE_OP_STEP ||
+           op == HASTE_OP_FIXED_FWD || op == HASTE_OP_FIXED_BWD_W;
+}
+
+bool op_has_dh(int op) { return op == HASTE_OP_BWD_H || op == HASTE_OP_STEP || op == HASTE_OP_FIXED_BWD_H; }
+
+Layout layout(int op, int64_t B, int64_t H, int dh_mode)
+{
+    Layout l{};
+    l.Bp = round_up(B, 32);
+    l.ntiles = (int)((B + kDhRows - 1) / kDhRows);
+    int nc = (512 / l.ntiles) / 8 * 8;
+    l.nchunks = nc < 8 ? 8 : nc;
+    l.hT_bytes = op_needs_hT(op) ? align256((size_t)H * (size_t)l.Bp * 2) : 0;
+    l.part_bytes = (op_has_dh(op) && dh_mode == HASTE_DH_DETERMINISTIC)
+                       ? align256((size_t)l.nchunks * l.ntiles * kDhRows * (size_t)H * 4)
+                       : 0;
+    l.total = l.hT_bytes + l.part_bytes;
+    return l;
+}
+
+int check_shape(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, bool fixed)
+{
+    if (B < 1 || H < 1 || K < 1 || G < 1 || F < 1) return HASTE_ERR_DIM;
+    if (F > H) return HASTE_ERR_DIM;
+    if (fixed ? (G != 1) : (G != 16 && G != 32 && G != 64)) return HASTE_ERR_UNSUPPORTED;
+    if (F != 32 && F != 64 && F != 128) return HASTE_ERR_UNSUPPORTED;
+    if (H > 1024) return HASTE_ERR_UNSUPPORTED;
+    if (K > kMaxLabels / G) return HASTE_ERR_UNSUPPORTED;
+    if (B > (1 << 24)) return HASTE_ERR_UNSUPPORTED;
+    return HASTE_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0) return HASTE_OK;
+    if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255u) != 0) return HASTE_ERR_WORKSPACE;
+    return HASTE_OK;
+}
+
+int hip_status()
+{
+    return hipGetLastError() == hipSuccess ? HASTE_OK : HASTE_ERR_HIP;
+}
+
+int fwd_grid(int64_t K)
+{
+    int64_t g = (K + 3) / 4;
+    return (int)(g > 512 ? 512 : (g < 1 ? 1 : g));
+}
+
+#define HASTE_TRY(x)                 \
+    do {                             \
+        int _st = (x);               \
+        if (_st != HASTE_OK) return _st; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t haste_workspace_size(int op, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode)
+{
+    (void)K;
+    (void)G;
+    (void)F;
+    if (op < HASTE_OP_FWD || op > HASTE_OP_FIXED_BWD_H || B < 1 || H < 1) return 0;
+    return layout(op, B, H, dh_mode).total;
+}
+
+int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, float* Z, int64_t B, int64_t H,
+              int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !idx || !W || !Z) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_FWD, B, H, 0);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    uint16_t* hT = (uint16_t*)workspace;
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    FwdArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K; a.scale = 1.f; a.Z = Z;
+    if (!launch_fwd((int)G, (int)F, FWD_Z, false, a, fwd_grid(K), stream)) return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+int haste_bwd_w(const haste_bf16* h, const int32_t* idx, const haste_bf16* dZ, float* dW, int64_t B, int64_t H,
+                int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !idx || !dZ || !dW) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_BWD_W, B, H, 0);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    uint16_t* hT = (uint16_t*)workspace;
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    FwdArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.K = K; a.scale = 1.f;
+    a.dZ = const_cast<uint16_t*>(dZ); a.dW = dW;
+    if (!launch_fwd((int)G, (int)F, BWD_W, false, a, fwd_grid(K), stream)) return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, float* dh, int64_t B, int64_t H,
+                int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace, size_t workspace_bytes,
+                hipStream_t stream)
+{
+    if (!dZ || !idx || !W || !dh) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(dZ) || !aligned16(idx) || !aligned16(W) || !aligned16(dh)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_BWD_H, B, H, dh_mode);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
+    DhArgs a{};
+    a.Bp = l.Bp; a.B = B; a.H = H; a.idx = idx; a.W = W; a.K = K; a.dZ = dZ; a.scale = 1.f;
+    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
+    if (!det) launch_fill_f32(dh, B * H, stream);
+    if (!launch_dh((int)G, (int)F, DH_FROM_DZ, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
+    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    return hip_status();
+}
+
+int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                  const int32_t* y_col, float scale, haste_bf16* dZ, float* Z, double* loss, int64_t B, int64_t H,
+                  int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !idx || !W || !y_rowptr || !y_col || !dZ) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (B > kMaxLabelBatch) return HASTE_ERR_UNSUPPORTED;
+    if (!(scale > 0.f)) return HASTE_ERR_DIM;
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) ||
+        !aligned16(dZ) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
+        return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_FWD_BCE, B, H, 0);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    uint16_t* hT = (uint16_t*)workspace;
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    if (loss) launch_fill_f64(loss, 1, stream);
+    FwdArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;
+    a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dZ = dZ; a.loss = loss;
+    if (!launch_fwd((int)G, (int)F, FWD_BCE, loss != nullptr, a, fwd_grid(K), stream))
+        return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                     const int32_t* y_col, float scale, float* dW, float* dh, float* Z, double* loss, int64_t B,
+                     int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    if (!h || !idx || !W || !y_rowptr || !y_col || !dW || !dh) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (B > kMaxLabelBatch) return HASTE_ERR_UNSUPPORTED;
+    if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
+    if (!(scale > 0.f)) return HASTE_ERR_DIM;
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) ||
+        !aligned16(dW) || !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
+        return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_STEP, B, H, dh_mode);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
+    uint16_t* hT = (uint16_t*)workspace;
+    float* part = det ? (float*)((char*)workspace + l.hT_bytes) : nullptr;
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord(events[i], stream);
+    };
+    mark(0);
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    if (loss) launch_fill_f64(loss, 1, stream);
+    if (!det) launch_fill_f32(dh, B * H, stream);
+    mark(1);
+    FwdArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;
+    a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dW = dW; a.loss = loss;
+    if (!launch_fwd((int)G, (int)F, STEP_DW, loss != nullptr, a, fwd_grid(K), stream))
+        return HASTE_ERR_UNSUPPORTED;
+    mark(2);
+    DhArgs d{};
+    d.hT = hT; d.Bp = l.Bp; d.B = B; d.H = H; d.idx = idx; d.W = W; d.K = K;
+    d.y_rowptr = y_rowptr; d.y_col = y_col; d.scale = scale;
+    d.nchunks = l.nchunks; d.ntiles = l.ntiles; d.dh = dh; d.part = part;
+    if (!launch_dh((int)G, (int)F, DH_FROM_LABELS, det, d, stream)) return HASTE_ERR_UNSUPPORTED;
+    mark(3);
+    if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    mark(4);
+    return hip_status();
+}
+
+int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+               const int32_t* y_col, float scale, float* dW, float* dh, float* Z, double* loss, int64_t B,
+               int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace, size_t workspace_bytes,
+               hipStream_t stream)
+{
+    return haste_step_timed(h, idx, W, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* W, float* Z, int64_t B,
+                    int64_t H, int64_t L, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !idx1 || !W || !Z) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, L, 1, F, true));
+    if (!aligned16(h) || !aligned16(idx1) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_FIXED_FWD, B, H, 0);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    uint16_t* hT = (uint16_t*)workspace;
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    FixedArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.W = W; a.L = L; a.Z = Z;
+    if (!launch_fixed_fwd((int)F, a, 1024, stream)) return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+int haste_fixed_bwd_w(const haste_bf16* h, const int32_t* idx1, const haste_bf16* dZ, float* dW, int64_t B,
+                      int64_t H, int64_t L, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !idx1 || !dZ || !dW) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, L, 1, F, true));
+    if (!aligned16(h) || !aligned16(idx1) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_FIXED_BWD_W, B, H, 0);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    uint16_t* hT = (uint16_t*)workspace;
+    launch_transpose_h(h, hT, B, H, l.Bp, stream);
+    FixedArgs a{};
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.L = L; a.dZ = dZ; a.dW = dW;
+    if (!launch_fixed_bwd_w((int)F, a, 1024, stream)) return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf16* W, float* dh, int64_t B,
+                      int64_t H, int64_t L, int64_t F, int dh_mode, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    if (!dZ || !idx1 || !W || !dh) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, L, 1, F, true));
+    if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(dZ) || !aligned16(idx1) || !aligned16(W) || !aligned16(dh)) return HASTE_ERR_ALIGN;
+    const Layout l = layout(HASTE_OP_FIXED_BWD_H, B, H, dh_mode);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
+    FixedArgs a{};
+    a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.W = W; a.L = L; a.dZ = dZ;
+    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
+    if (!det) launch_fill_f32(dh, B * H, stream);
+    if (!launch_fixed_bwd_h((int)F, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
+    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    return hip_status();
+}
+
+int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t stream)
+{
+    if (!idx || !bad) return HASTE_ERR_NULL;
+    if (rows < 1 || F < 1 || H < 1) return HASTE_ERR_DIM;
+    launch_fill_i32(bad, 1, stream);
+    launch_validate_idx(idx, rows, F, H, bad, stream);
+    return hip_status();
+}
+
+int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t B, int64_t L, int32_t* bad,
+                          hipStream_t stream)
+{
+    if (!y_rowptr || !y_col || !bad) return HASTE_ERR_NULL;
+    if (B < 1 || L < 1) return HASTE_ERR_DIM;
+    launch_fill_i32(bad, 1, stream);
+    launch_validate_labels(y_rowptr, y_col, B, L, bad, stream);
+    return hip_status();
+}
+
+const char* haste_status_string(int status)
+{
+    switch (status) {
+    case HASTE_OK: return "ok";
+    case HASTE_ERR_NULL: return "a required pointer is NULL";
+    case HASTE_ERR_DIM: return "invalid or inconsistent sizes";
+    case HASTE_ERR_UNSUPPORTED: return "shape not supported by the gfx950 kernels";
+    case HASTE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case HASTE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case HASTE_ERR_INDEX: return "invalid index set or labels";
+    case HASTE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+const char* haste_version(void) { return "libhaste 0.1 (gfx950)"; }
+
+}  // extern "C"

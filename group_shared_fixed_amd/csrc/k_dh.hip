@@ -1,0 +1,324 @@
+// Feature gradient of the group-shared fixed fan-in layer.
+//
+// HASTE ("gather-once + dense MMA kernel" section of the paper notes): the
+// feature gradient is the sum over groups of dZ_k W_k added into the columns
+// I_k; index sets of different groups overlap, so partial results from
+// subsets of groups are computed in parallel and then reduced ("split-K"
+// along the label dimension).
+//
+// Work split: a workgroup owns one chunk of consecutive groups and one tile
+// of kDhRows batch rows, and accumulates P_k = dZ_k[tile] W_k for its groups
+// into an LDS accumulator acc[kDhRows][H] (scatter-add into columns I_k).
+// The workgroups of one chunk sit on one XCD (workgroup ids are dealt to the
+// XCDs round-robin), so the W_k they all read is fetched from HBM once and
+// served to the other batch tiles from that XCD's L2.  Each wave takes every
+// fourth group of the chunk.
+//
+// dZ comes either from the caller (bf16) or is recomputed from the logits
+// of the tile (Z_k^T = W_k H_k^T on matrix cores) and the labels, as
+// s (sigmoid(Z) - Y), split into bf16 hi + lo.
+//
+// Reduction of the per-workgroup accumulators:
+//   atomic:        fp32 atomic adds into dh (order of the adds varies);
+//   deterministic: the four waves of a workgroup add their P_k into acc in a
+//                  fixed order (barrier-separated turns), each workgroup
+//                  writes its accumulator to its own slice of a partials
+//                  buffer, and a second kernel sums the slices in chunk
+//                  order: bitwise reproducible for a fixed shape.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace haste {
+
+__device__ __forceinline__ int swz16(int r, int nchunks)
+{
+    return ((r & 7) ^ ((r >> 3) << 2)) & (nchunks - 1);
+}
+
+// W^T tile [slot f][label g]: 16-byte chunks along g, swizzled by f.
+__device__ __forceinline__ int swzw(int f, int nchunks)
+{
+    return ((f >> 1) ^ (f >> 3)) & (nchunks - 1);
+}
+
+template <int G, int F, int SRC, bool DET>
+__global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
+{
+    constexpr int NT = F / 16;          // output slot tiles of P
+    constexpr int KSF = F / 32;         // contraction steps of Z^T = W H^T
+    constexpr int GT = G / 16;          // label tiles
+    constexpr int KSG = (G + 31) / 32;  // contraction steps of P = dZ W
+    constexpr int NCH = F / 8;
+    constexpr int GCH = G / 8;
+    constexpr int R = kDhRows;
+
+    extern __shared__ float acc[];      // R x H
+    __shared__ __attribute__((aligned(16))) uint16_t sH[SRC == DH_FROM_LABELS ? 4 : 1][SRC == DH_FROM_LABELS ? R * F : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sWT[4][F * G];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int r16 = lane & 15;
+    const int q = lane >> 4;
+
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int tile = slot % a.ntiles;
+    const int chunk = (slot / a.ntiles) * 8 + xcd;
+    const int64_t kc0 = (int64_t)chunk * a.K / a.nchunks;
+    const int64_t kc1 = (int64_t)(chunk + 1) * a.K / a.nchunks;
+    const int64_t b0 = (int64_t)tile * R;
+    const int64_t L = a.K * G;
+    const int64_t H = a.H;
+
+    for (int64_t i = threadIdx.x; i < R * H; i += 256)
+        acc[i] = 0.f;
+
+    LabelCursor cur;
+    if constexpr (SRC == DH_FROM_LABELS)
+        cur.init(a.y_rowptr, a.y_col, b0 + r16, a.B, kc0 * G);
+    const float scale = a.scale;
+    const float inv_s = 1.0f / a.scale;
+    const int64_t brow = b0 + r16;            // batch row of this lane's A rows
+    const bool brow_ok = brow < a.B;
+
+    __syncthreads();
+
+    const int64_t ng = kc1 - kc0;
+    const int64_t nrounds = (ng + 3) / 4;
+    for (int64_t rd = 0; rd < nrounds; ++rd) {
+        const int64_t k = kc0 + 4 * rd + wv;
+        const bool active = k < kc1;
+        f32x4_t p[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            p[t] = zero4();
+        int col[NT];
+
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                col[t] = a.idx[k * F + 16 * t + r16];
+            // W_k rows: lane (label 16gt + r16, q) holds slots 32s + 8q .. +8
+            u32x4_t wreg[GT][KSF];
+#pragma unroll
+            for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                for (int s = 0; s < KSF; ++s)
+                    wreg[gt][s] = ldg16(a.W + ((k * G + 16 * gt + r16) * F + 32 * s + 8 * q));
+            // W_k^T into LDS for the B operand of P = dZ W (contraction over labels)
+            uint16_t* wt = sWT[wv];
+#pragma unroll
+            for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                for (int s = 0; s < KSF; ++s)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int f = 32 * s + 8 * q + e;
+                        const int g = 16 * gt + r16;
+                        const uint32_t wd = wreg[gt][s][e >> 1];
+                        wt[f * G + ((((g >> 3) ^ swzw(f, GCH))) << 3) + (g & 7)] =
+                            (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu));
+                    }
+
+            u32x4_t ahi[KSG], alo[KSG];
+            if constexpr (SRC == DH_FROM_DZ) {
+                // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
+#pragma unroll
+                for (int s = 0; s < KSG; ++s) {
+                    ahi[s] = u32x4_t{0u, 0u, 0u, 0u};
+                    alo[s] = u32x4_t{0u, 0u, 0u, 0u};
+                    if (brow_ok && 32 * s + 8 * q < G)
+                        ahi[s] = ldg16(a.dZ + brow * L + k * G + 32 * s + 8 * q);
+                }
+            } else {
+                // gather the tile of H_k: lane (slot 32u + lane%32, half) <- 8 rows
+                uint16_t* ht = sH[wv];
+#pragma unroll
+                for (int u = 0; u < F / 32; ++u) {
+                    const int f = 32 * u + (lane & 31);
+                    const int half = lane >> 5;
+                    const int jc = a.idx[k * F + f];
+                    const u32x4_t v = ldg16(a.hT + (int64_t)jc * a.Bp + b0 + 8 * half);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = 8 * half + e;
+                        ht[r * F + ((((f >> 3) ^ swz16(r, NCH))) << 3) + (f & 7)] =
+                            (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+                    }
+                }
+                wave_sync();
+                // Z^T = W_k H^T: result lane (row r16, q) holds labels 16gt + 4q + i
+                f32x4_t zt[GT];
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt)
+                    zt[gt] = zero4();
+#pragma unroll
+                for (int s = 0; s < KSF; ++s) {
+                    const int ch = 4 * s + q;
+                    const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(ht + r16 * F + ((ch ^ swz16(r16, NCH)) << 3));
+#pragma unroll
+                    for (int gt = 0; gt < GT; ++gt)
+                        zt[gt] = mfma16(wreg[gt][s], bv, zt[gt]);
+                }
+                // labels of this row for this group
+                const uint64_t mrow = cur.take(k * G, G, a.y_col);
+                float dz[GT][4];
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float t = __builtin_amdgcn_exp2f(-zt[gt][i] * kLog2e);
+                        float d = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
+                        if ((mrow >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
+                        dz[gt][i] = brow_ok ? d : 0.f;
+                    }
+                // contraction element e of step s <-> label 32s + 16*(e/4) + 4q + e%4
+#pragma unroll
+                for (int s = 0; s < KSG; ++s) {
+                    const int g0 = 2 * s, g1 = 2 * s + 1;
+                    const float x0 = dz[g0][0], x1 = dz[g0][1], x2 = dz[g0][2], x3 = dz[g0][3];
+                    const float y0 = g1 < GT ? dz[g1 < GT ? g1 : 0][0] : 0.f;
+                    const float y1 = g1 < GT ? dz[g1 < GT ? g1 : 0][1] : 0.f;
+                    const float y2 = g1 < GT ? dz[g1 < GT ? g1 : 0][2] : 0.f;
+                    const float y3 = g1 < GT ? dz[g1 < GT ? g1 : 0][3] : 0.f;
+                    { const u32x2_t _p = split_pair(x0, x1); ahi[s][0] = _p[0]; alo[s][0] = _p[1]; }
+                    { const u32x2_t _p = split_pair(x2, x3); ahi[s][1] = _p[0]; alo[s][1] = _p[1]; }
+                    { const u32x2_t _p = split_pair(y0, y1); ahi[s][2] = _p[0]; alo[s][2] = _p[1]; }
+                    { const u32x2_t _p = split_pair(y2, y3); ahi[s][3] = _p[0]; alo[s][3] = _p[1]; }
+                }
+            }
+            wave_sync();
+            // P = dZ_tile W_k: result lane (slot 16t + r16, q) holds rows 4q + i
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int f = 16 * t + r16;
+                const uint16_t* wrow = sWT[wv] + f * G;
+#pragma unroll
+                for (int s = 0; s < KSG; ++s) {
+                    u32x4_t bv;
+                    if constexpr (SRC == DH_FROM_DZ) {
+                        const int g = 32 * s + 8 * q;
+                        if (g < G)
+                            bv = *reinterpret_cast<const u32x4_t*>(wrow + ((((g >> 3) ^ swzw(f, GCH))) << 3));
+                        else
+                            bv = u32x4_t{0u, 0u, 0u, 0u};
+                    } else {
+                        const int ga = 32 * s + 4 * q;
+                        const int gb = 32 * s + 16 + 4 * q;
+                        const u32x2_t lo2 = *reinterpret_cast<const u32x2_t*>(
+                            wrow + ((((ga >> 3) ^ swzw(f, GCH))) << 3) + (ga & 7));
+                        u32x2_t hi2 = u32x2_t{0u, 0u};
+                        if (gb < G)
+                            hi2 = *reinterpret_cast<const u32x2_t*>(
+                                wrow + ((((gb >> 3) ^ swzw(f, GCH))) << 3) + (gb & 7));
+                        bv = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+                    }
+                    p[t] = mfma16(ahi[s], bv, p[t]);
+                    if constexpr (SRC == DH_FROM_LABELS)
+                        p[t] = mfma16(alo[s], bv, p[t]);
+                }
+            }
+        }
+
+        // scatter-add P into acc[:, I_k]
+        if constexpr (DET) {
+#pragma unroll 1
+            for (int turn = 0; turn < 4; ++turn) {
+                __syncthreads();
+                if (turn == wv && active) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            atomicAdd(&acc[(4 * q + i) * H + col[t]], p[t][i]);
+                }
+            }
+        } else {
+            if (active) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        atomicAdd(&acc[(4 * q + i) * H + col[t]], p[t][i]);
+            }
+        }
+    }
+    __syncthreads();
+
+    if constexpr (DET) {
+        float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
+        for (int64_t i = threadIdx.x; i < R * H; i += 256)
+            dst[i] = acc[i];
+    } else {
+        for (int64_t i = threadIdx.x; i < R * H; i += 256) {
+            const int64_t b = b0 + i / H;
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[i]);
+        }
+    }
+}
+
+// dh[b, j] = sum over chunks c (in order) of part[c, b, j]
+__global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, float* __restrict__ dh,
+                                                   int64_t B, int64_t H, int nchunks, int rows_per_chunk)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * H) return;
+    const int64_t b = i / H, j = i % H;
+    float s = 0.f;
+    for (int c = 0; c < nchunks; ++c)
+        s += part[((int64_t)c * rows_per_chunk + b) * H + j];
+    dh[i] = s;
+}
+
+template <int G, int F>
+static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
+{
+    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
+    const dim3 grid(a.nchunks * a.ntiles), blk(256);
+    auto go = [&](auto kern) {
+        static bool attr = false;
+        if (!attr) {
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+            attr = true;
+        }
+        hipLaunchKernelGGL(kern, grid, blk, lds, s, a);
+    };
+    if (src == DH_FROM_DZ) {
+        if (det) go(k_group_dh<G, F, DH_FROM_DZ, true>); else go(k_group_dh<G, F, DH_FROM_DZ, false>);
+    } else {
+        if (det) go(k_group_dh<G, F, DH_FROM_LABELS, true>); else go(k_group_dh<G, F, DH_FROM_LABELS, false>);
+    }
+    return true;
+}
+
+template <int G>
+static bool launch_dh_g(int F, int src, bool det, const DhArgs& a, hipStream_t s)
+{
+    switch (F) {
+    case 32: return launch_dh_gf<G, 32>(src, det, a, s);
+    case 64: return launch_dh_gf<G, 64>(src, det, a, s);
+    case 128: return launch_dh_gf<G, 128>(src, det, a, s);
+    }
+    return false;
+}
+
+bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s)
+{
+    switch (G) {
+    case 16: return launch_dh_g<16>(F, src, det, a, s);
+    case 32: return launch_dh_g<32>(F, src, det, a, s);
+    case 64: return launch_dh_g<64>(F, src, det, a, s);
+    }
+    return false;
+}
+
+void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
+                      hipStream_t s)
+{
+    const int64_t n = B * H;
+    hipLaunchKernelGGL(k_dh_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, dh, B, H, nchunks,
+                       rows_per_chunk);
+}
+
+}  // namespace haste

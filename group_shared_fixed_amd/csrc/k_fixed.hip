@@ -1,0 +1,238 @@
+// Standard (per-label) fixed fan-in: the baseline the HASTE notes measure
+// against ("background" and "key findings" sections): every label has its own
+// F-index set, so each label is a thin dot product with no shared feature
+// tile and no matrix-core work.
+//
+// These kernels are an honest gfx950 implementation of that baseline, not a
+// strawman: batch rows are spread over lanes so every gather reads a
+// contiguous piece of a feature column of the feature-major copy hT (two
+// batch rows per 4-byte load), the index row and weights of a label are
+// loaded once per wave with coalesced reads and broadcast from registers,
+// outputs leave through LDS as contiguous rows, and the feature gradient
+// uses the same LDS accumulator and split-K reduction as the grouped path.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace haste {
+
+template <int F>
+__device__ __forceinline__ void load_label_row(const FixedArgs& a, int64_t l, int lane, int (&jv)[(F + 63) / 64],
+                                               float (&wv)[(F + 63) / 64])
+{
+#pragma unroll
+    for (int u = 0; u < (F + 63) / 64; ++u) {
+        const int f = lane + 64 * u;
+        jv[u] = 0;
+        wv[u] = 0.f;
+        if (f < F && l < a.L) {
+            jv[u] = a.idx1[l * F + f];
+            wv[u] = __uint_as_float((uint32_t)a.W[l * F + f] << 16);
+        }
+    }
+}
+
+// Z[b, l] = sum_f h[b, idx1[l, f]] W[l, f]; a wave owns 16 consecutive
+// labels at a time, lanes own batch-row pairs.
+template <int F>
+__global__ __launch_bounds__(256, 2) void k_fixed_fwd(FixedArgs a)
+{
+    constexpr int NU = (F + 63) / 64;
+    __shared__ float sZ[4][128 * 17];
+    const int lane = threadIdx.x & 63, wvi = threadIdx.x >> 6;
+    float* zt = sZ[wvi];
+    const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wvi;
+    const int64_t nblk = (a.L + 15) / 16;
+    const int64_t lb0 = gw * nblk / nw, lb1 = (gw + 1) * nblk / nw;
+    for (int64_t lb = lb0; lb < lb1; ++lb) {
+        for (int64_t bc = 0; bc < a.Bp; bc += 128) {
+            const int64_t b = bc + 2 * lane;
+            const bool ok = b < a.Bp;
+            for (int li = 0; li < 16; ++li) {
+                const int64_t l = lb * 16 + li;
+                int jv[NU];
+                float wv[NU];
+                load_label_row<F>(a, l, lane, jv, wv);
+                float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+                for (int f = 0; f < F; ++f) {
+                    const int j = __builtin_amdgcn_readlane(jv[f / 64], f % 64);
+                    const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                  __builtin_bit_cast(int, wv[f / 64]), f % 64));
+                    if (ok) {
+                        const uint32_t hv = *reinterpret_cast<const uint32_t*>(a.hT + (int64_t)j * a.Bp + b);
+                        z0 = fmaf(w, bf16lo_to_f32(hv), z0);
+                        z1 = fmaf(w, bf16hi_to_f32(hv), z1);
+                    }
+                }
+                zt[(2 * lane) * 17 + li] = z0;
+                zt[(2 * lane + 1) * 17 + li] = z1;
+            }
+            wave_sync();
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int row = it * 16 + (lane >> 2);
+                const int c4 = (lane & 3) * 4;
+                const int64_t b2 = bc + row;
+                if (b2 < a.B) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t l = lb * 16 + c4 + e;
+                        if (l < a.L) a.Z[b2 * a.L + l] = zt[row * 17 + c4 + e];
+                    }
+                }
+            }
+            wave_sync();
+        }
+    }
+}
+
+// dW[l, f] = sum_b dZ[b, l] h[b, idx1[l, f]]; a wave owns a contiguous label
+// range, lanes own batch-row pairs and keep 32 partial sums (one block of 32
+// slots at a time), which a butterfly over the 64 lanes reduces (each stage
+// halves the values per lane; lanes 2i and 2i+1 end with slot i of the block).
+template <int F>
+__global__ __launch_bounds__(256, 2) void k_fixed_bwd_w(FixedArgs a)
+{
+    constexpr int NU = (F + 63) / 64;
+    const int lane = threadIdx.x & 63, wvi = threadIdx.x >> 6;
+    const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wvi;
+    const int64_t l0 = gw * a.L / nw, l1 = (gw + 1) * a.L / nw;
+    for (int64_t l = l0; l < l1; ++l) {
+        int jv[NU];
+        float wv[NU];
+        load_label_row<F>(a, l, lane, jv, wv);
+#pragma unroll 1
+        for (int fb = 0; fb < F / 32; ++fb) {
+            float v[32];
+#pragma unroll
+            for (int f = 0; f < 32; ++f)
+                v[f] = 0.f;
+            for (int64_t bc = 0; bc < a.Bp; bc += 128) {
+                const int64_t b = bc + 2 * lane;
+                if (b < a.Bp) {
+                    const float d0 = b < a.B ? __uint_as_float((uint32_t)a.dZ[b * a.L + l] << 16) : 0.f;
+                    const float d1 =
+                        b + 1 < a.B ? __uint_as_float((uint32_t)a.dZ[(b + 1) * a.L + l] << 16) : 0.f;
+#pragma unroll
+                    for (int f = 0; f < 32; ++f) {
+                        const int ff = 32 * fb + f;
+                        int j;
+                        if constexpr (NU == 1) {
+                            j = __builtin_amdgcn_readlane(jv[0], ff);
+                        } else {
+                            j = fb < 2 ? __builtin_amdgcn_readlane(jv[0], ff & 63)
+                                       : __builtin_amdgcn_readlane(jv[NU - 1], ff & 63);
+                        }
+                        const uint32_t hv = *reinterpret_cast<const uint32_t*>(a.hT + (int64_t)j * a.Bp + b);
+                        v[f] = fmaf(d0, bf16lo_to_f32(hv), fmaf(d1, bf16hi_to_f32(hv), v[f]));
+                    }
+                }
+            }
+            int n = 32;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                if (n >= 2) {
+                    const bool up = (lane & o) != 0;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        if (i < n / 2) {
+                            const float keep = up ? v[i + n / 2] : v[i];
+                            const float send = up ? v[i] : v[i + n / 2];
+                            v[i] = keep + __shfl_xor(send, o, 64);
+                        }
+                    }
+                    n >>= 1;
+                } else {
+                    v[0] += __shfl_xor(v[0], o, 64);
+                }
+            }
+            if ((lane & 1) == 0) a.dW[l * F + 32 * fb + (lane >> 1)] = v[0];
+        }
+    }
+}
+
+// dh via an LDS accumulator of kDhRows batch rows per workgroup; wave w owns
+// rows 4w .. 4w+3 and walks every label of the workgroup's chunk, so each
+// accumulator cell is updated by one wave in label order (deterministic).
+template <int F, bool DET>
+__global__ __launch_bounds__(256, 2) void k_fixed_bwd_h(FixedArgs a)
+{
+    constexpr int NU = (F + 63) / 64;
+    constexpr int R = kDhRows;
+    extern __shared__ float acc[];
+    const int lane = threadIdx.x & 63, wvi = threadIdx.x >> 6;
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int tile = slot % a.ntiles;
+    const int chunk = (slot / a.ntiles) * 8 + xcd;
+    const int64_t lc0 = (int64_t)chunk * a.L / a.nchunks, lc1 = (int64_t)(chunk + 1) * a.L / a.nchunks;
+    const int64_t b0 = (int64_t)tile * R;
+    const int64_t H = a.H;
+    for (int64_t i = threadIdx.x; i < R * H; i += 256)
+        acc[i] = 0.f;
+    __syncthreads();
+    for (int64_t l = lc0; l < lc1; ++l) {
+        int jv[NU];
+        float wv[NU];
+        load_label_row<F>(a, l, lane, jv, wv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t b = b0 + 4 * wvi + r;
+            const float d = b < a.B ? __uint_as_float((uint32_t)a.dZ[b * a.L + l] << 16) : 0.f;
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                if (lane + 64 * u < F)
+                    atomicAdd(&acc[(4 * wvi + r) * H + jv[u]], d * wv[u]);
+        }
+    }
+    __syncthreads();
+    if constexpr (DET) {
+        float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
+        for (int64_t i = threadIdx.x; i < R * H; i += 256)
+            dst[i] = acc[i];
+    } else {
+        for (int64_t i = threadIdx.x; i < R * H; i += 256) {
+            const int64_t b = b0 + i / H;
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[i]);
+        }
+    }
+}
+
+bool launch_fixed_fwd(int F, const FixedArgs& a, int grid, hipStream_t s)
+{
+    switch (F) {
+    case 32: hipLaunchKernelGGL(k_fixed_fwd<32>, dim3(grid), dim3(256), 0, s, a); return true;
+    case 64: hipLaunchKernelGGL(k_fixed_fwd<64>, dim3(grid), dim3(256), 0, s, a); return true;
+    case 128: hipLaunchKernelGGL(k_fixed_fwd<128>, dim3(grid), dim3(256), 0, s, a); return true;
+    }
+    return false;
+}
+
+bool launch_fixed_bwd_w(int F, const FixedArgs& a, int grid, hipStream_t s)
+{
+    switch (F) {
+    case 32: hipLaunchKernelGGL(k_fixed_bwd_w<32>, dim3(grid), dim3(256), 0, s, a); return true;
+    case 64: hipLaunchKernelGGL(k_fixed_bwd_w<64>, dim3(grid), dim3(256), 0, s, a); return true;
+    case 128: hipLaunchKernelGGL(k_fixed_bwd_w<128>, dim3(grid), dim3(256), 0, s, a); return true;
+    }
+    return false;
+}
+
+bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s)
+{
+    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
+    const dim3 grid(a.nchunks * a.ntiles), blk(256);
+#define HASTE_FIXED_DH(FF)                                                                           \
+    if (det) hipLaunchKernelGGL((k_fixed_bwd_h<FF, true>), grid, blk, lds, s, a);                    \
+    else hipLaunchKernelGGL((k_fixed_bwd_h<FF, false>), grid, blk, lds, s, a);                       \
+    return true;
+    switch (F) {
+    case 32: HASTE_FIXED_DH(32)
+    case 64: HASTE_FIXED_DH(64)
+    case 128: HASTE_FIXED_DH(128)
+    }
+#undef HASTE_FIXED_DH
+    return false;
+}
+
+}  // namespace haste

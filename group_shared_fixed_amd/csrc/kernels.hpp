@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI (haste_api.hip) and the HIP
+// kernels.  Nothing here is exported from libhaste.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace haste {
+
+// Batch rows per dh accumulator tile (one LDS accumulator of kDhRows x H fp32
+// per workgroup).
+constexpr int kDhRows = 16;
+// Largest batch the label cursors of the BCE paths cover (4 per lane).
+constexpr int kMaxLabelBatch = 256;
+
+enum FwdMode { FWD_Z = 0, FWD_BCE = 1, STEP_DW = 2, BWD_W = 3 };
+enum DhSrc { DH_FROM_DZ = 0, DH_FROM_LABELS = 1 };
+
+struct FwdArgs {
+    const uint16_t* hT;   // H x Bp bf16, Bp = B rounded up to 32, zero padded
+    int64_t Bp, B;
+    const int32_t* idx;   // K x F
+    const uint16_t* W;    // L x F bf16
+    int64_t K;
+    const int32_t* y_rowptr;
+    const int32_t* y_col;
+    float scale;
+    float* Z;             // B x L fp32 (FWD_Z; optional otherwise)
+    uint16_t* dZ;         // B x L bf16 (FWD_BCE output, BWD_W input)
+    float* dW;            // L x F fp32 (STEP_DW)
+    double* loss;         // 1 double, accumulated (optional)
+};
+
+struct DhArgs {
+    const uint16_t* hT;   // H x Bp bf16 (DH_FROM_LABELS)
+    int64_t Bp, B, H;
+    const int32_t* idx;
+    const uint16_t* W;
+    int64_t K;
+    const uint16_t* dZ;   // B x L bf16 (DH_FROM_DZ)
+    const int32_t* y_rowptr;
+    const int32_t* y_col;
+    float scale;
+    int nchunks, ntiles;
+    float* dh;            // B x H fp32, pre-zeroed (atomic flush)
+    float* part;          // nchunks x (ntiles*kDhRows) x H fp32 (deterministic flush)
+};
+
+struct FixedArgs {
+    const uint16_t* hT;
+    int64_t Bp, B, H;
+    const int32_t* idx1;  // L x F
+    const uint16_t* W;    // L x F
+    int64_t L;
+    const uint16_t* dZ;   // B x L bf16
+    float* Z;
+    float* dW;
+    int nchunks, ntiles;
+    float* dh;
+    float* part;
+};
+
+// Each launcher returns false when no kernel exists for (G, F).
+bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s);
+bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s);
+void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
+                      hipStream_t s);
+bool launch_fixed_fwd(int F, const FixedArgs& a, int grid, hipStream_t s);
+bool launch_fixed_bwd_w(int F, const FixedArgs& a, int grid, hipStream_t s);
+bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s);
+void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s);
+void launch_fill_f32(float* p, int64_t n, hipStream_t s);
+void launch_fill_f64(double* p, int64_t n, hipStream_t s);
+void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
+void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s);
+void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B, int64_t L, int32_t* bad,
+                            hipStream_t s);
+
+}  // namespace haste

@@ -1,0 +1,185 @@
+/*
+ * libhaste — group-shared fixed fan-in sparse output layer on AMD MI355X
+ * (gfx950), C ABI.
+ *
+ * Method: "HASTE: Hardware-Aware Dynamic Sparse Training for Large Output
+ * Spaces" (papernotes.org notes on the ICML 2026 paper).  L = K*G labels are
+ * split into K groups of G labels; the G labels of group k share one fan-in
+ * index set I_k of F distinct feature columns out of H ("group-shared fixed
+ * fan-in" section), and label l = k*G + g has its own weights W[l, 0..F).
+ *
+ * Shapes and layouts (all row-major, contiguous):
+ *   h    B x H  bf16   features (the encoder output feeding the layer)
+ *   idx  K x F  int32  I_k = idx[k, :], entries in [0, H), strictly increasing
+ *   W    L x F  bf16   W[l, f] multiplies h[:, idx[l / G, f]]
+ *   Z    B x L  fp32   logits
+ *   dZ   B x L  bf16   upstream gradient of the logits
+ *   dW   L x F  fp32   weight gradient
+ *   dh   B x H  fp32   feature gradient
+ *   labels: the B x L 0/1 label matrix Y as CSR, y_rowptr[B + 1] and
+ *           y_col[y_rowptr[B]]; row b lists the positive label ids of sample
+ *           b, strictly increasing (haste_validate_labels checks this).
+ * bf16 values are passed as their 16-bit patterns (haste_bf16).
+ *
+ * Conventions shared by every call:
+ *   - All pointers except `workspace` arguments of size 0 and the optional
+ *     outputs marked "nullable" are device pointers the caller allocated; the
+ *     library never allocates or frees them, keeps no pointer after the call
+ *     returns and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (0 = default stream) and return
+ *     before the GPU work finishes; outputs are valid after the stream
+ *     synchronises.  Outputs are overwritten, never accumulated into.
+ *   - Arguments are validated on the host before any HIP call; a negative
+ *     haste_status is returned without touching the GPU.  HASTE_ERR_HIP
+ *     means a launch failed (hipGetLastError).  Faults inside kernels surface
+ *     at the next synchronisation.  The hot calls do not re-validate index
+ *     sets or labels: out-of-range or unsorted entries are undefined behaviour
+ *     (use haste_validate_idx / haste_validate_labels).
+ *   - Supported: G in {16, 32, 64} (G = 1 for the haste_fixed_* baseline),
+ *     F in {32, 64, 128}, F <= H <= 1024, L = K*G < 2^31 - 64; label-consuming
+ *     calls need B <= 256.  Pointers must be 16-byte aligned.  Other shapes
+ *     return HASTE_ERR_UNSUPPORTED; the CPU oracle accepts any shape.
+ *   - `workspace` is caller-owned device scratch of at least
+ *     haste_workspace_size(op, ...) bytes, 256-byte aligned.
+ *   - Calls that overlap on one workspace race; separate streams need
+ *     separate workspaces.
+ */
+#ifndef HASTE_H
+#define HASTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t haste_bf16;
+
+typedef enum {
+    HASTE_OK = 0,
+    HASTE_ERR_NULL = -1,         /* a required pointer is NULL */
+    HASTE_ERR_DIM = -2,          /* a size is < 1, or sizes are inconsistent */
+    HASTE_ERR_UNSUPPORTED = -3,  /* valid shape without a kernel (see above) */
+    HASTE_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+    HASTE_ERR_WORKSPACE = -5,    /* workspace missing, too small or misaligned */
+    HASTE_ERR_INDEX = -6,        /* reserved for validation results */
+    HASTE_ERR_HIP = -7           /* a HIP launch failed */
+} haste_status;
+
+/* Reduction of the feature gradient across groups. */
+typedef enum {
+    HASTE_DH_ATOMIC = 0,         /* fp32 atomic adds; summation order varies run to run */
+    HASTE_DH_DETERMINISTIC = 1   /* per-chunk partials reduced in fixed order; bitwise reproducible */
+} haste_dh_mode;
+
+typedef enum {
+    HASTE_OP_FWD = 0,
+    HASTE_OP_BWD_W = 1,
+    HASTE_OP_BWD_H = 2,
+    HASTE_OP_FWD_BCE = 3,
+    HASTE_OP_STEP = 4,
+    HASTE_OP_FIXED_FWD = 5,
+    HASTE_OP_FIXED_BWD_W = 6,
+    HASTE_OP_FIXED_BWD_H = 7
+} haste_op;
+
+/* Workspace bytes `op` needs for this shape (K = L and G = 1 for the
+ * haste_fixed_* ops).  Returns 0 for an invalid op. */
+size_t haste_workspace_size(int op, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode);
+
+/* Forward logits.  Z[b, l] = sum_f h[b, idx[l/G, f]] * W[l, f]; per group
+ * Z_k = H_k W_k^T with H_k = h[:, I_k] ("overall framework" logit formula and
+ * "gather-once + dense MMA kernel" section).  Z is B x L fp32. */
+int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, float* Z,
+              int64_t B, int64_t H, int64_t K, int64_t G, int64_t F,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Weight gradient.  dW[l, f] = sum_b dZ[b, l] * h[b, idx[l/G, f]]; per group
+ * dW_k = dZ_k^T H_k ("gather-once + dense MMA kernel").  dW is L x F fp32. */
+int haste_bwd_w(const haste_bf16* h, const int32_t* idx, const haste_bf16* dZ, float* dW,
+                int64_t B, int64_t H, int64_t K, int64_t G, int64_t F,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Feature gradient.  dh[b, j] = sum over (l, f) with idx[l/G, f] == j of
+ * dZ[b, l] * W[l, f]: the per-group products dZ_k W_k added into the
+ * overlapping columns I_k and reduced across groups ("gather-once + dense
+ * MMA kernel": split-K reduction).  dh is B x H fp32; columns in no index set
+ * are 0.  dh_mode selects the cross-workgroup reduction (haste_dh_mode). */
+int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, float* dh,
+                int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward with the BCE-gradient epilogue: dZ = scale * (sigmoid(Z) - Y)
+ * rounded to bf16 (objective of the "head-tail split" section; mean over
+ * samples, sum over labels: pass scale = 1/B).  Z (nullable) also receives
+ * the fp32 logits.  loss (nullable, 1 double on the device) receives
+ * scale * sum_{b,l} [max(z,0) + log(1 + e^-|z|) - y z]. */
+int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+                  const int32_t* y_rowptr, const int32_t* y_col, float scale,
+                  haste_bf16* dZ, float* Z, double* loss,
+                  int64_t B, int64_t H, int64_t K, int64_t G, int64_t F,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One training pass of the layer: forward, BCE gradient, dW and dh, with dZ
+ * kept on chip in fp32 (fed to the matrix cores as bf16 hi + lo parts) and
+ * never written to memory.  dW (L x F fp32) and dh (B x H fp32) are
+ * required; Z (B x L fp32) and loss (1 double) are nullable. */
+int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+               const int32_t* y_rowptr, const int32_t* y_col, float scale,
+               float* dW, float* dh, float* Z, double* loss,
+               int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* haste_step plus timing: when `events` is non-NULL, events[0..4] (created
+ * by the caller) are recorded on `stream` at the phase boundaries of the
+ * pass: [0] start, [1] after the feature-major copy of h and output
+ * clearing, [2] after the forward + BCE + dW kernel, [3] after the dh kernel,
+ * [4] after the deterministic reduction (same point as [3] in atomic mode).
+ * For benchmarks that need per-kernel durations on the caller's stream.
+ * Same work, arguments and errors as haste_step. */
+int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+                     const int32_t* y_rowptr, const int32_t* y_col, float scale,
+                     float* dW, float* dh, float* Z, double* loss,
+                     int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
+/* G = 1 baseline: standard fixed fan-in with one index set per label
+ * (idx1 is L x F), thin per-label dot products without a shared tile
+ * ("background" and "key findings": the micro-benchmark baseline).  Same
+ * formulas, shapes and conventions as haste_fwd / haste_bwd_w / haste_bwd_h
+ * with K = L and G = 1. */
+int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* W, float* Z,
+                    int64_t B, int64_t H, int64_t L, int64_t F,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+int haste_fixed_bwd_w(const haste_bf16* h, const int32_t* idx1, const haste_bf16* dZ, float* dW,
+                      int64_t B, int64_t H, int64_t L, int64_t F,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf16* W, float* dh,
+                      int64_t B, int64_t H, int64_t L, int64_t F, int dh_mode,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Count (into *bad, a device int32 the call zeroes first) the index rows
+ * that have an entry outside [0, H) or are not strictly increasing. */
+int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad,
+                       hipStream_t stream);
+
+/* Count (into *bad, zeroed first) the samples whose CSR label row is not
+ * non-decreasing in y_rowptr, has an id outside [0, L) or is not strictly
+ * increasing. */
+int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t B, int64_t L, int32_t* bad,
+                          hipStream_t stream);
+
+/* Static text for a haste_status value. */
+const char* haste_status_string(int status);
+
+/* Library version string. */
+const char* haste_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HASTE_H */

@@ -32,9 +32,16 @@
  * depend on the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below use (reported next to oracle timings). */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 static double bf16_to_double(uint16_t u)
 {

@@ -48,6 +48,8 @@ def load(path: str | None = None):
     lib.oracle_bce.restype = None
     lib.oracle_step.argtypes = [P, P, P, P, P, ctypes.c_double, P, P, P, P, P, I, I, I, I, I]
     lib.oracle_step.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -66,6 +68,10 @@ def _check(name, a, dtype, shape):
 def _dims(idx, G, h=None, B=None, H=None):
     K, F = idx.shape
     return K, F, K * G
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
 
 
 def oracle_fwd(h, idx, W, G, lib=None):

@@ -1,0 +1,120 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/haste.h declares, and rejects bad arguments on the host before any
+HIP call (so these run on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from group_shared_fixed_amd import binding as hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "haste.h")
+
+OK, NULL, DIM, UNSUP, ALIGN, WS = 0, -1, -2, -3, -4, -5
+P = ctypes.c_void_p
+A = P(0x100000)          # 16-byte aligned fake device pointer (never dereferenced)
+MIS = P(0x100008)        # misaligned fake pointer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(haste_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hb.LIB_PATH):
+        pytest.fail("libhaste.so is not built (run __graft_entry__.build())")
+    return hb.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), f"libhaste.so does not export {n}"
+        assert n in hb.SIGNATURES, f"binding has no signature for {n}"
+
+
+def test_version_and_status_strings(L):
+    assert b"gfx950" in L.haste_version()
+    for code in range(-7, 1):
+        assert L.haste_status_string(code)
+    assert L.haste_status_string(5) == b"unknown status"
+
+
+def test_workspace_size(L):
+    # feature-major copy of h: H * round_up(B, 32) * 2 bytes, 256-aligned
+    assert L.haste_workspace_size(0, 128, 768, 93748, 32, 64, 0) == 768 * 128 * 2
+    assert L.haste_workspace_size(0, 100, 768, 10, 32, 64, 0) == 768 * 128 * 2
+    assert L.haste_workspace_size(2, 128, 768, 10, 32, 64, 0) == 0           # atomic dh needs none
+    det = L.haste_workspace_size(2, 128, 768, 10, 32, 64, 1)
+    assert det > 0 and det % 256 == 0
+    assert L.haste_workspace_size(4, 128, 768, 10, 32, 64, 1) == 768 * 128 * 2 + det
+    assert L.haste_workspace_size(99, 128, 768, 10, 32, 64, 0) == 0
+
+
+def _fwd(L, h=A, idx=A, W=A, Z=A, B=128, H=768, K=100, G=32, F=64, ws=A, wsb=1 << 30):
+    return L.haste_fwd(h, idx, W, Z, B, H, K, G, F, ws, wsb, None)
+
+
+def test_fwd_rejects(L):
+    assert _fwd(L, h=None) == NULL
+    assert _fwd(L, Z=None) == NULL
+    assert _fwd(L, B=0) == DIM
+    assert _fwd(L, K=-1) == DIM
+    assert _fwd(L, F=64, H=32) == DIM                 # F distinct columns out of H
+    assert _fwd(L, G=8) == UNSUP
+    assert _fwd(L, G=1) == UNSUP                      # G = 1 is the haste_fixed_* path
+    assert _fwd(L, F=48) == UNSUP
+    assert _fwd(L, H=2048) == UNSUP
+    assert _fwd(L, K=(1 << 31) // 32) == UNSUP        # L = K*G must fit int32 label ids
+    assert _fwd(L, W=MIS) == ALIGN
+    assert _fwd(L, Z=MIS) == ALIGN
+    assert _fwd(L, ws=None) == WS
+    assert _fwd(L, wsb=100) == WS
+    assert _fwd(L, ws=P(0x100010)) == WS             # not 256-aligned
+
+
+def test_bwd_rejects(L):
+    assert L.haste_bwd_w(A, A, None, A, 128, 768, 10, 32, 64, A, 1 << 30, None) == NULL
+    assert L.haste_bwd_w(A, A, A, A, 128, 768, 10, 32, 96, A, 1 << 30, None) == UNSUP
+    assert L.haste_bwd_h(A, A, A, None, 128, 768, 10, 32, 64, 0, None, 0, None) == NULL
+    assert L.haste_bwd_h(A, A, A, A, 128, 768, 10, 32, 64, 2, None, 0, None) == UNSUP   # bad mode
+    assert L.haste_bwd_h(A, A, A, A, 128, 768, 10, 32, 64, 1, None, 0, None) == WS      # det needs ws
+    assert L.haste_bwd_h(A, A, MIS, A, 128, 768, 10, 32, 64, 0, None, 0, None) == ALIGN
+
+
+def test_label_paths_reject(L):
+    f = L.haste_fwd_bce
+    assert f(A, A, A, None, A, 1.0, A, None, None, 128, 768, 10, 32, 64, A, 1 << 30, None) == NULL
+    assert f(A, A, A, A, A, 1.0, None, None, None, 128, 768, 10, 32, 64, A, 1 << 30, None) == NULL
+    assert f(A, A, A, A, A, 1.0, A, None, None, 300, 768, 10, 32, 64, A, 1 << 30, None) == UNSUP   # B > 256
+    assert f(A, A, A, A, A, 0.0, A, None, None, 128, 768, 10, 32, 64, A, 1 << 30, None) == DIM    # scale
+    assert f(A, A, A, A, A, 1.0, A, MIS, None, 128, 768, 10, 32, 64, A, 1 << 30, None) == ALIGN   # Z
+    s = L.haste_step
+    assert s(A, A, A, A, A, 1.0, None, A, None, None, 128, 768, 10, 32, 64, 0, A, 1 << 30, None) == NULL
+    assert s(A, A, A, A, A, 1.0, A, A, None, None, 128, 768, 10, 32, 64, 5, A, 1 << 30, None) == UNSUP
+    assert s(A, A, A, A, A, 1.0, A, A, None, None, 128, 768, 10, 32, 64, 1, A, 1000, None) == WS
+
+
+def test_fixed_rejects(L):
+    assert L.haste_fixed_fwd(A, None, A, A, 128, 768, 1000, 64, A, 1 << 30, None) == NULL
+    assert L.haste_fixed_fwd(A, A, A, A, 128, 768, 1000, 80, A, 1 << 30, None) == UNSUP
+    assert L.haste_fixed_bwd_w(A, A, A, A, 128, 768, 0, 64, A, 1 << 30, None) == DIM
+    assert L.haste_fixed_bwd_h(A, A, A, A, 128, 768, 1000, 64, 1, None, 0, None) == WS
+
+
+def test_validate_rejects(L):
+    assert L.haste_validate_idx(None, 10, 64, 768, A, None) == NULL
+    assert L.haste_validate_idx(A, 0, 64, 768, A, None) == DIM
+    assert L.haste_validate_labels(A, A, 0, 10, A, None) == DIM
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(hb.HasteError):
+        hb.lib(str(tmp_path / "nope.so"))

@@ -1,0 +1,132 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle cannot redo a whole 3M-label pass in seconds, so
+it checks sampled outputs that it computes exactly:
+  * Z and dh rows of sampled samples (the oracle runs on those batch rows and
+    all labels; dh of a row depends only on that row),
+  * dW rows of sampled label groups (the oracle runs on those groups and all
+    batch rows, with the labels restricted to the groups),
+and properties that hold at any size: <dh, h> = <dW, W> for the fused step
+(both equal <dZ, Z>), and bitwise repeatability of the deterministic mode."""
+
+import numpy as np
+import pytest
+
+import group_shared_fixed_amd as hs
+from gpu_util import assert_parity, say, to_dev_bf16, to_dev_i32, to_host
+from oracle import oracle as O
+from synthetic import get_workload, make_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+ROWS = (0, 1, -1)          # sampled batch rows (negative = from the end)
+NGROUPS = 48               # groups per sampled group slice
+
+
+def rows_of(B):
+    return sorted({r % B for r in ROWS} | {B // 2})
+
+
+def label_rows(rowptr, col, rows):
+    rp = [0]
+    cols = []
+    for b in rows:
+        c = col[rowptr[b]:rowptr[b + 1]]
+        cols.append(c)
+        rp.append(rp[-1] + c.size)
+    return np.array(rp, np.int32), (np.concatenate(cols).astype(np.int32) if rp[-1] else np.zeros(0, np.int32))
+
+
+def label_groups(rowptr, col, lo, hi):
+    """Labels restricted to ids [lo, hi), renumbered from 0."""
+    rp = [0]
+    cols = []
+    for b in range(rowptr.size - 1):
+        c = col[rowptr[b]:rowptr[b + 1]]
+        c = c[(c >= lo) & (c < hi)] - lo
+        cols.append(c)
+        rp.append(rp[-1] + c.size)
+    return np.array(rp, np.int32), (np.concatenate(cols).astype(np.int32) if rp[-1] else np.zeros(0, np.int32))
+
+
+_inputs = {}
+
+
+def inputs(name, dZ=False):
+    key = (name, dZ)
+    if key not in _inputs:
+        _inputs.clear()
+        w = get_workload(name)
+        say(f"  generating {name} (L={w.L}, G={w.G}, F={w.F}, B={w.B})")
+        _inputs[key] = (w, make_inputs(w, dZ=dZ))
+    return _inputs[key]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["amazon3m_shaped", "amazon670k_shaped", "lfpaper8600k_shaped"])
+def test_step_fullsize_sampled(name):
+    w, d = inputs(name)
+    B, L, G, K, H = w.B, w.L, w.G, w.K, w.H
+    s = 1.0 / B
+    h, idx, W = to_dev_bf16(d["h"]), to_dev_i32(d["idx"]), to_dev_bf16(d["W"])
+    rp, col = to_dev_i32(d["y_rowptr"]), to_dev_i32(d["y_col"])
+    say(f"  step[det] {name}")
+    out = hs.step(h, idx, W, rp, col, s, G, mode="det", want_Z=True)
+    dW = to_host(out["dW"])
+    dh = to_host(out["dh"])
+    rows = rows_of(B)
+    Zrows = to_host(out["Z"][rows])
+    del out
+    # adjoint identity on GPU outputs
+    a = float(np.dot(dh.ravel().astype(np.float64), (d["h"].astype(np.uint32) << 16).view(np.float32)
+                     .ravel().astype(np.float64)))
+    wv = (d["W"].astype(np.uint32) << 16).view(np.float32)
+    bsum = float(np.einsum("lf,lf->", dW.astype(np.float64), wv.astype(np.float64)))
+    say(f"    <dh,h>={a:.9g} <dW,W>={bsum:.9g}")
+    assert abs(a - bsum) <= 1e-4 * max(abs(a), abs(bsum), 1e-30)
+    # sampled batch rows: Z and dh
+    rpr, colr = label_rows(d["y_rowptr"], d["y_col"], rows)
+    say(f"    oracle on rows {rows}")
+    ref = O.oracle_step(np.ascontiguousarray(d["h"][rows]), d["idx"], d["W"], rpr, colr, s, G, want_dW=False)
+    assert_parity(Zrows, ref["Z"], "Z rows")
+    assert_parity(dh[rows], ref["dh"], "dh rows")
+    del ref
+    # sampled group slices: dW
+    for k0 in (0, K // 2 - NGROUPS // 2, K - NGROUPS):
+        k1 = k0 + NGROUPS
+        rpg, colg = label_groups(d["y_rowptr"], d["y_col"], k0 * G, k1 * G)
+        ref = O.oracle_step(d["h"], np.ascontiguousarray(d["idx"][k0:k1]), np.ascontiguousarray(d["W"][k0 * G:k1 * G]),
+                            rpg, colg, s, G, want_dh=False)
+        assert_parity(dW[k0 * G:k1 * G], ref["dW"], f"dW groups [{k0},{k1})")
+    # atomic mode agrees with deterministic mode, deterministic mode repeats
+    say("  step[atomic] and step[det] repeat")
+    dh_at = to_host(hs.step(h, idx, W, rp, col, s, G, mode="atomic")["dh"])
+    assert_parity(dh_at, dh, "dh atomic vs det", rel=1e-5, mabs=1e-6)
+    dh2 = to_host(hs.step(h, idx, W, rp, col, s, G, mode="det")["dh"])
+    assert (dh2.view(np.uint32) == dh.view(np.uint32)).all(), "deterministic dh not bitwise repeatable"
+
+
+@pytest.mark.timeout(900)
+def test_unfused_calls_fullsize_sampled():
+    name = "amazon3m_shaped"
+    w, d = inputs(name, dZ=True)
+    B, L, G, K, H = w.B, w.L, w.G, w.K, w.H
+    h, idx, W, dZ = to_dev_bf16(d["h"]), to_dev_i32(d["idx"]), to_dev_bf16(d["W"]), to_dev_bf16(d["dZ"])
+    rows = rows_of(B)
+    say(f"  fwd {name}")
+    Z = hs.fwd(h, idx, W, G)
+    Zr = to_host(Z[rows])
+    del Z
+    assert_parity(Zr, O.oracle_fwd(np.ascontiguousarray(d["h"][rows]), d["idx"], d["W"], G), "Z rows")
+    say(f"  bwd_h {name}")
+    dZr = np.ascontiguousarray(d["dZ"][rows])
+    ref_dh = O.oracle_bwd_h(dZr, d["idx"], d["W"], G, H)
+    for mode in ("atomic", "det"):
+        dh = to_host(hs.bwd_h(dZ, idx, W, G, H, mode=mode))
+        assert_parity(dh[rows], ref_dh, f"dh rows [{mode}]")
+    say(f"  bwd_w {name}")
+    dW = to_host(hs.bwd_w(h, idx, dZ, G))
+    for k0 in (0, K // 3, K - NGROUPS):
+        k1 = k0 + NGROUPS
+        ref = O.oracle_bwd_w(d["h"], np.ascontiguousarray(d["idx"][k0:k1]),
+                             np.ascontiguousarray(d["dZ"][:, k0 * G:k1 * G]), G)
+        assert_parity(dW[k0 * G:k1 * G], ref, f"dW groups [{k0},{k1})")
