@@ -51,9 +51,11 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     constexpr int NCH = F / 8;
     constexpr int GCH = G / 8;
     constexpr int R = kDhRows;
+    constexpr bool LAB = (SRC == DH_FROM_LABELS);
+    constexpr int NU = F / 32;          // gather loads per lane (16 rows x F slots)
 
-    extern __shared__ float acc[];      // R x H
-    __shared__ __attribute__((aligned(16))) uint16_t sH[SRC == DH_FROM_LABELS ? 4 : 1][SRC == DH_FROM_LABELS ? R * F : 8];
+    extern __shared__ float acc[];      // R rows, stride dh_stride(H)
+    __shared__ __attribute__((aligned(16))) uint16_t sH[LAB ? 4 : 1][LAB ? R * F : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sWT[4][F * G];
 
     const int lane = threadIdx.x & 63;
@@ -70,42 +72,94 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     const int64_t b0 = (int64_t)tile * R;
     const int64_t L = a.K * G;
     const int64_t H = a.H;
+    const int64_t S = dh_stride(H);
 
-    for (int64_t i = threadIdx.x; i < R * H; i += 256)
+    for (int64_t i = threadIdx.x; i < R * S; i += 256)
         acc[i] = 0.f;
 
     LabelCursor cur;
-    if constexpr (SRC == DH_FROM_LABELS)
+    if constexpr (LAB)
         cur.init(a.y_rowptr, a.y_col, b0 + r16, a.B, kc0 * G);
     const float scale = a.scale;
     const float inv_s = 1.0f / a.scale;
     const int64_t brow = b0 + r16;            // batch row of this lane's A rows
     const bool brow_ok = brow < a.B;
 
-    __syncthreads();
+    // per-round inputs, requested one round ahead
+    auto load_col = [&](int64_t kk, int (&cl)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            cl[t] = a.idx[kk * F + 16 * t + r16];
+    };
+    auto load_w = [&](int64_t kk, u32x4_t (&wr)[GT][KSF]) {
+#pragma unroll
+        for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+            for (int s = 0; s < KSF; ++s)
+                wr[gt][s] = ldg16(a.W + ((kk * G + 16 * gt + r16) * F + 32 * s + 8 * q));
+    };
+    auto load_gcol = [&](int64_t kk, int (&gc)[NU]) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            gc[u] = a.idx[kk * F + 32 * u + (lane & 31)];
+    };
+    // lane (slot 32u + lane%32, half) <- 8 rows b0 + 8*half .. of feature column gc[u]
+    auto gather = [&](const int (&gc)[NU], u32x4_t (&hv)[NU]) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            hv[u] = ldg16(a.hT + (int64_t)gc[u] * a.Bp + b0 + 8 * (lane >> 5));
+    };
+    // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
+    auto load_dz = [&](int64_t kk, u32x4_t (&dv)[KSG]) {
+#pragma unroll
+        for (int s = 0; s < KSG; ++s) {
+            dv[s] = u32x4_t{0u, 0u, 0u, 0u};
+            if (brow_ok && 32 * s + 8 * q < G)
+                dv[s] = ldg16(a.dZ + brow * L + kk * G + 32 * s + 8 * q);
+        }
+    };
 
     const int64_t ng = kc1 - kc0;
     const int64_t nrounds = (ng + 3) / 4;
+    auto group_of = [&](int64_t rd) {
+        const int64_t kk = kc0 + 4 * rd + wv;
+        return kk < kc1 ? kk : kc1 - 1;       // idle waves reload a valid group
+    };
+
+    int col[NT], col_n[NT];
+    u32x4_t wreg[GT][KSF], wreg_n[GT][KSF];
+    int gcol[LAB ? NU : 1], gcol_n[LAB ? NU : 1];
+    u32x4_t hv[LAB ? NU : 1], hv_n[LAB ? NU : 1];
+    u32x4_t dv[LAB ? 1 : KSG], dv_n[LAB ? 1 : KSG];
+    if (ng > 0) {
+        const int64_t kk = group_of(0);
+        load_col(kk, col);
+        load_w(kk, wreg);
+        if constexpr (LAB) {
+            load_gcol(kk, gcol);
+            gather(gcol, hv);
+        } else {
+            load_dz(kk, dv);
+        }
+    }
+
+    __syncthreads();
+
     for (int64_t rd = 0; rd < nrounds; ++rd) {
         const int64_t k = kc0 + 4 * rd + wv;
         const bool active = k < kc1;
+        const int64_t kn = group_of(rd + 1 < nrounds ? rd + 1 : rd);
+        load_col(kn, col_n);
+        load_w(kn, wreg_n);
+        if constexpr (LAB) load_gcol(kn, gcol_n);
+        else load_dz(kn, dv_n);
+
         f32x4_t p[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             p[t] = zero4();
-        int col[NT];
 
         if (active) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                col[t] = a.idx[k * F + 16 * t + r16];
-            // W_k rows: lane (label 16gt + r16, q) holds slots 32s + 8q .. +8
-            u32x4_t wreg[GT][KSF];
-#pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                for (int s = 0; s < KSF; ++s)
-                    wreg[gt][s] = ldg16(a.W + ((k * G + 16 * gt + r16) * F + 32 * s + 8 * q));
             // W_k^T into LDS for the B operand of P = dZ W (contraction over labels)
             uint16_t* wt = sWT[wv];
 #pragma unroll
@@ -122,29 +176,24 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                     }
 
             u32x4_t ahi[KSG], alo[KSG];
-            if constexpr (SRC == DH_FROM_DZ) {
-                // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
+            if constexpr (!LAB) {
 #pragma unroll
                 for (int s = 0; s < KSG; ++s) {
-                    ahi[s] = u32x4_t{0u, 0u, 0u, 0u};
+                    ahi[s] = dv[s];
                     alo[s] = u32x4_t{0u, 0u, 0u, 0u};
-                    if (brow_ok && 32 * s + 8 * q < G)
-                        ahi[s] = ldg16(a.dZ + brow * L + k * G + 32 * s + 8 * q);
                 }
             } else {
-                // gather the tile of H_k: lane (slot 32u + lane%32, half) <- 8 rows
+                // transposed copy of the gathered tile: [row][slot]
                 uint16_t* ht = sH[wv];
 #pragma unroll
-                for (int u = 0; u < F / 32; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     const int f = 32 * u + (lane & 31);
                     const int half = lane >> 5;
-                    const int jc = a.idx[k * F + f];
-                    const u32x4_t v = ldg16(a.hT + (int64_t)jc * a.Bp + b0 + 8 * half);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int r = 8 * half + e;
                         ht[r * F + ((((f >> 3) ^ swz16(r, NCH))) << 3) + (f & 7)] =
-                            (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+                            (uint16_t)((e & 1) ? (hv[u][e >> 1] >> 16) : (hv[u][e >> 1] & 0xffffu));
                     }
                 }
                 wave_sync();
@@ -197,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 #pragma unroll
                 for (int s = 0; s < KSG; ++s) {
                     u32x4_t bv;
-                    if constexpr (SRC == DH_FROM_DZ) {
+                    if constexpr (!LAB) {
                         const int g = 32 * s + 8 * q;
                         if (g < G)
                             bv = *reinterpret_cast<const u32x4_t*>(wrow + ((((g >> 3) ^ swzw(f, GCH))) << 3));
@@ -215,33 +264,56 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                         bv = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
                     }
                     p[t] = mfma16(ahi[s], bv, p[t]);
-                    if constexpr (SRC == DH_FROM_LABELS)
+                    if constexpr (LAB)
                         p[t] = mfma16(alo[s], bv, p[t]);
                 }
             }
         }
 
-        // scatter-add P into acc[:, I_k]
-        if constexpr (DET) {
+        // next round's gathered rows (their index row arrived meanwhile)
+        if constexpr (LAB) gather(gcol_n, hv_n);
+
+        // scatter-add P into acc[:, I_k] with plain read-add-write: the waves
+        // take turns (barrier-separated) so every accumulator cell is updated
+        // by one wave at a time and in group order; inside one wave the index
+        // set is duplicate-free, so no two lanes touch the same cell.
 #pragma unroll 1
-            for (int turn = 0; turn < 4; ++turn) {
-                __syncthreads();
-                if (turn == wv && active) {
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            atomicAdd(&acc[(4 * q + i) * H + col[t]], p[t][i]);
-                }
-            }
-        } else {
-            if (active) {
+        for (int turn = 0; turn < 4; ++turn) {
+            __syncthreads();
+            if (turn == wv && active) {
+                float* base = acc + (4 * q) * S;
+                float v[NT][4];
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        atomicAdd(&acc[(4 * q + i) * H + col[t]], p[t][i]);
+                        v[t][i] = base[i * S + col[t]];
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        base[i * S + col[t]] = v[t][i] + p[t][i];
             }
+        }
+
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            col[t] = col_n[t];
+#pragma unroll
+        for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+            for (int s = 0; s < KSF; ++s)
+                wreg[gt][s] = wreg_n[gt][s];
+        if constexpr (LAB) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                gcol[u] = gcol_n[u];
+                hv[u] = hv_n[u];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KSG; ++s)
+                dv[s] = dv_n[s];
         }
     }
     __syncthreads();
@@ -249,11 +321,11 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += 256)
-            dst[i] = acc[i];
+            dst[i] = acc[(i / H) * S + (i % H)];
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += 256) {
             const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[i]);
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[(i / H) * S + (i % H)]);
         }
     }
 }
@@ -274,7 +346,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 template <int G, int F>
 static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
 {
-    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
+    const size_t lds = (size_t)kDhRows * dh_stride(a.H) * sizeof(float);
     const dim3 grid(a.nchunks * a.ntiles), blk(256);
     auto go = [&](auto kern) {
         static bool attr = false;

@@ -168,32 +168,45 @@ __global__ __launch_bounds__(256, 2) void k_fixed_bwd_h(FixedArgs a)
     const int64_t lc0 = (int64_t)chunk * a.L / a.nchunks, lc1 = (int64_t)(chunk + 1) * a.L / a.nchunks;
     const int64_t b0 = (int64_t)tile * R;
     const int64_t H = a.H;
-    for (int64_t i = threadIdx.x; i < R * H; i += 256)
+    const int64_t S = dh_stride(H);
+    for (int64_t i = threadIdx.x; i < R * S; i += 256)
         acc[i] = 0.f;
     __syncthreads();
+    // rows owned by this wave; an index row is duplicate-free, so the lanes
+    // of one label never touch the same cell: plain read-add-write suffices
+    float* rows = acc + (4 * wvi) * S;
     for (int64_t l = lc0; l < lc1; ++l) {
         int jv[NU];
         float wv[NU];
         load_label_row<F>(a, l, lane, jv, wv);
+        float d[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t b = b0 + 4 * wvi + r;
-            const float d = b < a.B ? __uint_as_float((uint32_t)a.dZ[b * a.L + l] << 16) : 0.f;
+            d[r] = b < a.B ? __uint_as_float((uint32_t)a.dZ[b * a.L + l] << 16) : 0.f;
+        }
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
-                if (lane + 64 * u < F)
-                    atomicAdd(&acc[(4 * wvi + r) * H + jv[u]], d * wv[u]);
+        for (int u = 0; u < NU; ++u) {
+            if (lane + 64 * u < F) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = rows[r * S + jv[u]];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    rows[r * S + jv[u]] = fmaf(d[r], wv[u], v[r]);
+            }
         }
     }
     __syncthreads();
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += 256)
-            dst[i] = acc[i];
+            dst[i] = acc[(i / H) * S + (i % H)];
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += 256) {
             const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[i]);
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[(i / H) * S + (i % H)]);
         }
     }
 }
@@ -220,7 +233,7 @@ bool launch_fixed_bwd_w(int F, const FixedArgs& a, int grid, hipStream_t s)
 
 bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s)
 {
-    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
+    const size_t lds = (size_t)kDhRows * dh_stride(a.H) * sizeof(float);
     const dim3 grid(a.nchunks * a.ntiles), blk(256);
 #define HASTE_FIXED_DH(FF)                                                                           \
     if (det) hipLaunchKernelGGL((k_fixed_bwd_h<FF, true>), grid, blk, lds, s, a);                    \

@@ -27,8 +27,15 @@
 
 namespace haste {
 
+// Wide variants (weight-gradient tiles of G x 128 or 64 x F) need more than
+// 256 registers per lane; they run one workgroup per CU with up to 512.
+constexpr int fwd_min_blocks(int G, int F, int mode)
+{
+    return ((mode == STEP_DW && (F == 128 || G == 64)) || (G == 64 && F == 128)) ? 1 : 2;
+}
+
 template <int G, int F, int MODE, bool LOSS>
-__global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
+__global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(FwdArgs a)
 {
     constexpr int NT = F / 16;    // 16-slot tiles (gather units, dW columns)
     constexpr int KS = F / 32;    // contraction steps of the forward product
@@ -38,6 +45,9 @@ __global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
     constexpr bool FWD = (MODE != BWD_W);          // runs the forward product
     constexpr bool DW = (MODE == STEP_DW || MODE == BWD_W);
     constexpr int DST = G + 2;                     // row stride of the dZ tile (BWD_W)
+    // Prefetch the next group's weights only when they are small; wide tiles
+    // would push the wave past 256 registers (two waves per SIMD).
+    constexpr bool PF_W = FWD && (GT * KS <= 4);
 
     __shared__ __attribute__((aligned(16))) uint16_t sH[4][FWD ? 32 * F : 8];
     __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
@@ -66,19 +76,43 @@ __global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
     }
     float lsum = 0.f;
 
-    for (int64_t k = k0; k < k1; ++k) {
-        int col[NT];
+    // Software pipeline: the index row and weights of the next group and the
+    // gathered rows of the next batch chunk are requested one step ahead.
+    auto load_col = [&](int64_t kk, int (&cl)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            col[t] = a.idx[k * F + 16 * t + r16];
-        u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
+            cl[t] = a.idx[kk * F + 16 * t + r16];
+    };
+    auto load_w = [&](int64_t kk, u32x4_t (&wr)[FWD ? GT : 1][FWD ? KS : 1]) {
         if constexpr (FWD) {
 #pragma unroll
             for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
-                    wreg[gt][s] = ldg16(a.W + ((k * G + 16 * gt + r16) * F + 32 * s + 8 * q));
+                    wr[gt][s] = ldg16(a.W + ((kk * G + 16 * gt + r16) * F + 32 * s + 8 * q));
         }
+    };
+    // gather: lane (slot 16t + r16, q) <- h[32c + 8q .. +8, I_k[slot]]
+    auto gather = [&](const int (&cl)[NT], int c, u32x4_t (&hr)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            hr[t] = ldg16(a.hT + (int64_t)cl[t] * a.Bp + 32 * c + 8 * q);
+    };
+
+    int col[NT], col_n[NT];
+    u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1], wreg_n[PF_W ? GT : 1][PF_W ? KS : 1];
+    u32x4_t hreg[NT], hnext[NT];
+    if (k0 < k1) {
+        load_col(k0, col);
+        load_w(k0, wreg);
+        gather(col, 0, hreg);
+    }
+
+    for (int64_t k = k0; k < k1; ++k) {
+        const int64_t kn = k + 1 < k1 ? k + 1 : k;
+        load_col(kn, col_n);
+        if constexpr (PF_W) load_w(kn, wreg_n);
+        else if (k != k0) load_w(k, wreg);
 
         bool anypos = false;
         if constexpr (LABELS) {
@@ -108,11 +142,9 @@ __global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
         }
 
         for (int c = 0; c < nchunk; ++c) {
-            // 1. gather: lane (slot 16t + r16, q) <- h[32c + 8q .. +8, I_k[slot]]
-            u32x4_t hreg[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                hreg[t] = ldg16(a.hT + (int64_t)col[t] * a.Bp + 32 * c + 8 * q);
+            // 1. rows of this chunk are in hreg; request the next chunk's rows
+            if (c + 1 < nchunk) gather(col, c + 1, hnext);
+            else gather(col_n, 0, hnext);
             if constexpr (MODE == BWD_W) {
                 // dZ chunk rows 32c .. 32c+31 of the group's G columns into LDS
                 uint16_t* dt = sD[wv];
@@ -253,6 +285,9 @@ __global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
                     }
                 }
             }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                hreg[t] = hnext[t];
         }
 
         if constexpr (DW) {
@@ -264,6 +299,16 @@ __global__ __launch_bounds__(256, 2) void k_group_fwd(FwdArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         a.dW[(k * G + 16 * gt + 4 * q + i) * F + 16 * t + r16] = dw[gt][t][i];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            col[t] = col_n[t];
+        if constexpr (PF_W) {
+#pragma unroll
+            for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    wreg[gt][s] = wreg_n[gt][s];
         }
     }
 

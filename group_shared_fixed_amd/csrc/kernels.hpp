@@ -10,6 +10,9 @@ namespace haste {
 // Batch rows per dh accumulator tile (one LDS accumulator of kDhRows x H fp32
 // per workgroup).
 constexpr int kDhRows = 16;
+// Row stride (floats) of an LDS dh accumulator: H rounded up to 16, plus 4,
+// so the four row groups a matrix-core result tile spans start 16 banks apart.
+__host__ __device__ inline int64_t dh_stride(int64_t H) { return (H + 15) / 16 * 16 + 4; }
 // Largest batch the label cursors of the BCE paths cover (4 per lane).
 constexpr int kMaxLabelBatch = 256;
 
