@@ -59,6 +59,22 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4r + c supplies the address of 4 consecutive 16-bit values;
+// lane 4c + e receives value e of the lanes c, 4 + c, 8 + c, 12 + c (in that
+// order).  So if lane 4r + c points at row k0 + r, column n0 + 4c of a tile
+// stored row-major with rows along the contraction index, lane i receives
+// column n0 + i, rows k0 .. k0 + 3: the K-contiguous matrix-core operand.
+__device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p)
+{
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return u32x4_t{a[0], a[1], b[0], b[1]}; }
+
 __device__ __forceinline__ u32x4_t ldg16(const void* p)
 {
     return *reinterpret_cast<const u32x4_t*>(p);

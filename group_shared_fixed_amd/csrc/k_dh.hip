@@ -30,15 +30,22 @@
 
 namespace haste {
 
-__device__ __forceinline__ int swz16(int r, int nchunks)
+// W_k tile in LDS, [label g][slot f] as in W: the 16-byte chunk index of a
+// row is XORed with (g / 2) so the row writes and the transposing operand
+// reads of one instruction spread over the banks.
+template <int F>
+__device__ __forceinline__ int wt_off(int g, int f)
 {
-    return ((r & 7) ^ ((r >> 3) << 2)) & (nchunks - 1);
+    constexpr int NCH = F / 8;
+    return g * F + ((((f >> 3) ^ (g >> 1)) & (NCH - 1)) << 3) + (f & 7);
 }
 
-// W^T tile [slot f][label g]: 16-byte chunks along g, swizzled by f.
-__device__ __forceinline__ int swzw(int f, int nchunks)
+// Gathered H tile in LDS, [slot f][16 batch rows] (32-byte rows, the layout
+// of hT); rows f with bit 3 set are stored 4 rows further so the four
+// lane groups of a transposing read cover all banks.
+__device__ __forceinline__ int ht_off(int f, int b)
 {
-    return ((f >> 1) ^ (f >> 3)) & (nchunks - 1);
+    return ((f ^ (((f >> 3) & 1) << 2)) << 4) + b;
 }
 
 template <int G, int F, int SRC, bool DET>
@@ -48,20 +55,20 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     constexpr int KSF = F / 32;         // contraction steps of Z^T = W H^T
     constexpr int GT = G / 16;          // label tiles
     constexpr int KSG = (G + 31) / 32;  // contraction steps of P = dZ W
-    constexpr int NCH = F / 8;
-    constexpr int GCH = G / 8;
     constexpr int R = kDhRows;
     constexpr bool LAB = (SRC == DH_FROM_LABELS);
     constexpr int NU = F / 32;          // gather loads per lane (16 rows x F slots)
+    static_assert(R == 16, "one 16-row matrix-core tile per workgroup");
 
-    extern __shared__ float acc[];      // R rows, stride dh_stride(H)
-    __shared__ __attribute__((aligned(16))) uint16_t sH[LAB ? 4 : 1][LAB ? R * F : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t sWT[4][F * G];
+    extern __shared__ __attribute__((aligned(16))) float acc[];   // column-major: acc[j * 16 + row]
+    __shared__ __attribute__((aligned(16))) uint16_t sH[LAB ? 4 : 1][LAB ? F * 16 : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sW[4][G * F];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int q = lane >> 4;
+    const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
 
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
@@ -72,9 +79,8 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     const int64_t b0 = (int64_t)tile * R;
     const int64_t L = a.K * G;
     const int64_t H = a.H;
-    const int64_t S = dh_stride(H);
 
-    for (int64_t i = threadIdx.x; i < R * S; i += 256)
+    for (int64_t i = threadIdx.x; i < R * H; i += 256)
         acc[i] = 0.f;
 
     LabelCursor cur;
@@ -91,6 +97,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         for (int t = 0; t < NT; ++t)
             cl[t] = a.idx[kk * F + 16 * t + r16];
     };
+    // W_k rows: lane (label 16gt + r16, q) holds slots 32s + 8q .. +8
     auto load_w = [&](int64_t kk, u32x4_t (&wr)[GT][KSF]) {
 #pragma unroll
         for (int gt = 0; gt < GT; ++gt)
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         for (int u = 0; u < NU; ++u)
             gc[u] = a.idx[kk * F + 32 * u + (lane & 31)];
     };
-    // lane (slot 32u + lane%32, half) <- 8 rows b0 + 8*half .. of feature column gc[u]
+    // lane (slot 32u + lane%32, half) <- batch rows b0 + 8*half .. +8 of column gc[u]
     auto gather = [&](const int (&gc)[NU], u32x4_t (&hv)[NU]) {
 #pragma unroll
         for (int u = 0; u < NU; ++u)
@@ -145,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     __syncthreads();
 
+    uint16_t* wt = sW[wv];
     for (int64_t rd = 0; rd < nrounds; ++rd) {
         const int64_t k = kc0 + 4 * rd + wv;
         const bool active = k < kc1;
@@ -160,20 +168,12 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             p[t] = zero4();
 
         if (active) {
-            // W_k^T into LDS for the B operand of P = dZ W (contraction over labels)
-            uint16_t* wt = sWT[wv];
+            // W_k rows into LDS as they are (contraction over labels reads them transposed)
 #pragma unroll
             for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
                 for (int s = 0; s < KSF; ++s)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int f = 32 * s + 8 * q + e;
-                        const int g = 16 * gt + r16;
-                        const uint32_t wd = wreg[gt][s][e >> 1];
-                        wt[f * G + ((((g >> 3) ^ swzw(f, GCH))) << 3) + (g & 7)] =
-                            (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu));
-                    }
+                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(16 * gt + r16, 32 * s + 8 * q)) = wreg[gt][s];
 
             u32x4_t ahi[KSG], alo[KSG];
             if constexpr (!LAB) {
@@ -183,29 +183,21 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                     alo[s] = u32x4_t{0u, 0u, 0u, 0u};
                 }
             } else {
-                // transposed copy of the gathered tile: [row][slot]
                 uint16_t* ht = sH[wv];
 #pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    const int f = 32 * u + (lane & 31);
-                    const int half = lane >> 5;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = 8 * half + e;
-                        ht[r * F + ((((f >> 3) ^ swz16(r, NCH))) << 3) + (f & 7)] =
-                            (uint16_t)((e & 1) ? (hv[u][e >> 1] >> 16) : (hv[u][e >> 1] & 0xffffu));
-                    }
-                }
+                for (int u = 0; u < NU; ++u)
+                    *reinterpret_cast<u32x4_t*>(ht + ht_off(32 * u + (lane & 31), 8 * (lane >> 5))) = hv[u];
                 wave_sync();
-                // Z^T = W_k H^T: result lane (row r16, q) holds labels 16gt + 4q + i
+                // Z^T = W_k H^T; B = H^T read transposed: lane (row r16, q) gets
+                // slots 32s + 8q + e.  Result lane (row r16, q) holds labels 16gt + 4q + i.
                 f32x4_t zt[GT];
 #pragma unroll
                 for (int gt = 0; gt < GT; ++gt)
                     zt[gt] = zero4();
 #pragma unroll
                 for (int s = 0; s < KSF; ++s) {
-                    const int ch = 4 * s + q;
-                    const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(ht + r16 * F + ((ch ^ swz16(r16, NCH)) << 3));
+                    const int f0 = 32 * s + 8 * q + tr_r;
+                    const u32x4_t bv = cat(lds_tr16(ht + ht_off(f0, 4 * tr_c)), lds_tr16(ht + ht_off(f0 + 4, 4 * tr_c)));
 #pragma unroll
                     for (int gt = 0; gt < GT; ++gt)
                         zt[gt] = mfma16(wreg[gt][s], bv, zt[gt]);
@@ -219,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                     for (int i = 0; i < 4; ++i) {
                         const float t = __builtin_amdgcn_exp2f(-zt[gt][i] * kLog2e);
                         float d = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
-                        if ((mrow >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
+                        if (mrow && ((mrow >> (16 * gt + 4 * q + i)) & 1ull)) d -= scale;
                         dz[gt][i] = brow_ok ? d : 0.f;
                     }
                 // contraction element e of step s <-> label 32s + 16*(e/4) + 4q + e%4
@@ -238,31 +230,35 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 }
             }
             wave_sync();
-            // P = dZ_tile W_k: result lane (slot 16t + r16, q) holds rows 4q + i
+            // P = dZ_tile W_k with B = W_k read transposed: lane (slot 16t + r16, q)
+            // gets the labels of contraction elements e.  Result lane
+            // (slot 16t + r16, q) holds batch rows 4q + i.
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const int f = 16 * t + r16;
-                const uint16_t* wrow = sWT[wv] + f * G;
+                const int fc = 16 * t + 4 * tr_c;
 #pragma unroll
                 for (int s = 0; s < KSG; ++s) {
-                    u32x4_t bv;
+                    // Transposing reads run with the whole wave active (under a
+                    // partial EXEC mask they overwrite the inactive lanes'
+                    // registers); rows past G read a valid row and are zeroed.
+                    u32x2_t lo2, hi2;
+                    const u32x2_t z2 = u32x2_t{0u, 0u};
                     if constexpr (!LAB) {
-                        const int g = 32 * s + 8 * q;
-                        if (g < G)
-                            bv = *reinterpret_cast<const u32x4_t*>(wrow + ((((g >> 3) ^ swzw(f, GCH))) << 3));
-                        else
-                            bv = u32x4_t{0u, 0u, 0u, 0u};
+                        const int g = 32 * s + 8 * q;          // elements e <-> g + e
+                        const bool ok = g < G;
+                        const int gr = ok ? g : 0;
+                        lo2 = lds_tr16(wt + wt_off<F>(gr + tr_r, fc));
+                        hi2 = lds_tr16(wt + wt_off<F>(gr + 4 + tr_r, fc));
+                        lo2 = ok ? lo2 : z2;
+                        hi2 = ok ? hi2 : z2;
                     } else {
-                        const int ga = 32 * s + 4 * q;
-                        const int gb = 32 * s + 16 + 4 * q;
-                        const u32x2_t lo2 = *reinterpret_cast<const u32x2_t*>(
-                            wrow + ((((ga >> 3) ^ swzw(f, GCH))) << 3) + (ga & 7));
-                        u32x2_t hi2 = u32x2_t{0u, 0u};
-                        if (gb < G)
-                            hi2 = *reinterpret_cast<const u32x2_t*>(
-                                wrow + ((((gb >> 3) ^ swzw(f, GCH))) << 3) + (gb & 7));
-                        bv = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+                        const int ga = 32 * s + 4 * q;         // e < 4 <-> ga + e
+                        const int gb = ga + 16;                // e >= 4 <-> gb + e - 4
+                        lo2 = lds_tr16(wt + wt_off<F>(ga + tr_r, fc));
+                        if constexpr (G > 16) hi2 = lds_tr16(wt + wt_off<F>(gb + tr_r, fc));
+                        else hi2 = z2;
                     }
+                    const u32x4_t bv = cat(lo2, hi2);
                     p[t] = mfma16(ahi[s], bv, p[t]);
                     if constexpr (LAB)
                         p[t] = mfma16(alo[s], bv, p[t]);
@@ -273,26 +269,22 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         // next round's gathered rows (their index row arrived meanwhile)
         if constexpr (LAB) gather(gcol_n, hv_n);
 
-        // scatter-add P into acc[:, I_k] with plain read-add-write: the waves
-        // take turns (barrier-separated) so every accumulator cell is updated
-        // by one wave at a time and in group order; inside one wave the index
-        // set is duplicate-free, so no two lanes touch the same cell.
+        // scatter-add P into the accumulator columns I_k with 16-byte
+        // read-add-write (rows 4q .. 4q+3 of column col[t] are adjacent).  The
+        // waves take turns (barrier-separated) so every accumulator cell is
+        // updated by one wave at a time and in group order; inside one wave
+        // the index set is duplicate-free, so no two lanes touch the same cell.
 #pragma unroll 1
         for (int turn = 0; turn < 4; ++turn) {
             __syncthreads();
             if (turn == wv && active) {
-                float* base = acc + (4 * q) * S;
-                float v[NT][4];
+                f32x4_t v[NT];
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        v[t][i] = base[i * S + col[t]];
+                    v[t] = *reinterpret_cast<const f32x4_t*>(acc + col[t] * R + 4 * q);
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        base[i * S + col[t]] = v[t][i] + p[t][i];
+                    *reinterpret_cast<f32x4_t*>(acc + col[t] * R + 4 * q) = v[t] + p[t];
             }
         }
 
@@ -321,11 +313,11 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += 256)
-            dst[i] = acc[(i / H) * S + (i % H)];
+            dst[i] = acc[(i % H) * R + i / H];
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += 256) {
             const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[(i / H) * S + (i % H)]);
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[(i % H) * R + i / H]);
         }
     }
 }
@@ -346,7 +338,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 template <int G, int F>
 static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
 {
-    const size_t lds = (size_t)kDhRows * dh_stride(a.H) * sizeof(float);
+    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
     const dim3 grid(a.nchunks * a.ntiles), blk(256);
     auto go = [&](auto kern) {
         static bool attr = false;

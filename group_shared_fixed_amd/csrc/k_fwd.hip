@@ -34,13 +34,21 @@ constexpr int fwd_min_blocks(int G, int F, int mode)
     return ((mode == STEP_DW && (F == 128 || G == 64)) || (G == 64 && F == 128)) ? 1 : 2;
 }
 
+// Offset (16-bit elements) of (slot f, batch row b) in a wave's gathered tile
+// [F slots][32 rows]: the 16-byte chunk index is XORed with (f/8) % 4 and the
+// 8-byte half with (f/8) % 2, so the chunk writes and the transposing reads of
+// one instruction spread over the banks.
+__device__ __forceinline__ int tile_off(int f, int b)
+{
+    return f * 32 + ((((b >> 3) ^ (f >> 3)) & 3) << 3) + (((((b >> 2) ^ (f >> 3)) & 1)) << 2) + (b & 3);
+}
+
 template <int G, int F, int MODE, bool LOSS>
 __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(FwdArgs a)
 {
     constexpr int NT = F / 16;    // 16-slot tiles (gather units, dW columns)
     constexpr int KS = F / 32;    // contraction steps of the forward product
     constexpr int GT = G / 16;    // 16-label tiles
-    constexpr int NCH = F / 8;    // 16-byte chunks per LDS tile row
     constexpr bool LABELS = (MODE == FWD_BCE || MODE == STEP_DW);
     constexpr bool FWD = (MODE != BWD_W);          // runs the forward product
     constexpr bool DW = (MODE == STEP_DW || MODE == BWD_W);
@@ -57,6 +65,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     const int wv = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int q = lane >> 4;
+    const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
     uint16_t* tile = sH[wv];
 
     const int64_t L = a.K * G;
@@ -175,22 +184,18 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 }
                 wave_sync();
             } else {
-                // 2. transposed copy into the LDS tile [row 8q + e][slot]
+                // 2. the same rows into the wave's LDS tile [slot][32 batch rows]
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int cc = 16 * t + r16;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = 8 * q + e;
-                        const uint32_t wd = hreg[t][e >> 1];
-                        tile[r * F + ((((cc >> 3) ^ swz(r, NCH))) << 3) + (cc & 7)] =
-                            (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu));
-                    }
+                    const int f = 16 * t + r16;
+                    u32x4_t v = hreg[t];
+                    if ((f >> 3) & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+                    *reinterpret_cast<u32x4_t*>(tile + f * 32 + ((q ^ ((f >> 3) & 3)) << 3)) = v;
                 }
                 wave_sync();
-                // 3. Z_chunk = H_chunk W_k^T.  A row m of tile mt is batch row
-                //    8*(m/4) + 4*mt + m%4, so result lane (label r16, q) holds batch
-                //    rows 8q + 4*mt + i.
+                // 3. Z_chunk = H_chunk W_k^T with A = H read transposed from the
+                //    tile.  A row m of tile mt is batch row 8*(m/4) + 4*mt + m%4, so
+                //    result lane (label r16, q) holds batch rows 8q + 4*mt + i.
                 f32x4_t z[2][GT];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -199,11 +204,11 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         z[mt][gt] = zero4();
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const int r = 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
-                        const int ch = 4 * s + q;
-                        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(tile + r * F + ((ch ^ swz(r, NCH)) << 3));
+                        const int f0 = 32 * s + 8 * q + tr_r;
+                        const u32x4_t av = cat(lds_tr16(tile + tile_off(f0, 8 * tr_c + 4 * mt)),
+                                               lds_tr16(tile + tile_off(f0 + 4, 8 * tr_c + 4 * mt)));
 #pragma unroll
                         for (int gt = 0; gt < GT; ++gt)
                             z[mt][gt] = mfma16(av, wreg[gt][s], z[mt][gt]);

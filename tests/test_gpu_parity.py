@@ -23,6 +23,13 @@ CASES = {
     "g64_f32_b33": (33, 96, 17, 64, 32),
     "g32_f32_b1": (1, 64, 9, 32, 32),
     "g32_f64_h1024": (50, 1024, 10, 32, 64),
+    # many groups per label chunk: every wave of a dh workgroup gets several
+    # groups, so the ordered accumulation and the one-ahead prefetch run
+    "g16_f32_many": (64, 256, 4096, 16, 32),
+    "g16_f64_many_b40": (40, 512, 3000, 16, 64),
+    "g32_f64_many_b100": (100, 768, 3000, 32, 64),
+    "g64_f64_many_b70": (70, 768, 1500, 64, 64),
+    "g16_f128_many_b130": (130, 768, 1200, 16, 128),
 }
 
 _cache = {}
