@@ -48,6 +48,14 @@ __device__ __forceinline__ int ht_off(int f, int b)
     return ((f ^ (((f >> 3) & 1) << 2)) << 4) + b;
 }
 
+// Offset (floats) of (batch row r, column j) in the column-major accumulator:
+// 16 floats per column, 4-row quads XORed with (j / 4) % 4 so the 16-byte
+// read-add-writes of one instruction (random columns) use all bank quads.
+__device__ __forceinline__ int acc_off(int j, int r)
+{
+    return j * 16 + ((((r >> 2) ^ (j >> 2)) & 3) << 2) + (r & 3);
+}
+
 template <int G, int F, int SRC, bool DET>
 __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 {
@@ -90,6 +98,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     const float inv_s = 1.0f / a.scale;
     const int64_t brow = b0 + r16;            // batch row of this lane's A rows
     const bool brow_ok = brow < a.B;
+    const bool tile_full = b0 + R <= a.B;
 
     // per-round inputs, requested one round ahead
     auto load_col = [&](int64_t kk, int (&cl)[NT]) {
@@ -205,15 +214,24 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 // labels of this row for this group
                 const uint64_t mrow = cur.take(k * G, G, a.y_col);
                 float dz[GT][4];
+                // s * sigmoid(z) = 1 / ((1 + e^-z) / s); e^-z = +inf gives 0
 #pragma unroll
                 for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float t = __builtin_amdgcn_exp2f(-zt[gt][i] * kLog2e);
-                        float d = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
-                        if (mrow && ((mrow >> (16 * gt + 4 * q + i)) & 1ull)) d -= scale;
-                        dz[gt][i] = brow_ok ? d : 0.f;
+                        dz[gt][i] = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
                     }
+                if (__any(mrow != 0) || !tile_full) {   // rare: positives or padding rows
+#pragma unroll
+                    for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float d = dz[gt][i];
+                            if ((mrow >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
+                            dz[gt][i] = brow_ok ? d : 0.f;
+                        }
+                }
                 // contraction element e of step s <-> label 32s + 16*(e/4) + 4q + e%4
 #pragma unroll
                 for (int s = 0; s < KSG; ++s) {
@@ -281,10 +299,10 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 f32x4_t v[NT];
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    v[t] = *reinterpret_cast<const f32x4_t*>(acc + col[t] * R + 4 * q);
+                    v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    *reinterpret_cast<f32x4_t*>(acc + col[t] * R + 4 * q) = v[t] + p[t];
+                    *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
             }
         }
 
@@ -313,11 +331,11 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += 256)
-            dst[i] = acc[(i % H) * R + i / H];
+            dst[i] = acc[acc_off((int)(i % H), (int)(i / H))];
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += 256) {
             const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[(i % H) * R + i / H]);
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc_off((int)(i % H), (int)(i / H))]);
         }
     }
 }
