@@ -9,19 +9,26 @@
 //
 // One wavefront owns one group at a time and walks a contiguous range of
 // groups.  Per 32-row batch chunk it
-//   1. gathers the chunk of H_k from the feature-major copy hT (row I_k[f] of
-//      hT holds h[:, I_k[f]]): one 16-byte load per lane per 16 slots, rows
-//      read whole, and keeps it in registers in the matrix-core B layout of
-//      the weight-gradient product (slot f = lane % 16, eight consecutive
-//      batch rows per lane);
-//   2. writes the same values transposed into a wave-private LDS tile
-//      [batch row][slot], which feeds the forward product's A operand;
+//   1. has the chunk of H_k in registers, gathered from the feature-major
+//      copy hT (row I_k[f] of hT holds h[:, I_k[f]]) with one 16-byte load
+//      per lane per 16 slots; each quad of lanes reads 64 contiguous bytes of
+//      one row, so an instruction asks for 16 cache lines, not 64; the next
+//      chunk's rows are requested meanwhile;
+//   2. writes them into a wave-private LDS tile [slot][row] and reads them
+//      back K-contiguous with transposing LDS reads as the A operand of the
+//      forward product, and row-wise as the B operand of the weight-gradient
+//      product (slot f = lane % 16, eight consecutive batch rows per lane);
 //   3. runs Z_chunk = H_chunk W_k^T on 16x16x32 bf16 matrix cores;
 //   4. applies the epilogue of the mode: store Z, or BCE -> store dZ, or
 //      BCE -> dW_k += dZ_chunk^T H_chunk with dZ split into bf16 hi + lo.
 // Batch rows of the forward product are permuted so that every lane ends up
 // holding eight consecutive batch rows of one label, which is exactly the A
 // layout of the weight-gradient product: no data moves between the two.
+//
+// Vector-memory operations retire in issue order, so waiting for one load
+// also waits for every older one.  The next group's weights (an HBM round
+// trip) are therefore requested only after the last gather of the current
+// group that is still needed before them.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,15 +42,15 @@ constexpr int fwd_min_blocks(int G, int F, int mode)
 }
 
 // Offset (16-bit elements) of (slot f, batch row b) in a wave's gathered tile
-// [F slots][32 rows]: the 16-byte chunk index is XORed with (f/8) % 4 and the
-// 8-byte half with (f/8) % 2, so the chunk writes and the transposing reads of
-// one instruction spread over the banks.
+// [F slots][32 rows]: the 16-byte chunk index is XORed with (f/8) % 4 so the
+// transposing reads of one instruction spread over more banks.
 __device__ __forceinline__ int tile_off(int f, int b)
 {
-    return f * 32 + ((((b >> 3) ^ (f >> 3)) & 3) << 3) + (((((b >> 2) ^ (f >> 3)) & 1)) << 2) + (b & 3);
+    return f * 32 + ((((b >> 3) ^ (f >> 3)) & 3) << 3) + (b & 7);
 }
 
-template <int G, int F, int MODE, bool LOSS>
+// WZ: also write the fp32 logits (optional output of the BCE modes).
+template <int G, int F, int MODE, bool LOSS, bool WZ>
 __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(FwdArgs a)
 {
     constexpr int NT = F / 16;    // 16-slot tiles (gather units, dW columns)
@@ -52,12 +59,15 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     constexpr bool LABELS = (MODE == FWD_BCE || MODE == STEP_DW);
     constexpr bool FWD = (MODE != BWD_W);          // runs the forward product
     constexpr bool DW = (MODE == STEP_DW || MODE == BWD_W);
+    constexpr bool STORE_Z = (MODE == FWD_Z) || WZ;
     constexpr int DST = G + 2;                     // row stride of the dZ tile (BWD_W)
+    constexpr int NDZ = (32 * G / 8 + 63) / 64;    // 16-byte dZ pieces per lane per chunk (BWD_W)
     // Prefetch the next group's weights only when they are small; wide tiles
     // would push the wave past 256 registers (two waves per SIMD).
     constexpr bool PF_W = FWD && (GT * KS <= 4);
 
-    __shared__ __attribute__((aligned(16))) uint16_t sH[4][FWD ? 32 * F : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sH[4][32 * F];
+    __shared__ __attribute__((aligned(16))) uint16_t sWk[4][FWD ? G * F : 8];
     __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sD[4][MODE == BWD_W ? 32 * DST : 2];
 
@@ -66,6 +76,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
+    const int qr = lane >> 2, qc = lane & 3;     // quad-contiguous load position
     uint16_t* tile = sH[wv];
 
     const int64_t L = a.K * G;
@@ -74,6 +85,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     const int64_t k0 = gw * a.K / nw;
     const int64_t k1 = (gw + 1) * a.K / nw;
     const int nchunk = (int)(a.Bp / 32);
+    const int wchunk = nchunk >= 2 ? nchunk - 2 : 0;   // chunk that requests the next W
     const float scale = a.scale;
     const float inv_s = 1.0f / a.scale;
 
@@ -85,43 +97,86 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     }
     float lsum = 0.f;
 
-    // Software pipeline: the index row and weights of the next group and the
-    // gathered rows of the next batch chunk are requested one step ahead.
+    // index entries of the lane's gather slots 16t + qr
     auto load_col = [&](int64_t kk, int (&cl)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            cl[t] = a.idx[kk * F + 16 * t + r16];
+            cl[t] = a.idx[kk * F + 16 * t + qr];
     };
-    auto load_w = [&](int64_t kk, u32x4_t (&wr)[FWD ? GT : 1][FWD ? KS : 1]) {
+    // W_k (G x F bf16, contiguous) as 16-byte pieces, lane + 64 p in order
+    constexpr int NWP = FWD ? (G * F / 8 + 63) / 64 : 1;
+    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
         if constexpr (FWD) {
 #pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    wr[gt][s] = ldg16(a.W + ((kk * G + 16 * gt + r16) * F + 32 * s + 8 * q));
+            for (int p = 0; p < NWP; ++p)
+                wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
         }
     };
-    // gather: lane (slot 16t + r16, q) <- h[32c + 8q .. +8, I_k[slot]]
-    auto gather = [&](const int (&cl)[NT], int c, u32x4_t (&hr)[NT]) {
+    // gather: lane (slot 16t + qr, quad position qc) <- h[32c + 8qc .. +8, I_k[slot]];
+    // the row pointers of a group are formed once and reused for its chunks
+    auto rows_of = [&](const int (&cl)[NT], const uint16_t* (&gp)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            hr[t] = ldg16(a.hT + (int64_t)cl[t] * a.Bp + 32 * c + 8 * q);
+            gp[t] = a.hT + (int64_t)cl[t] * a.Bp + 8 * qc;
+    };
+    auto gather = [&](const uint16_t* const (&gp)[NT], int c, u32x4_t (&hr)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            hr[t] = ldg16(gp[t] + 32 * c);
+    };
+    // BWD_W: lane's 16-byte pieces of the chunk's dZ rows (piece ci = lane + 64 it:
+    // row ci / (G/8), labels 8 (ci % (G/8)) .. +8 of the group)
+    auto load_dz = [&](int64_t kk, int c, u32x4_t (&dv)[NDZ]) {
+#pragma unroll
+        for (int it = 0; it < NDZ; ++it) {
+            const int ci = lane + 64 * it;
+            const int64_t b = 32 * c + ci / (G / 8);
+            dv[it] = u32x4_t{0u, 0u, 0u, 0u};
+            if (ci < 32 * G / 8 && b < a.B) dv[it] = ldg16(a.dZ + b * L + kk * G + 8 * (ci % (G / 8)));
+        }
     };
 
     int col[NT], col_n[NT];
-    u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1], wreg_n[PF_W ? GT : 1][PF_W ? KS : 1];
-    u32x4_t hreg[NT], hnext[NT];
+    const uint16_t* gp[NT];
+    u32x4_t wraw[NWP];                      // next weights as loaded
+    u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
+    u32x4_t hA[NT], hB[NT];
+    u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1];
     if (k0 < k1) {
         load_col(k0, col);
-        load_w(k0, wreg);
-        gather(col, 0, hreg);
+        load_w(k0, wraw);
+        rows_of(col, gp);
+        gather(gp, 0, hA);
+        if constexpr (MODE == BWD_W) load_dz(k0, 0, dA);
     }
 
     for (int64_t k = k0; k < k1; ++k) {
         const int64_t kn = k + 1 < k1 ? k + 1 : k;
         load_col(kn, col_n);
-        if constexpr (PF_W) load_w(kn, wreg_n);
-        else if (k != k0) load_w(k, wreg);
+        if constexpr (FWD) {
+            // this group's weights: through LDS into the matrix-core B layout
+            // of the forward product (lane (label 16gt + r16, q): slots 32s + 8q ..)
+            uint16_t* wk = sWk[wv];
+            if constexpr (!PF_W) {
+                if (k != k0) load_w(k, wraw);
+            }
+            // 16-byte piece j of label row g sits at piece j ^ (g % (F/8)) of the row
+            constexpr int PR = F / 8;
+#pragma unroll
+            for (int p = 0; p < NWP; ++p) {
+                const int u = lane + 64 * p;
+                if (u < G * PR)
+                    *reinterpret_cast<u32x4_t*>(wk + (u / PR) * F + 8 * ((u ^ (u / PR)) & (PR - 1))) = wraw[p];
+            }
+            wave_sync();
+#pragma unroll
+            for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int g = 16 * gt + r16;
+                    wreg[gt][s] = *reinterpret_cast<const u32x4_t*>(wk + g * F + 8 * (((4 * s + q) ^ g) & (PR - 1)));
+                }
+        }
 
         bool anypos = false;
         if constexpr (LABELS) {
@@ -150,27 +205,47 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     dw[gt][t] = zero4();
         }
 
-        for (int c = 0; c < nchunk; ++c) {
-            // 1. rows of this chunk are in hreg; request the next chunk's rows
-            if (c + 1 < nchunk) gather(col, c + 1, hnext);
-            else gather(col_n, 0, hnext);
+        // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W); the
+        // next chunk's inputs go to hn / dn
+        auto chunk = [&](int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT], u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1],
+                         u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1]) {
+            // 1. request the next chunk (or the next group's first chunk)
+            if (c + 1 < nchunk) {
+                gather(gp, c + 1, hn);
+                if constexpr (MODE == BWD_W) load_dz(k, c + 1, dn);
+            } else {
+                const uint16_t* gpn[NT];
+                rows_of(col_n, gpn);
+                gather(gpn, 0, hn);
+                if constexpr (MODE == BWD_W) load_dz(kn, 0, dn);
+            }
+            if constexpr (PF_W) {
+                if (c == wchunk) load_w(kn, wraw);
+            }
+
+            // 2. the rows into the wave's LDS tile [slot][32 batch rows]
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<u32x4_t*>(tile + tile_off(16 * t + qr, 8 * qc)) = hc[t];
+            // B operand of the weight-gradient product: lane (slot 16t + r16, q)
+            // holds batch rows 32c + 8q .. +8 (read after the wave_sync below)
+            auto hrow = [&](int t) {
+                return *reinterpret_cast<const u32x4_t*>(tile + tile_off(16 * t + r16, 8 * q));
+            };
             if constexpr (MODE == BWD_W) {
-                // dZ chunk rows 32c .. 32c+31 of the group's G columns into LDS
+                // dZ chunk into LDS [row][label], then dW_k += dZ_chunk^T H_chunk
                 uint16_t* dt = sD[wv];
 #pragma unroll
-                for (int it = 0; it < (32 * G / 8 + 63) / 64; ++it) {
+                for (int it = 0; it < NDZ; ++it) {
                     const int ci = lane + 64 * it;
                     if (ci < 32 * G / 8) {
                         const int r = ci / (G / 8), gc = ci % (G / 8);
-                        const int64_t b = 32 * c + r;
-                        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-                        if (b < a.B) v = ldg16(a.dZ + b * L + k * G + 8 * gc);
                         uint32_t* d32 = reinterpret_cast<uint32_t*>(dt + r * DST + 8 * gc);
-                        d32[0] = v[0]; d32[1] = v[1]; d32[2] = v[2]; d32[3] = v[3];
+                        d32[0] = dc[it][0]; d32[1] = dc[it][1]; d32[2] = dc[it][2]; d32[3] = dc[it][3];
                     }
                 }
                 wave_sync();
-                // dW_k += dZ_chunk^T H_chunk; A lane (label r16, q): rows 8q + e
+                // A lane (label r16, q): rows 8q + e
 #pragma unroll
                 for (int gt = 0; gt < GT; ++gt) {
                     const uint16_t* cp = dt + 8 * q * DST + 16 * gt + r16;
@@ -180,18 +255,11 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         av[j] = (uint32_t)cp[(2 * j) * DST] | ((uint32_t)cp[(2 * j + 1) * DST] << 16);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
-                        dw[gt][t] = mfma16(av, hreg[t], dw[gt][t]);
+                        dw[gt][t] = mfma16(av, hrow(t), dw[gt][t]);
                 }
                 wave_sync();
+                return;
             } else {
-                // 2. the same rows into the wave's LDS tile [slot][32 batch rows]
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int f = 16 * t + r16;
-                    u32x4_t v = hreg[t];
-                    if ((f >> 3) & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
-                    *reinterpret_cast<u32x4_t*>(tile + f * 32 + ((q ^ ((f >> 3) & 3)) << 3)) = v;
-                }
                 wave_sync();
                 // 3. Z_chunk = H_chunk W_k^T with A = H read transposed from the
                 //    tile.  A row m of tile mt is batch row 8*(m/4) + 4*mt + m%4, so
@@ -232,67 +300,110 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         }
                 } else {
                     float dz[2][GT][4];
+                    if constexpr (!LOSS) {
+                        // s * sigmoid(z) = 1 / ((1 + e^-z) / s), and e^-z = +inf gives 0
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
+                        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int64_t b = bq + 4 * mt + i;
-                            const bool valid = b < a.B;
-                            const uint64_t mrow = anypos ? sM[wv][b & (kMaxLabelBatch - 1)] : 0ull;
+                            for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
-                            for (int gt = 0; gt < GT; ++gt) {
-                                const float zz = z[mt][gt][i];
-                                const bool y = (mrow >> (16 * gt + r16)) & 1ull;
-                                float d;
-                                if constexpr (LOSS) {
+                                for (int i = 0; i < 4; ++i) {
+                                    const float t = __builtin_amdgcn_exp2f(-z[mt][gt][i] * kLog2e);
+                                    dz[mt][gt][i] = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
+                                }
+                        if (anypos) {   // rare: positive labels in this group
+#pragma unroll
+                            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const uint64_t mrow = sM[wv][(bq + 4 * mt + i) & (kMaxLabelBatch - 1)];
+#pragma unroll
+                                    for (int gt = 0; gt < GT; ++gt)
+                                        if ((mrow >> (16 * gt + r16)) & 1ull) dz[mt][gt][i] -= scale;
+                                }
+                        }
+                    } else {
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int64_t b = bq + 4 * mt + i;
+                                const bool valid = b < a.B;
+                                const uint64_t mrow = anypos ? sM[wv][b & (kMaxLabelBatch - 1)] : 0ull;
+#pragma unroll
+                                for (int gt = 0; gt < GT; ++gt) {
+                                    const float zz = z[mt][gt][i];
+                                    const bool y = (mrow >> (16 * gt + r16)) & 1ull;
                                     // u = e^-|z|; sigmoid(|z|) = 1/(1+u); sigmoid(-|z|) = u/(1+u)
                                     const float u = __builtin_amdgcn_exp2f(-fabsf(zz) * kLog2e);
                                     const float r = __builtin_amdgcn_rcpf(1.0f + u);
                                     const float sg = zz >= 0.f ? r : u * r;
-                                    d = scale * sg;
+                                    float d = scale * sg;
                                     const float le = fmaxf(zz, 0.f) + __builtin_amdgcn_logf(1.0f + u) * kLn2 -
                                                      (y ? zz : 0.f);
                                     lsum += valid ? le : 0.f;
-                                } else {
-                                    // s * sigmoid(z) = 1 / ((1 + e^-z) / s); e^-z = +inf gives 0
-                                    const float t = __builtin_amdgcn_exp2f(-zz * kLog2e);
-                                    d = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
-                                }
-                                if (y) d -= scale;
-                                dz[mt][gt][i] = d;
-                                if constexpr (MODE == FWD_BCE) {
-                                    if (valid) {
-                                        const int64_t o = b * L + k * G + 16 * gt + r16;
-                                        a.dZ[o] = (uint16_t)(pack_bf16(d, 0.f) & 0xffffu);
-                                        if (a.Z) a.Z[o] = zz;
-                                    }
-                                } else {
-                                    if (valid && a.Z) a.Z[b * L + k * G + 16 * gt + r16] = zz;
+                                    if (y) d -= scale;
+                                    dz[mt][gt][i] = d;
                                 }
                             }
-                        }
+                    }
+                    if constexpr (MODE == FWD_BCE || STORE_Z) {
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int64_t b = bq + 4 * mt + i;
+                                if (b < a.B) {
+#pragma unroll
+                                    for (int gt = 0; gt < GT; ++gt) {
+                                        const int64_t o = b * L + k * G + 16 * gt + r16;
+                                        if constexpr (MODE == FWD_BCE)
+                                            a.dZ[o] = (uint16_t)(pack_bf16(dz[mt][gt][i], 0.f) & 0xffffu);
+                                        if constexpr (STORE_Z) a.Z[o] = z[mt][gt][i];
+                                    }
+                                }
+                            }
+                    }
                     if constexpr (MODE == STEP_DW) {
                         // dW_k += dZ_chunk^T H_chunk; A = dZ^T (label r16, rows 8q + e),
                         // contraction element e <-> batch row 32c + 8q + e on both sides.
+                        // Padding rows carry zero features, so they add nothing.
 #pragma unroll
                         for (int gt = 0; gt < GT; ++gt) {
                             u32x4_t ahi, alo;
-                            { const u32x2_t _p = split_pair(dz[0][gt][0], dz[0][gt][1]); ahi[0] = _p[0]; alo[0] = _p[1]; }
-                            { const u32x2_t _p = split_pair(dz[0][gt][2], dz[0][gt][3]); ahi[1] = _p[0]; alo[1] = _p[1]; }
-                            { const u32x2_t _p = split_pair(dz[1][gt][0], dz[1][gt][1]); ahi[2] = _p[0]; alo[2] = _p[1]; }
-                            { const u32x2_t _p = split_pair(dz[1][gt][2], dz[1][gt][3]); ahi[3] = _p[0]; alo[3] = _p[1]; }
+                            { const u32x2_t p = split_pair(dz[0][gt][0], dz[0][gt][1]); ahi[0] = p[0]; alo[0] = p[1]; }
+                            { const u32x2_t p = split_pair(dz[0][gt][2], dz[0][gt][3]); ahi[1] = p[0]; alo[1] = p[1]; }
+                            { const u32x2_t p = split_pair(dz[1][gt][0], dz[1][gt][1]); ahi[2] = p[0]; alo[2] = p[1]; }
+                            { const u32x2_t p = split_pair(dz[1][gt][2], dz[1][gt][3]); ahi[3] = p[0]; alo[3] = p[1]; }
 #pragma unroll
                             for (int t = 0; t < NT; ++t) {
-                                dw[gt][t] = mfma16(ahi, hreg[t], dw[gt][t]);
-                                dw[gt][t] = mfma16(alo, hreg[t], dw[gt][t]);
+                                const u32x4_t hb = hrow(t);
+                                dw[gt][t] = mfma16(ahi, hb, dw[gt][t]);
+                                dw[gt][t] = mfma16(alo, hb, dw[gt][t]);
                             }
                         }
                     }
                 }
+                wave_sync();
             }
+        };
+
+        // chunks in pairs so the register buffers alternate without copies
+        int c = 0;
+        for (; c + 1 < nchunk; c += 2) {
+            chunk(c, hA, hB, dA, dB);
+            chunk(c + 1, hB, hA, dB, dA);
+        }
+        if (c < nchunk) {
+            chunk(c, hA, hB, dA, dB);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                hreg[t] = hnext[t];
+                hA[t] = hB[t];
+            if constexpr (MODE == BWD_W) {
+#pragma unroll
+                for (int it = 0; it < NDZ; ++it)
+                    dA[it] = dB[it];
+            }
         }
 
         if constexpr (DW) {
@@ -308,13 +419,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             col[t] = col_n[t];
-        if constexpr (PF_W) {
-#pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    wreg[gt][s] = wreg_n[gt][s];
-        }
+        rows_of(col, gp);
     }
 
     if constexpr (LOSS) {
@@ -323,24 +428,33 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     }
 }
 
+template <int G, int F, int MODE, bool LOSS, bool WZ>
+static void go(const FwdArgs& a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_group_fwd<G, F, MODE, LOSS, WZ>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int G, int F, int MODE>
+static void go_bce(bool loss, bool wz, const FwdArgs& a, int grid, hipStream_t s)
+{
+    if (loss) {
+        if (wz) go<G, F, MODE, true, true>(a, grid, s);
+        else go<G, F, MODE, true, false>(a, grid, s);
+    } else {
+        if (wz) go<G, F, MODE, false, true>(a, grid, s);
+        else go<G, F, MODE, false, false>(a, grid, s);
+    }
+}
+
 template <int G, int F>
 static bool launch_gf(int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s)
 {
+    const bool wz = a.Z != nullptr;
     switch (mode) {
-    case FWD_Z:
-        hipLaunchKernelGGL((k_group_fwd<G, F, FWD_Z, false>), dim3(grid), dim3(256), 0, s, a);
-        return true;
-    case FWD_BCE:
-        if (loss) hipLaunchKernelGGL((k_group_fwd<G, F, FWD_BCE, true>), dim3(grid), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_group_fwd<G, F, FWD_BCE, false>), dim3(grid), dim3(256), 0, s, a);
-        return true;
-    case STEP_DW:
-        if (loss) hipLaunchKernelGGL((k_group_fwd<G, F, STEP_DW, true>), dim3(grid), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_group_fwd<G, F, STEP_DW, false>), dim3(grid), dim3(256), 0, s, a);
-        return true;
-    case BWD_W:
-        hipLaunchKernelGGL((k_group_fwd<G, F, BWD_W, false>), dim3(grid), dim3(256), 0, s, a);
-        return true;
+    case FWD_Z: go<G, F, FWD_Z, false, false>(a, grid, s); return true;
+    case FWD_BCE: go_bce<G, F, FWD_BCE>(loss, wz, a, grid, s); return true;
+    case STEP_DW: go_bce<G, F, STEP_DW>(loss, wz, a, grid, s); return true;
+    case BWD_W: go<G, F, BWD_W, false, false>(a, grid, s); return true;
     }
     return false;
 }
