@@ -56,6 +56,15 @@ __device__ __forceinline__ int acc_off(int j, int r)
     return j * 16 + ((((r >> 2) ^ (j >> 2)) & 3) << 2) + (r & 3);
 }
 
+// Offset (16-bit elements) of (batch row r, 16-byte label chunk c) in the
+// dZ tile [16 rows][G]: the chunk index is XORed with (r G / 128) so the
+// matrix-core operand reads (16 rows, one chunk each) spread over the banks.
+template <int G>
+__device__ __forceinline__ int dz_off(int r, int c)
+{
+    return r * G + ((((c ^ ((r * G) >> 7))) & (G / 8 - 1)) << 3);
+}
+
 template <int G, int F, int SRC, bool DET>
 __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 {
@@ -65,15 +74,20 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     constexpr int KSG = (G + 31) / 32;  // contraction steps of P = dZ W
     constexpr int R = kDhRows;
     constexpr bool LAB = (SRC == DH_FROM_LABELS);
-    constexpr int NU = F / 32;          // gather loads per lane (16 rows x F slots)
+    constexpr int NWP = (G * F / 8 + 63) / 64;   // 16-byte pieces of W_k per lane
+    constexpr int NHP = F / 32;                  // 16-byte pieces of the gathered tile per lane
+    constexpr int DCH = G / 8;                   // 16-byte chunks of a dZ row
+    constexpr int NDP = (16 * DCH + 63) / 64;    // 16-byte pieces of the dZ tile per lane
     static_assert(R == 16, "one 16-row matrix-core tile per workgroup");
 
     extern __shared__ __attribute__((aligned(16))) float acc[];   // column-major: acc[j * 16 + row]
-    __shared__ __attribute__((aligned(16))) uint16_t sH[LAB ? 4 : 1][LAB ? F * 16 : 8];
     __shared__ __attribute__((aligned(16))) uint16_t sW[4][G * F];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[4][LAB ? F * 16 : 16 * G];
+    __shared__ __attribute__((aligned(16))) int32_t sI[4][2 * F];
+    __shared__ int sTurn;                     // accumulator hand-off counter
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
@@ -90,6 +104,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     for (int64_t i = threadIdx.x; i < R * H; i += 256)
         acc[i] = 0.f;
+    if (threadIdx.x == 0) sTurn = 0;
 
     LabelCursor cur;
     if constexpr (LAB)
@@ -100,38 +115,42 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     const bool brow_ok = brow < a.B;
     const bool tile_full = b0 + R <= a.B;
 
-    // per-round inputs, requested one round ahead
-    auto load_col = [&](int64_t kk, int (&cl)[NT]) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            cl[t] = a.idx[kk * F + 16 * t + r16];
+    uint16_t* wt = sW[wv];
+    uint16_t* tt = sT[wv];
+    int32_t* si = sI[wv];                     // two index rows, alternating by round
+
+    // All global loads below are quad-contiguous (four consecutive lanes read
+    // 64 consecutive bytes), which keeps the address units' per-cache-line
+    // work low.
+    // index row of group kk: lane < F/4 holds entries 4 lane .. +4
+    auto load_idx = [&](int64_t kk, u32x4_t& iv) {
+        if (lane < F / 4) iv = ldg16(a.idx + kk * F + 4 * lane);
     };
-    // W_k rows: lane (label 16gt + r16, q) holds slots 32s + 8q .. +8
-    auto load_w = [&](int64_t kk, u32x4_t (&wr)[GT][KSF]) {
-#pragma unroll
-        for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-            for (int s = 0; s < KSF; ++s)
-                wr[gt][s] = ldg16(a.W + ((kk * G + 16 * gt + r16) * F + 32 * s + 8 * q));
+    auto put_idx = [&](int buf, const u32x4_t& iv) {
+        if (lane < F / 4) *reinterpret_cast<u32x4_t*>(si + buf * F + 4 * lane) = iv;
     };
-    auto load_gcol = [&](int64_t kk, int (&gc)[NU]) {
+    // W_k (G x F bf16, contiguous): piece lane + 64 p
+    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-            gc[u] = a.idx[kk * F + 32 * u + (lane & 31)];
+        for (int p = 0; p < NWP; ++p)
+            if (lane + 64 * p < G * F / 8) wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
     };
-    // lane (slot 32u + lane%32, half) <- batch rows b0 + 8*half .. +8 of column gc[u]
-    auto gather = [&](const int (&gc)[NU], u32x4_t (&hv)[NU]) {
+    // gathered tile: piece lane + 64 u is slot lane/2 + 32 u, batch rows b0 + 8 (lane % 2) .. +8
+    auto gather = [&](int buf, u32x4_t (&hv)[NHP]) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-            hv[u] = ldg16(a.hT + (int64_t)gc[u] * a.Bp + b0 + 8 * (lane >> 5));
+        for (int u = 0; u < NHP; ++u) {
+            const int f = (lane >> 1) + 32 * u;
+            hv[u] = ldg16(a.hT + ((uint32_t)si[buf * F + f] * (uint32_t)a.Bp + (uint32_t)(b0 + 8 * (lane & 1))));
+        }
     };
-    // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
-    auto load_dz = [&](int64_t kk, u32x4_t (&dv)[KSG]) {
+    // dZ tile: piece pc = lane + 64 u is batch row b0 + pc / DCH, labels 8 (pc % DCH) .. +8
+    auto load_dz = [&](int64_t kk, u32x4_t (&dv)[NDP]) {
 #pragma unroll
-        for (int s = 0; s < KSG; ++s) {
-            dv[s] = u32x4_t{0u, 0u, 0u, 0u};
-            if (brow_ok && 32 * s + 8 * q < G)
-                dv[s] = ldg16(a.dZ + brow * L + kk * G + 32 * s + 8 * q);
+        for (int u = 0; u < NDP; ++u) {
+            const int pc = lane + 64 * u;
+            const int64_t b = b0 + pc / DCH;
+            dv[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (pc < 16 * DCH && b < a.B) dv[u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
         }
     };
 
@@ -142,62 +161,82 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         return kk < kc1 ? kk : kc1 - 1;       // idle waves reload a valid group
     };
 
-    int col[NT], col_n[NT];
-    u32x4_t wreg[GT][KSF], wreg_n[GT][KSF];
-    int gcol[LAB ? NU : 1], gcol_n[LAB ? NU : 1];
-    u32x4_t hv[LAB ? NU : 1], hv_n[LAB ? NU : 1];
-    u32x4_t dv[LAB ? 1 : KSG], dv_n[LAB ? 1 : KSG];
+    // Software pipeline (vector-memory operations retire in issue order, so
+    // every load is issued one round before it is needed and after the loads
+    // that must arrive first): round rd consumes the gathered tile / dZ tile
+    // and W_k of its group, issued in round rd - 1, and issues the gather for
+    // round rd + 1 (its index row arrived during round rd - 1), the index row
+    // for round rd + 2 and the weights for round rd + 1.
+    u32x4_t iv = u32x4_t{0u, 0u, 0u, 0u};
+    u32x4_t wcur[NWP];
+    u32x4_t hv[LAB ? NHP : 1];
+    u32x4_t dv[LAB ? 1 : NDP];
     if (ng > 0) {
         const int64_t kk = group_of(0);
-        load_col(kk, col);
-        load_w(kk, wreg);
-        if constexpr (LAB) {
-            load_gcol(kk, gcol);
-            gather(gcol, hv);
-        } else {
-            load_dz(kk, dv);
-        }
+        load_idx(kk, iv);
+        put_idx(0, iv);
+        wave_sync();
+        if constexpr (LAB) gather(0, hv);
+        else load_dz(kk, dv);
+        load_idx(group_of(1), iv);
+        load_w(kk, wcur);
     }
 
     __syncthreads();
 
-    uint16_t* wt = sW[wv];
-    for (int64_t rd = 0; rd < nrounds; ++rd) {
+    // One round: this wave's group k = kc0 + 4 rd + wv.  wc/hc/dc hold this
+    // round's inputs, wn/hn/dn receive the next round's.
+    auto round = [&](int64_t rd, const u32x4_t (&wc)[NWP], u32x4_t (&wn)[NWP],
+                     const u32x4_t (&hc)[LAB ? NHP : 1], u32x4_t (&hn)[LAB ? NHP : 1],
+                     const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP]) {
+        const int cb = (int)(rd & 1), nb = cb ^ 1;
         const int64_t k = kc0 + 4 * rd + wv;
         const bool active = k < kc1;
-        const int64_t kn = group_of(rd + 1 < nrounds ? rd + 1 : rd);
-        load_col(kn, col_n);
-        load_w(kn, wreg_n);
-        if constexpr (LAB) load_gcol(kn, gcol_n);
-        else load_dz(kn, dv_n);
+        const int64_t kn = group_of(rd + 1);
+        put_idx(nb, iv);
+        wave_sync();
+        if constexpr (LAB) gather(nb, hn);
+        else load_dz(kn, dn);
+        load_idx(group_of(rd + 2), iv);
+        load_w(kn, wn);
 
         f32x4_t p[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            p[t] = zero4();
-
         if (active) {
-            // W_k rows into LDS as they are (contraction over labels reads them transposed)
+            // W_k rows into LDS (the contraction over labels reads them transposed)
 #pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                for (int s = 0; s < KSF; ++s)
-                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(16 * gt + r16, 32 * s + 8 * q)) = wreg[gt][s];
+            for (int pp = 0; pp < NWP; ++pp) {
+                const int u = lane + 64 * pp;
+                if (u < G * F / 8)
+                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = wc[pp];
+            }
 
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                p[t] = zero4();
             u32x4_t ahi[KSG], alo[KSG];
             if constexpr (!LAB) {
 #pragma unroll
+                for (int u = 0; u < NDP; ++u) {
+                    const int pc = lane + 64 * u;
+                    if (pc < 16 * DCH)
+                        *reinterpret_cast<u32x4_t*>(tt + dz_off<G>(pc / DCH, pc % DCH)) = dc[u];
+                }
+                wave_sync();
+                // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
+#pragma unroll
                 for (int s = 0; s < KSG; ++s) {
-                    ahi[s] = dv[s];
+                    const int c = 4 * s + q;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tt + dz_off<G>(r16, c < DCH ? c : 0));
+                    ahi[s] = c < DCH ? v : u32x4_t{0u, 0u, 0u, 0u};
                     alo[s] = u32x4_t{0u, 0u, 0u, 0u};
                 }
             } else {
-                uint16_t* ht = sH[wv];
 #pragma unroll
-                for (int u = 0; u < NU; ++u)
-                    *reinterpret_cast<u32x4_t*>(ht + ht_off(32 * u + (lane & 31), 8 * (lane >> 5))) = hv[u];
+                for (int u = 0; u < NHP; ++u)
+                    *reinterpret_cast<u32x4_t*>(tt + ht_off((lane >> 1) + 32 * u, 8 * (lane & 1))) = hc[u];
                 wave_sync();
-                // Z^T = W_k H^T; B = H^T read transposed: lane (row r16, q) gets
+                // Z^T = W_k H^T; A = W_k rows (lane (label 16gt + r16, q): slots
+                // 32s + 8q ..), B = H^T read transposed: lane (row r16, q) gets
                 // slots 32s + 8q + e.  Result lane (row r16, q) holds labels 16gt + 4q + i.
                 f32x4_t zt[GT];
 #pragma unroll
@@ -206,10 +245,13 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 #pragma unroll
                 for (int s = 0; s < KSF; ++s) {
                     const int f0 = 32 * s + 8 * q + tr_r;
-                    const u32x4_t bv = cat(lds_tr16(ht + ht_off(f0, 4 * tr_c)), lds_tr16(ht + ht_off(f0 + 4, 4 * tr_c)));
+                    const u32x4_t bv = cat(lds_tr16(tt + ht_off(f0, 4 * tr_c)), lds_tr16(tt + ht_off(f0 + 4, 4 * tr_c)));
 #pragma unroll
-                    for (int gt = 0; gt < GT; ++gt)
-                        zt[gt] = mfma16(wreg[gt][s], bv, zt[gt]);
+                    for (int gt = 0; gt < GT; ++gt) {
+                        const u32x4_t wa =
+                            *reinterpret_cast<const u32x4_t*>(wt + wt_off<F>(16 * gt + r16, 32 * s + 8 * q));
+                        zt[gt] = mfma16(wa, bv, zt[gt]);
+                    }
                 }
                 // labels of this row for this group
                 const uint64_t mrow = cur.take(k * G, G, a.y_col);
@@ -284,48 +326,38 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             }
         }
 
-        // next round's gathered rows (their index row arrived meanwhile)
-        if constexpr (LAB) gather(gcol_n, hv_n);
-
         // scatter-add P into the accumulator columns I_k with 16-byte
         // read-add-write (rows 4q .. 4q+3 of column col[t] are adjacent).  The
-        // waves take turns (barrier-separated) so every accumulator cell is
-        // updated by one wave at a time and in group order; inside one wave
-        // the index set is duplicate-free, so no two lanes touch the same cell.
-#pragma unroll 1
-        for (int turn = 0; turn < 4; ++turn) {
-            __syncthreads();
-            if (turn == wv && active) {
-                f32x4_t v[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
-            }
-        }
-
+        // waves take turns in the fixed order (round, wave), handed on through
+        // an LDS counter, so every accumulator cell is updated by one wave at a
+        // time and in group order; inside one wave the index set is
+        // duplicate-free, so no two lanes touch the same cell.
+        int col[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            col[t] = col_n[t];
+            col[t] = si[cb * F + 16 * t + r16];
+        const int turn = (int)(4 * rd) + wv;
+        wait_turn(&sTurn, turn);
+        if (active) {
+            f32x4_t v[NT];
 #pragma unroll
-        for (int gt = 0; gt < GT; ++gt)
+            for (int t = 0; t < NT; ++t)
+                v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
 #pragma unroll
-            for (int s = 0; s < KSF; ++s)
-                wreg[gt][s] = wreg_n[gt][s];
-        if constexpr (LAB) {
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                gcol[u] = gcol_n[u];
-                hv[u] = hv_n[u];
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < KSG; ++s)
-                dv[s] = dv_n[s];
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
         }
+        pass_turn(&sTurn, turn);
+    };
+
+    u32x4_t wB[NWP];
+    u32x4_t hB[LAB ? NHP : 1], dB[LAB ? 1 : NDP];
+    int64_t rd = 0;
+    for (; rd + 1 < nrounds; rd += 2) {
+        round(rd, wcur, wB, hv, hB, dv, dB);
+        round(rd + 1, wB, wcur, hB, hv, dB, dv);
     }
+    if (rd < nrounds) round(rd, wcur, wB, hv, hB, dv, dB);
     __syncthreads();
 
     if constexpr (DET) {

@@ -70,6 +70,13 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     __shared__ __attribute__((aligned(16))) uint16_t sWk[4][FWD ? G * F : 8];
     __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sD[4][MODE == BWD_W ? 32 * DST : 2];
+    // output staging (fp32, 16 rows of OST floats): dW per 16-label tile, Z and
+    // dZ per 16 batch rows; the 4-float row padding puts the four lane groups
+    // of a write on different banks
+    constexpr int ZST = G + 4, WST = F + 4;
+    constexpr int OST = DW ? (STORE_Z || MODE == FWD_BCE ? (WST > ZST ? WST : ZST) : WST)
+                           : (STORE_Z || MODE == FWD_BCE ? ZST : 1);
+    __shared__ __attribute__((aligned(16))) float sO[4][16 * OST];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -204,6 +211,36 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 for (int t = 0; t < NT; ++t)
                     dw[gt][t] = zero4();
         }
+
+        // Store a 16-row slice of a chunk's outputs (v[gt][i]: label 16gt + r16,
+        // batch row 32c + 8q + 4mt + i) as fp32 Z or bf16 dZ rows.
+        auto store_rows = [&](const auto& v, int c, int mt, bool as_bf16) {
+            float* so = sO[wv];
+#pragma unroll
+            for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    so[(4 * q + i) * ZST + 16 * gt + r16] = v[gt][i];
+            wave_sync();
+            // piece u: local row u / (G/4) (batch row 32c + 8 (lr/4) + 4mt + lr%4), labels 4 (u % (G/4)) ..
+            constexpr int NP = (4 * G + 63) / 64;
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) {
+                const int u = lane + 64 * pp;
+                const int lr = u / (G / 4), cc = u % (G / 4);
+                const int64_t b = 32 * c + 8 * (lr >> 2) + 4 * mt + (lr & 3);
+                if (u < 4 * G && b < a.B) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc);
+                    const int64_t o = b * L + k * G + 4 * cc;
+                    if (as_bf16) {
+                        *reinterpret_cast<u32x2_t*>(a.dZ + o) = u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+                    } else {
+                        *reinterpret_cast<f32x4_t*>(a.Z + o) = x;
+                    }
+                }
+            }
+            wave_sync();
+        };
 
         // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W); the
         // next chunk's inputs go to hn / dn
@@ -348,21 +385,13 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                             }
                     }
                     if constexpr (MODE == FWD_BCE || STORE_Z) {
+                        // through LDS so that four consecutive lanes store 64
+                        // consecutive bytes of one row
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int64_t b = bq + 4 * mt + i;
-                                if (b < a.B) {
-#pragma unroll
-                                    for (int gt = 0; gt < GT; ++gt) {
-                                        const int64_t o = b * L + k * G + 16 * gt + r16;
-                                        if constexpr (MODE == FWD_BCE)
-                                            a.dZ[o] = (uint16_t)(pack_bf16(dz[mt][gt][i], 0.f) & 0xffffu);
-                                        if constexpr (STORE_Z) a.Z[o] = z[mt][gt][i];
-                                    }
-                                }
-                            }
+                        for (int mt = 0; mt < 2; ++mt) {
+                            if constexpr (STORE_Z) store_rows(z[mt], c, mt, false);
+                            if constexpr (MODE == FWD_BCE) store_rows(dz[mt], c, mt, true);
+                        }
                     }
                     if constexpr (MODE == STEP_DW) {
                         // dW_k += dZ_chunk^T H_chunk; A = dZ^T (label r16, rows 8q + e),
@@ -407,14 +436,28 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         }
 
         if constexpr (DW) {
-            // result lane (slot 16t + r16, q) holds labels 16gt + 4q + i
+            // result lane (slot 16t + r16, q) holds labels 16gt + 4q + i; through
+            // LDS per 16-label tile so the stores are contiguous 16-byte pieces
+            float* so = sO[wv];
+            constexpr int NP = (4 * F + 63) / 64;
 #pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
+            for (int gt = 0; gt < GT; ++gt) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        a.dW[(k * G + 16 * gt + 4 * q + i) * F + 16 * t + r16] = dw[gt][t][i];
+                        so[(4 * q + i) * WST + 16 * t + r16] = dw[gt][t][i];
+                wave_sync();
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    const int u = lane + 64 * pp;
+                    const int g = u / (F / 4), cc = u % (F / 4);
+                    if (u < 4 * F)
+                        *reinterpret_cast<f32x4_t*>(a.dW + (k * G + 16 * gt + g) * F + 4 * cc) =
+                            *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                }
+                wave_sync();
+            }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
