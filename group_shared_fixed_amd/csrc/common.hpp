@@ -90,22 +90,25 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // Ordered hand-off between the waves of a workgroup through a counter in LDS:
 // wait_turn blocks the wave until the counter reads v, pass_turn sets it to
-// v + 1 after the wave's earlier LDS writes.  The wait is bounded (about 2^22
-// sleeps); a caller whose turn sequence is complete never reaches the bound.
+// v + 1.  LDS executes the DS instructions of one wave in issue order, so the
+// LDS writes a wave made before pass_turn are visible to the wave that next
+// sees the counter move; only the compiler has to be kept from reordering
+// them.  The wait is bounded (2^24 polls); a caller whose turn sequence is
+// complete never reaches the bound.
 __device__ __forceinline__ void wait_turn(const int* t, int v)
 {
 #pragma unroll 1
-    for (int spin = 0; spin < (1 << 22); ++spin) {
+    for (int spin = 0; spin < (1 << 24); ++spin) {
         const int cur = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(t, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (cur == v) return;
-        __builtin_amdgcn_s_sleep(1);
     }
 }
 
 __device__ __forceinline__ void pass_turn(int* t, int v)
 {
-    __hip_atomic_store(t, v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __hip_atomic_store(t, v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // XOR swizzle of 16-byte chunks inside a row of an LDS tile so that the

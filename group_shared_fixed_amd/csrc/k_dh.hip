@@ -184,11 +184,13 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     __syncthreads();
 
-    // One round: this wave's group k = kc0 + 4 rd + wv.  wc/hc/dc hold this
-    // round's inputs, wn/hn/dn receive the next round's.
+    // One round: this wave's group k = kc0 + 4 rd + wv, up to P and its
+    // accumulator columns.  wc/hc/dc hold this round's inputs, wn/hn/dn
+    // receive the next round's.
     auto round = [&](int64_t rd, const u32x4_t (&wc)[NWP], u32x4_t (&wn)[NWP],
                      const u32x4_t (&hc)[LAB ? NHP : 1], u32x4_t (&hn)[LAB ? NHP : 1],
-                     const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP]) {
+                     const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP],
+                     f32x4_t (&p)[NT], int (&col)[NT]) {
         const int cb = (int)(rd & 1), nb = cb ^ 1;
         const int64_t k = kc0 + 4 * rd + wv;
         const bool active = k < kc1;
@@ -200,7 +202,6 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         load_idx(group_of(rd + 2), iv);
         load_w(kn, wn);
 
-        f32x4_t p[NT];
         if (active) {
             // W_k rows into LDS (the contraction over labels reads them transposed)
 #pragma unroll
@@ -326,38 +327,66 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             }
         }
 
-        // scatter-add P into the accumulator columns I_k with 16-byte
-        // read-add-write (rows 4q .. 4q+3 of column col[t] are adjacent).  The
-        // waves take turns in the fixed order (round, wave), handed on through
-        // an LDS counter, so every accumulator cell is updated by one wave at a
-        // time and in group order; inside one wave the index set is
-        // duplicate-free, so no two lanes touch the same cell.
-        int col[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             col[t] = si[cb * F + 16 * t + r16];
-        const int turn = (int)(4 * rd) + wv;
-        wait_turn(&sTurn, turn);
-        if (active) {
-            f32x4_t v[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
-        }
-        pass_turn(&sTurn, turn);
     };
 
+    // Scatter-add P into the accumulator columns I_k with 16-byte
+    // read-add-write (rows 4q .. 4q+3 of column col[t] are adjacent).  Inside
+    // one wave the index set is duplicate-free, so no two lanes touch the same
+    // cell, and a later read-add-write of the wave sees its earlier writes.
+    auto rmw = [&](const f32x4_t (&p)[NT], const int (&col)[NT]) {
+        f32x4_t v[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
+    };
+
+    // Rounds in pairs (one for wide index sets, where two P tiles would not
+    // fit in registers): the wave computes P for its groups of rounds 2i and
+    // 2i + 1, then takes its turn on the accumulator.  Turns go in the fixed
+    // order (pair, wave), handed on through an LDS counter, so every cell is
+    // updated by one wave at a time and in a fixed group order.
     u32x4_t wB[NWP];
     u32x4_t hB[LAB ? NHP : 1], dB[LAB ? 1 : NDP];
-    int64_t rd = 0;
-    for (; rd + 1 < nrounds; rd += 2) {
-        round(rd, wcur, wB, hv, hB, dv, dB);
-        round(rd + 1, wB, wcur, hB, hv, dB, dv);
+    if constexpr (F <= 64) {
+        const int64_t npairs = (nrounds + 1) / 2;
+        for (int64_t i = 0; i < npairs; ++i) {
+            const int64_t rd = 2 * i;
+            f32x4_t pa[NT], pb[NT];
+            int ca[NT], cbk[NT];
+            round(rd, wcur, wB, hv, hB, dv, dB, pa, ca);
+            const bool second = rd + 1 < nrounds;
+            if (second) round(rd + 1, wB, wcur, hB, hv, dB, dv, pb, cbk);
+            const int turn = (int)(4 * i) + wv;
+            wait_turn(&sTurn, turn);
+            if (kc0 + 4 * rd + wv < kc1) rmw(pa, ca);
+            if (second && kc0 + 4 * (rd + 1) + wv < kc1) rmw(pb, cbk);
+            pass_turn(&sTurn, turn);
+        }
+    } else {
+        auto one = [&](int64_t rd, const u32x4_t (&wc)[NWP], u32x4_t (&wn)[NWP],
+                       const u32x4_t (&hc)[LAB ? NHP : 1], u32x4_t (&hn)[LAB ? NHP : 1],
+                       const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP]) {
+            f32x4_t pa[NT];
+            int ca[NT];
+            round(rd, wc, wn, hc, hn, dc, dn, pa, ca);
+            const int turn = (int)(4 * rd) + wv;
+            wait_turn(&sTurn, turn);
+            if (kc0 + 4 * rd + wv < kc1) rmw(pa, ca);
+            pass_turn(&sTurn, turn);
+        };
+        int64_t rd = 0;
+        for (; rd + 1 < nrounds; rd += 2) {
+            one(rd, wcur, wB, hv, hB, dv, dB);
+            one(rd + 1, wB, wcur, hB, hv, dB, dv);
+        }
+        if (rd < nrounds) one(rd, wcur, wB, hv, hB, dv, dB);
     }
-    if (rd < nrounds) round(rd, wcur, wB, hv, hB, dv, dB);
     __syncthreads();
 
     if constexpr (DET) {
