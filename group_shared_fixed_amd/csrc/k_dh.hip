@@ -83,7 +83,6 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     extern __shared__ __attribute__((aligned(16))) float acc[];   // column-major: acc[j * 16 + row]
     __shared__ __attribute__((aligned(16))) uint16_t sW[4][G * F];
     __shared__ __attribute__((aligned(16))) uint16_t sT[4][LAB ? F * 16 : 16 * G];
-    __shared__ __attribute__((aligned(16))) int32_t sI[4][2 * F];
     __shared__ int sTurn;                     // accumulator hand-off counter
 
     const int lane = threadIdx.x & 63;
@@ -117,31 +116,37 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     uint16_t* wt = sW[wv];
     uint16_t* tt = sT[wv];
-    int32_t* si = sI[wv];                     // two index rows, alternating by round
 
-    // All global loads below are quad-contiguous (four consecutive lanes read
-    // 64 consecutive bytes), which keeps the address units' per-cache-line
-    // work low.
-    // index row of group kk: lane < F/4 holds entries 4 lane .. +4
-    auto load_idx = [&](int64_t kk, u32x4_t& iv) {
-        if (lane < F / 4) iv = ldg16(a.idx + kk * F + 4 * lane);
+    // Inputs of one round of a wave.
+    struct Stage {
+        u32x4_t w[NWP];             // W_k (G x F, contiguous) as 16-byte pieces lane + 64 p
+        u32x4_t h[LAB ? NHP : 1];   // gathered tile pieces
+        u32x4_t d[LAB ? 1 : NDP];   // dZ tile pieces
+        int col[NT];                // accumulator columns I_k[16t + r16]
     };
-    auto put_idx = [&](int buf, const u32x4_t& iv) {
-        if (lane < F / 4) *reinterpret_cast<u32x4_t*>(si + buf * F + 4 * lane) = iv;
-    };
-    // W_k (G x F bf16, contiguous): piece lane + 64 p
+    // W_k as contiguous 16-byte pieces (four consecutive lanes read 64
+    // consecutive bytes, which keeps the address units' per-line work low)
     auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
 #pragma unroll
         for (int p = 0; p < NWP; ++p)
             if (lane + 64 * p < G * F / 8) wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
     };
-    // gathered tile: piece lane + 64 u is slot lane/2 + 32 u, batch rows b0 + 8 (lane % 2) .. +8
-    auto gather = [&](int buf, u32x4_t (&hv)[NHP]) {
+    auto load_col = [&](int64_t kk, int (&cl)[NT]) {
 #pragma unroll
-        for (int u = 0; u < NHP; ++u) {
-            const int f = (lane >> 1) + 32 * u;
-            hv[u] = ldg16(a.hT + ((uint32_t)si[buf * F + f] * (uint32_t)a.Bp + (uint32_t)(b0 + 8 * (lane & 1))));
-        }
+        for (int t = 0; t < NT; ++t)
+            cl[t] = a.idx[kk * F + 16 * t + r16];
+    };
+    // gathered tile: piece lane + 64 u is slot lane/2 + 32 u, batch rows
+    // b0 + 8 (lane % 2) .. +8, so four consecutive lanes read two 32-byte runs
+    auto load_gcol = [&](int64_t kk, int (&gc)[NHP]) {
+#pragma unroll
+        for (int u = 0; u < NHP; ++u)
+            gc[u] = a.idx[kk * F + (lane >> 1) + 32 * u];
+    };
+    auto gather = [&](const int (&gc)[NHP], u32x4_t (&hv)[NHP]) {
+#pragma unroll
+        for (int u = 0; u < NHP; ++u)
+            hv[u] = ldg16(a.hT + ((uint32_t)gc[u] * (uint32_t)a.Bp + (uint32_t)(b0 + 8 * (lane & 1))));
     };
     // dZ tile: piece pc = lane + 64 u is batch row b0 + pc / DCH, labels 8 (pc % DCH) .. +8
     auto load_dz = [&](int64_t kk, u32x4_t (&dv)[NDP]) {
@@ -162,45 +167,42 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     };
 
     // Software pipeline (vector-memory operations retire in issue order, so
-    // every load is issued one round before it is needed and after the loads
-    // that must arrive first): round rd consumes the gathered tile / dZ tile
-    // and W_k of its group, issued in round rd - 1, and issues the gather for
-    // round rd + 1 (its index row arrived during round rd - 1), the index row
-    // for round rd + 2 and the weights for round rd + 1.
-    u32x4_t iv = u32x4_t{0u, 0u, 0u, 0u};
-    u32x4_t wcur[NWP];
-    u32x4_t hv[LAB ? NHP : 1];
-    u32x4_t dv[LAB ? 1 : NDP];
+    // every load is issued a round before it is needed and after the loads
+    // that must arrive first): round rd consumes the gathered tile / dZ tile,
+    // W_k and columns of its group, all issued in round rd - 1, and issues
+    // the gather for round rd + 1 (its index entries arrived during round
+    // rd - 1), the gather indices for round rd + 2, and the columns and
+    // weights for round rd + 1.
+    Stage sa, sb;
+    int gcn[LAB ? NHP : 1];
     if (ng > 0) {
         const int64_t kk = group_of(0);
-        load_idx(kk, iv);
-        put_idx(0, iv);
-        wave_sync();
-        if constexpr (LAB) gather(0, hv);
-        else load_dz(kk, dv);
-        load_idx(group_of(1), iv);
-        load_w(kk, wcur);
+        if constexpr (LAB) {
+            load_gcol(kk, gcn);
+            gather(gcn, sa.h);
+            load_gcol(group_of(1), gcn);
+        } else {
+            load_dz(kk, sa.d);
+        }
+        load_col(kk, sa.col);
+        load_w(kk, sa.w);
     }
 
     __syncthreads();
 
-    // One round: this wave's group k = kc0 + 4 rd + wv, up to P and its
-    // accumulator columns.  wc/hc/dc hold this round's inputs, wn/hn/dn
-    // receive the next round's.
-    auto round = [&](int64_t rd, const u32x4_t (&wc)[NWP], u32x4_t (&wn)[NWP],
-                     const u32x4_t (&hc)[LAB ? NHP : 1], u32x4_t (&hn)[LAB ? NHP : 1],
-                     const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP],
-                     f32x4_t (&p)[NT], int (&col)[NT]) {
-        const int cb = (int)(rd & 1), nb = cb ^ 1;
+    // One round: this wave's group k = kc0 + 4 rd + wv, up to P.
+    auto round = [&](int64_t rd, const Stage& c, Stage& n, f32x4_t (&p)[NT]) {
         const int64_t k = kc0 + 4 * rd + wv;
         const bool active = k < kc1;
         const int64_t kn = group_of(rd + 1);
-        put_idx(nb, iv);
-        wave_sync();
-        if constexpr (LAB) gather(nb, hn);
-        else load_dz(kn, dn);
-        load_idx(group_of(rd + 2), iv);
-        load_w(kn, wn);
+        if constexpr (LAB) {
+            gather(gcn, n.h);
+            load_gcol(group_of(rd + 2), gcn);
+        } else {
+            load_dz(kn, n.d);
+        }
+        load_col(kn, n.col);
+        load_w(kn, n.w);
 
         if (active) {
             // W_k rows into LDS (the contraction over labels reads them transposed)
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             for (int pp = 0; pp < NWP; ++pp) {
                 const int u = lane + 64 * pp;
                 if (u < G * F / 8)
-                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = wc[pp];
+                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = c.w[pp];
             }
 
 #pragma unroll
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 for (int u = 0; u < NDP; ++u) {
                     const int pc = lane + 64 * u;
                     if (pc < 16 * DCH)
-                        *reinterpret_cast<u32x4_t*>(tt + dz_off<G>(pc / DCH, pc % DCH)) = dc[u];
+                        *reinterpret_cast<u32x4_t*>(tt + dz_off<G>(pc / DCH, pc % DCH)) = c.d[u];
                 }
                 wave_sync();
                 // A = dZ rows of the tile: lane (row r16, q) holds labels 32s + 8q .. +8
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             } else {
 #pragma unroll
                 for (int u = 0; u < NHP; ++u)
-                    *reinterpret_cast<u32x4_t*>(tt + ht_off((lane >> 1) + 32 * u, 8 * (lane & 1))) = hc[u];
+                    *reinterpret_cast<u32x4_t*>(tt + ht_off((lane >> 1) + 32 * u, 8 * (lane & 1))) = c.h[u];
                 wave_sync();
                 // Z^T = W_k H^T; A = W_k rows (lane (label 16gt + r16, q): slots
                 // 32s + 8q ..), B = H^T read transposed: lane (row r16, q) gets
@@ -327,9 +329,6 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             }
         }
 
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            col[t] = si[cb * F + 16 * t + r16];
     };
 
     // Scatter-add P into the accumulator columns I_k with 16-byte
@@ -351,41 +350,39 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     // 2i + 1, then takes its turn on the accumulator.  Turns go in the fixed
     // order (pair, wave), handed on through an LDS counter, so every cell is
     // updated by one wave at a time and in a fixed group order.
-    u32x4_t wB[NWP];
-    u32x4_t hB[LAB ? NHP : 1], dB[LAB ? 1 : NDP];
     if constexpr (F <= 64) {
         const int64_t npairs = (nrounds + 1) / 2;
         for (int64_t i = 0; i < npairs; ++i) {
             const int64_t rd = 2 * i;
             f32x4_t pa[NT], pb[NT];
-            int ca[NT], cbk[NT];
-            round(rd, wcur, wB, hv, hB, dv, dB, pa, ca);
+            int ca[NT];
+            round(rd, sa, sb, pa);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                ca[t] = sa.col[t];
             const bool second = rd + 1 < nrounds;
-            if (second) round(rd + 1, wB, wcur, hB, hv, dB, dv, pb, cbk);
+            if (second) round(rd + 1, sb, sa, pb);
             const int turn = (int)(4 * i) + wv;
             wait_turn(&sTurn, turn);
             if (kc0 + 4 * rd + wv < kc1) rmw(pa, ca);
-            if (second && kc0 + 4 * (rd + 1) + wv < kc1) rmw(pb, cbk);
+            if (second && kc0 + 4 * (rd + 1) + wv < kc1) rmw(pb, sb.col);
             pass_turn(&sTurn, turn);
         }
     } else {
-        auto one = [&](int64_t rd, const u32x4_t (&wc)[NWP], u32x4_t (&wn)[NWP],
-                       const u32x4_t (&hc)[LAB ? NHP : 1], u32x4_t (&hn)[LAB ? NHP : 1],
-                       const u32x4_t (&dc)[LAB ? 1 : NDP], u32x4_t (&dn)[LAB ? 1 : NDP]) {
+        auto one = [&](int64_t rd, const Stage& c, Stage& n) {
             f32x4_t pa[NT];
-            int ca[NT];
-            round(rd, wc, wn, hc, hn, dc, dn, pa, ca);
+            round(rd, c, n, pa);
             const int turn = (int)(4 * rd) + wv;
             wait_turn(&sTurn, turn);
-            if (kc0 + 4 * rd + wv < kc1) rmw(pa, ca);
+            if (kc0 + 4 * rd + wv < kc1) rmw(pa, c.col);
             pass_turn(&sTurn, turn);
         };
         int64_t rd = 0;
         for (; rd + 1 < nrounds; rd += 2) {
-            one(rd, wcur, wB, hv, hB, dv, dB);
-            one(rd + 1, wB, wcur, hB, hv, dB, dv);
+            one(rd, sa, sb);
+            one(rd + 1, sb, sa);
         }
-        if (rd < nrounds) one(rd, wcur, wB, hv, hB, dv, dB);
+        if (rd < nrounds) one(rd, sa, sb);
     }
     __syncthreads();
 
