@@ -8,8 +8,16 @@ gradient (libhaste's haste_step), on the Amazon-3M-shaped workload
 positives per sample; synthetic seeded inputs already resident in HBM).
 
 Prints ONE JSON line.  Besides the required fields it carries
-  roofline      dominant kernel (forward + BCE + dW) against HBM bandwidth,
-                from HIP events recorded around that kernel on its stream;
+  roofline      the kernel with the larger share of the step (forward + BCE +
+                dW, or the feature-gradient kernel) against HBM bandwidth:
+                algorithmic bytes per launch over its average duration, from
+                HIP events recorded around it on its stream; `traffic` is the
+                HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE
+                counters read for it, each scaled by what the same counter
+                reads for a plain copy of known size (taken from the counter
+                file under profiles/, and null when the kernel's sources have
+                changed since those counters were taken);
+  roofline_other the same figures for the other kernel;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same step;
   kernels_us    per-phase averages from the same events;
   extra         unfused calls and the G = 1 per-label baseline on the same
@@ -29,6 +37,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tail-layer fwd+bwd samples/s and useful TFLOP/s (% bf16 MFMA peak), L=3M G=32"
+CSRC = os.path.join(ROOT, "group_shared_fixed_amd", "csrc")
+# sources each measured kernel is compiled from (for the counter file's validity)
+KERNEL_SOURCES = {
+    "k_group_fwd": ["k_fwd.hip", "common.hpp", "kernels.hpp"],
+    "k_group_dh": ["k_dh.hip", "common.hpp", "kernels.hpp"],
+}
+COPY_BYTES = 1 << 30           # plain copy used to scale the byte counters
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 
@@ -69,6 +85,76 @@ class HipEvents:
     def close(self):
         for i in range(self.n):
             self.hip.hipEventDestroy(self.ev[i])
+
+
+def source_sha256(kernel):
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def counter_file(workload):
+    return os.path.join(ROOT, "profiles", f"hbm_counters_{workload}_step.json")
+
+
+def read_counter_csv(path):
+    """Average counter value per dispatch, by kernel base name, from a
+    rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    acc = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "").strip()
+            key = (name, r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_counters(fetch_csv, write_csv, workload, commands):
+    """Write the counter file from the FETCH_SIZE and WRITE_SIZE runs of
+    `bench.py --counter-run` (KiB per dispatch)."""
+    fetch, write = read_counter_csv(fetch_csv), read_counter_csv(write_csv)
+
+    def pick(pred, counter, table):
+        hits = [(v, k[0]) for k, v in table.items() if k[1] == counter and pred(k[0])]
+        if not hits:
+            raise SystemExit(f"no dispatch matching for {counter}")
+        return max(hits)
+
+    out = {"workload": workload, "unit": "KiB per dispatch", "commands": commands, "copy": {}, "kernels": {}}
+    cf, cname = pick(lambda n: "elementwise" in n or "copy" in n.lower(), "FETCH_SIZE", fetch)
+    cw, _ = pick(lambda n: n == cname, "WRITE_SIZE", write)
+    out["copy"] = {"kernel": cname, "bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw}
+    for kern in KERNEL_SOURCES:
+        f, name = pick(lambda n, kern=kern: kern in n, "FETCH_SIZE", fetch)
+        wv, _ = pick(lambda n, name=name: n == name, "WRITE_SIZE", write)
+        out["kernels"][kern] = {"dispatch": name, "fetch_kib": f, "write_kib": wv,
+                                "source_sha256": source_sha256(kern)}
+    with open(counter_file(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    log(f"[bench] wrote {counter_file(workload)}")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the counter file, scaled by the
+    copy calibration; None if absent or taken from other sources."""
+    try:
+        with open(counter_file(workload)) as fh:
+            c = json.load(fh)
+        k = c["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k["source_sha256"] != source_sha256(kernel):
+        return None
+    cp = c["copy"]
+    f_scale = cp["bytes"] / (cp["fetch_kib"] * 1024.0)
+    w_scale = cp["bytes"] / (cp["write_kib"] * 1024.0)
+    return int(round(1024.0 * (k["fetch_kib"] * f_scale + k["write_kib"] * w_scale)))
 
 
 def bf16_dev(a, dev):
@@ -138,7 +224,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip unfused calls and the G=1 baseline")
     ap.add_argument("--report", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="short run for rocprofv3 --pmc: a few steps plus a plain 1 GiB copy, no JSON line")
+    ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the counter file under profiles/ from the two --counter-run counter CSVs")
+    ap.add_argument("--commands", default="", help="with --ingest: the profiling commands, recorded in the file")
     args = ap.parse_args()
+
+    if args.ingest:
+        ingest_counters(args.ingest[0], args.ingest[1], args.workload, args.commands)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and measured on a single MI355X; "
@@ -168,6 +263,18 @@ def main():
            "dh": torch.empty(B, H, dtype=torch.float32, device=dev), "Z": None, "loss": None}
     ws = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, args.mode)), dtype=torch.uint8, device=dev)
 
+    if args.counter_run:
+        for _ in range(3):
+            hs.step(h, idx, W, rp, col, s, G, mode=args.mode, out=out, workspace=ws)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] counter run done (3 steps, 2 copies of 1 GiB)")
+        return
+
     nev = 5 * args.steps
     ev = HipEvents(nev + 2)
 
@@ -191,12 +298,26 @@ def main():
     ph = {"prep_us": 1e3 * avg(0, 1), "fwd_bce_dw_us": 1e3 * avg(1, 2), "dh_us": 1e3 * avg(2, 3),
           "dh_reduce_us": 1e3 * avg(3, 4), "step_events_us": 1e3 * avg(0, 4)}
     nnz = int(d["y_rowptr"][-1])
-    # algorithmic bytes of the forward + BCE + dW kernel: W, idx, h, labels in; dW out
-    bytes_a = L * F * 2 + K * F * 4 + B * H * 2 + (B + 1) * 4 + nnz * 4 + L * F * 4
-    t_a = ph["fwd_bce_dw_us"] * 1e-6
+    labels_bytes = (B + 1) * 4 + nnz * 4
+    # algorithmic bytes per launch: every input read once from HBM, every output written once
+    # forward + BCE + dW: W, idx, h, labels in; dW out
+    bytes_a = L * F * 2 + K * F * 4 + B * H * 2 + labels_bytes + L * F * 4
+    # feature gradient: W, idx, h, labels in; dh out
+    bytes_b = L * F * 2 + K * F * 4 + B * H * 2 + labels_bytes + B * H * 4
     flops_step = 6 * B * L * F
     useful_tflops = flops_step / (ms_step * 1e-3) / 1e12
     step_bytes = bytes_a + B * H * 4
+
+    def roof(kernel, label, nbytes, us):
+        ach = nbytes / (us * 1e-6) / 1e9
+        return {"kernel": label, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
+                "algorithmic_bytes": nbytes, "avg_us": round(us, 2)}
+
+    ra = roof("k_group_fwd", "k_group_fwd<STEP_DW> (forward + BCE + dW)", bytes_a, ph["fwd_bce_dw_us"])
+    rb = roof("k_group_dh", "k_group_dh<DH_FROM_LABELS> (feature gradient, logits recomputed)", bytes_b,
+              ph["dh_us"])
+    dom, other = (rb, ra) if ph["dh_us"] >= ph["fwd_bce_dw_us"] else (ra, rb)
     res = {
         "metric": METRIC,
         "value": round(B / (ms_step * 1e-3), 1),
@@ -216,10 +337,8 @@ def main():
         "useful_tflops": round(useful_tflops, 2),
         "pct_bf16_peak": round(100 * useful_tflops / BF16_PEAK_TFLOPS, 2),
         "step_hbm_floor_us": round(step_bytes / HBM_PEAK_GBS / 1e3, 1),
-        "roofline": {"kernel": "k_group_fwd<STEP_DW> (forward + BCE + dW)", "bound": "hbm",
-                     "achieved": round(bytes_a / t_a / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(bytes_a / t_a / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": bytes_a, "avg_us": round(ph["fwd_bce_dw_us"], 2)},
+        "roofline": dom,
+        "roofline_other": other,
         "kernels_us": {k: round(v, 2) for k, v in ph.items()},
     }
     log(f"[bench] step {ms_step:.3f} ms  phases {res['kernels_us']}")
