@@ -100,7 +100,9 @@ def test_step_fullsize_sampled(name):
     # atomic mode agrees with deterministic mode, deterministic mode repeats
     say("  step[atomic] and step[det] repeat")
     dh_at = to_host(hs.step(h, idx, W, rp, col, s, G, mode="atomic")["dh"])
-    assert_parity(dh_at, dh, "dh atomic vs det", rel=1e-5, mabs=1e-6)
+    # the two modes add the same fp32 partials in different orders: they agree
+    # to a few fp32 ulps of the largest |dh|, far inside the oracle tolerance
+    assert_parity(dh_at, dh, "dh atomic vs det", rel=1e-5, mabs=1e-5 * float(np.abs(dh).max()))
     dh2 = to_host(hs.step(h, idx, W, rp, col, s, G, mode="det")["dh"])
     assert (dh2.view(np.uint32) == dh.view(np.uint32)).all(), "deterministic dh not bitwise repeatable"
 
