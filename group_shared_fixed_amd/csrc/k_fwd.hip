@@ -26,9 +26,10 @@
 // layout of the weight-gradient product: no data moves between the two.
 //
 // Vector-memory operations retire in issue order, so waiting for one load
-// also waits for every older one.  The next group's weights (an HBM round
-// trip) are therefore requested only after the last gather of the current
-// group that is still needed before them.
+// also waits for every older one, and loads share their counter with stores.
+// Each chunk therefore first waits for its own rows, then issues the stores
+// deferred from the previous chunk or group (staged in LDS), then the loads
+// of the next chunk and, once per group, the next group's weights.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -60,26 +61,33 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     constexpr bool FWD = (MODE != BWD_W);          // runs the forward product
     constexpr bool DW = (MODE == STEP_DW || MODE == BWD_W);
     constexpr bool STORE_Z = (MODE == FWD_Z) || WZ;
-    constexpr int DST = G + 2;                     // row stride of the dZ tile (BWD_W)
+    constexpr bool STORE_DZ = (MODE == FWD_BCE);
+    constexpr int DST = G + 2;                     // row stride of the dZ input tile (BWD_W)
     constexpr int NDZ = (32 * G / 8 + 63) / 64;    // 16-byte dZ pieces per lane per chunk (BWD_W)
     // Prefetch the next group's weights only when they are small; wide tiles
     // would push the wave past 256 registers (two waves per SIMD).
     constexpr bool PF_W = FWD && (GT * KS <= 4);
+    // Output staging in LDS (row strides padded by 4 floats / 8 halves).  A
+    // group's whole dW is staged and stored after the next group's first
+    // wait when it fits; wide tiles go out per 16-label tile at once.
+    constexpr int ZST = G + 4, DZST = G + 8, WST = F + 4;
+    constexpr bool DEFER_DW = DW && (G * WST <= 2304);
+    constexpr int DW_ROWS = DEFER_DW ? G : 16;
+    // wide fused tiles with the optional Z output share one staging area
+    // (Z is flushed before dW is staged)
+    constexpr bool ALIAS_WZ = DW && !DEFER_DW && STORE_Z;
+    constexpr int WO_SIZE = DW ? (ALIAS_WZ && 32 * ZST > DW_ROWS * WST ? 32 * ZST : DW_ROWS * WST) : 4;
 
     __shared__ __attribute__((aligned(16))) uint16_t sH[4][32 * F];
     __shared__ __attribute__((aligned(16))) uint16_t sWk[4][FWD ? G * F : 8];
     __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sD[4][MODE == BWD_W ? 32 * DST : 2];
-    // output staging (fp32, 16 rows of OST floats): dW per 16-label tile, Z and
-    // dZ per 16 batch rows; the 4-float row padding puts the four lane groups
-    // of a write on different banks
-    constexpr int ZST = G + 4, WST = F + 4;
-    constexpr int OST = DW ? (STORE_Z || MODE == FWD_BCE ? (WST > ZST ? WST : ZST) : WST)
-                           : (STORE_Z || MODE == FWD_BCE ? ZST : 1);
-    __shared__ __attribute__((aligned(16))) float sO[4][16 * OST];
+    __shared__ __attribute__((aligned(16))) float sWo[4][WO_SIZE];
+    __shared__ __attribute__((aligned(16))) float sZo[4][STORE_Z && !ALIAS_WZ ? 32 * ZST : 4];
+    __shared__ __attribute__((aligned(16))) uint16_t sDo[4][STORE_DZ ? 32 * DZST : 8];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r16 = lane & 15;
     const int q = lane >> 4;
     const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     const int64_t k0 = gw * a.K / nw;
     const int64_t k1 = (gw + 1) * a.K / nw;
     const int nchunk = (int)(a.Bp / 32);
-    const int wchunk = nchunk >= 2 ? nchunk - 2 : 0;   // chunk that requests the next W
+    const int wchunk = nchunk >= 2 ? 1 : 0;   // chunk that requests the next group's weights
     const float scale = a.scale;
     const float inv_s = 1.0f / a.scale;
 
@@ -143,9 +151,69 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         }
     };
 
+    // Deferred stores.  Vector-memory loads and stores share one counter, and
+    // a wait for a load while a store is outstanding drains everything, so
+    // outputs are staged in LDS and stored right after the next wait for
+    // input data, a whole chunk of work before the next wait.
+    int64_t pend_dw = -1;                    // group whose dW sits in sWo
+    int64_t pend_zk = -1;                    // group and chunk whose Z / dZ sit in sZo / sDo
+    int pend_zc = 0;
+    auto flush_dw = [&]() {
+        if constexpr (DEFER_DW) {
+            if (pend_dw >= 0) {
+                const float* so = sWo[wv];
+                constexpr int NP = (G * F / 4 + 63) / 64;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    const int u = lane + 64 * pp;
+                    const int g = u / (F / 4), cc = u % (F / 4);
+                    if (u < G * F / 4)
+                        *reinterpret_cast<f32x4_t*>(a.dW + (pend_dw * G + g) * F + 4 * cc) =
+                            *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                }
+                pend_dw = -1;
+            }
+        }
+    };
+    auto flush_z = [&]() {
+        if constexpr (STORE_Z || STORE_DZ) {
+            if (pend_zk >= 0) {
+                if constexpr (STORE_Z) {
+                    // piece u: chunk row u / (G/4), labels 4 (u % (G/4)) ..
+                    const float* so = ALIAS_WZ ? sWo[wv] : sZo[wv];
+                    constexpr int NP = (8 * G + 63) / 64;
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) {
+                        const int u = lane + 64 * pp;
+                        const int lr = u / (G / 4), cc = u % (G / 4);
+                        const int64_t b = 32 * pend_zc + lr;
+                        if (u < 8 * G && b < a.B)
+                            *reinterpret_cast<f32x4_t*>(a.Z + b * L + pend_zk * G + 4 * cc) =
+                                *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc);
+                    }
+                }
+                if constexpr (STORE_DZ) {
+                    // piece u: chunk row u / (G/8), labels 8 (u % (G/8)) ..
+                    const uint16_t* so = sDo[wv];
+                    constexpr int NP = (4 * G + 63) / 64;
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) {
+                        const int u = lane + 64 * pp;
+                        const int lr = u / (G / 8), cc = u % (G / 8);
+                        const int64_t b = 32 * pend_zc + lr;
+                        if (u < 4 * G && b < a.B)
+                            *reinterpret_cast<u32x4_t*>(a.dZ + b * L + pend_zk * G + 8 * cc) =
+                                *reinterpret_cast<const u32x4_t*>(so + lr * DZST + 8 * cc);
+                    }
+                }
+                pend_zk = -1;
+            }
+        }
+    };
+
     int col[NT], col_n[NT];
     const uint16_t* gp[NT];
-    u32x4_t wraw[NWP];                      // next weights as loaded
+    u32x4_t wraw[NWP];                      // weights as loaded
     u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
     u32x4_t hA[NT], hB[NT];
     u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1];
@@ -159,6 +227,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
 
     for (int64_t k = k0; k < k1; ++k) {
         const int64_t kn = k + 1 < k1 ? k + 1 : k;
+        // the next group's index entries: needed by the last chunk's request,
+        // so they are loaded before any chunk of this group
         load_col(kn, col_n);
         if constexpr (FWD) {
             // this group's weights: through LDS into the matrix-core B layout
@@ -212,41 +282,33 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     dw[gt][t] = zero4();
         }
 
-        // Store a 16-row slice of a chunk's outputs (v[gt][i]: label 16gt + r16,
-        // batch row 32c + 8q + 4mt + i) as fp32 Z or bf16 dZ rows.
-        auto store_rows = [&](const auto& v, int c, int mt, bool as_bf16) {
-            float* so = sO[wv];
-#pragma unroll
-            for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    so[(4 * q + i) * ZST + 16 * gt + r16] = v[gt][i];
-            wave_sync();
-            // piece u: local row u / (G/4) (batch row 32c + 8 (lr/4) + 4mt + lr%4), labels 4 (u % (G/4)) ..
-            constexpr int NP = (4 * G + 63) / 64;
-#pragma unroll
-            for (int pp = 0; pp < NP; ++pp) {
-                const int u = lane + 64 * pp;
-                const int lr = u / (G / 4), cc = u % (G / 4);
-                const int64_t b = 32 * c + 8 * (lr >> 2) + 4 * mt + (lr & 3);
-                if (u < 4 * G && b < a.B) {
-                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc);
-                    const int64_t o = b * L + k * G + 4 * cc;
-                    if (as_bf16) {
-                        *reinterpret_cast<u32x2_t*>(a.dZ + o) = u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-                    } else {
-                        *reinterpret_cast<f32x4_t*>(a.Z + o) = x;
-                    }
-                }
-            }
-            wave_sync();
-        };
-
         // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W); the
         // next chunk's inputs go to hn / dn
         auto chunk = [&](int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT], u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1],
                          u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1]) {
-            // 1. request the next chunk (or the next group's first chunk)
+            // 1. this chunk's rows into the wave's LDS tile [slot][32 batch rows]
+            //    (the wait for the chunk's loads)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<u32x4_t*>(tile + tile_off(16 * t + qr, 8 * qc)) = hc[t];
+            if constexpr (MODE == BWD_W) {
+                // dZ chunk into LDS [row][label]
+                uint16_t* dt = sD[wv];
+#pragma unroll
+                for (int it = 0; it < NDZ; ++it) {
+                    const int ci = lane + 64 * it;
+                    if (ci < 32 * G / 8) {
+                        const int r = ci / (G / 8), gc = ci % (G / 8);
+                        uint32_t* d32 = reinterpret_cast<uint32_t*>(dt + r * DST + 8 * gc);
+                        d32[0] = dc[it][0]; d32[1] = dc[it][1]; d32[2] = dc[it][2]; d32[3] = dc[it][3];
+                    }
+                }
+            }
+            // 2. stores deferred from the previous chunk / group
+            flush_z();
+            if (c == 0) flush_dw();
+            // 3. requests: the next chunk (or the next group's first chunk), and
+            //    once per group the next group's weights and index entries
             if (c + 1 < nchunk) {
                 gather(gp, c + 1, hn);
                 if constexpr (MODE == BWD_W) load_dz(k, c + 1, dn);
@@ -259,30 +321,15 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             if constexpr (PF_W) {
                 if (c == wchunk) load_w(kn, wraw);
             }
-
-            // 2. the rows into the wave's LDS tile [slot][32 batch rows]
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *reinterpret_cast<u32x4_t*>(tile + tile_off(16 * t + qr, 8 * qc)) = hc[t];
+            wave_sync();
             // B operand of the weight-gradient product: lane (slot 16t + r16, q)
-            // holds batch rows 32c + 8q .. +8 (read after the wave_sync below)
+            // holds batch rows 32c + 8q .. +8
             auto hrow = [&](int t) {
                 return *reinterpret_cast<const u32x4_t*>(tile + tile_off(16 * t + r16, 8 * q));
             };
             if constexpr (MODE == BWD_W) {
-                // dZ chunk into LDS [row][label], then dW_k += dZ_chunk^T H_chunk
-                uint16_t* dt = sD[wv];
-#pragma unroll
-                for (int it = 0; it < NDZ; ++it) {
-                    const int ci = lane + 64 * it;
-                    if (ci < 32 * G / 8) {
-                        const int r = ci / (G / 8), gc = ci % (G / 8);
-                        uint32_t* d32 = reinterpret_cast<uint32_t*>(dt + r * DST + 8 * gc);
-                        d32[0] = dc[it][0]; d32[1] = dc[it][1]; d32[2] = dc[it][2]; d32[3] = dc[it][3];
-                    }
-                }
-                wave_sync();
-                // A lane (label r16, q): rows 8q + e
+                // dW_k += dZ_chunk^T H_chunk; A lane (label r16, q): rows 8q + e
+                const uint16_t* dt = sD[wv];
 #pragma unroll
                 for (int gt = 0; gt < GT; ++gt) {
                     const uint16_t* cp = dt + 8 * q * DST + 16 * gt + r16;
@@ -297,8 +344,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 wave_sync();
                 return;
             } else {
-                wave_sync();
-                // 3. Z_chunk = H_chunk W_k^T with A = H read transposed from the
+                // 4. Z_chunk = H_chunk W_k^T with A = H read transposed from the
                 //    tile.  A row m of tile mt is batch row 8*(m/4) + 4*mt + m%4, so
                 //    result lane (label r16, q) holds batch rows 8q + 4*mt + i.
                 f32x4_t z[2][GT];
@@ -319,23 +365,21 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                             z[mt][gt] = mfma16(av, wreg[gt][s], z[mt][gt]);
                     }
                 }
-                wave_sync();
 
-                // 4. epilogue over batch rows b = 32c + 8q + 4mt + i, label g = 16gt + r16
+                // 5. epilogue over batch rows b = 32c + 8q + 4mt + i, label g = 16gt + r16;
+                //    chunk outputs are staged for the deferred store (chunk row 8q + 4mt + i)
                 const int64_t bq = 32 * c + 8 * q;
-                if constexpr (MODE == FWD_Z) {
+                if constexpr (STORE_Z) {
+                    float* so = ALIAS_WZ ? sWo[wv] : sZo[wv];
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int64_t b = bq + 4 * mt + i;
-                            if (b < a.B) {
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                                for (int gt = 0; gt < GT; ++gt)
-                                    a.Z[b * L + k * G + 16 * gt + r16] = z[mt][gt][i];
-                            }
-                        }
-                } else {
+                            for (int gt = 0; gt < GT; ++gt)
+                                so[(8 * q + 4 * mt + i) * ZST + 16 * gt + r16] = z[mt][gt][i];
+                }
+                if constexpr (MODE != FWD_Z) {
                     float dz[2][GT][4];
                     if constexpr (!LOSS) {
                         // s * sigmoid(z) = 1 / ((1 + e^-z) / s), and e^-z = +inf gives 0
@@ -384,14 +428,16 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                                 }
                             }
                     }
-                    if constexpr (MODE == FWD_BCE || STORE_Z) {
-                        // through LDS so that four consecutive lanes store 64
-                        // consecutive bytes of one row
+                    if constexpr (STORE_DZ) {
+                        uint16_t* so = sDo[wv];
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt) {
-                            if constexpr (STORE_Z) store_rows(z[mt], c, mt, false);
-                            if constexpr (MODE == FWD_BCE) store_rows(dz[mt], c, mt, true);
-                        }
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int gt = 0; gt < GT; ++gt)
+                                    so[(8 * q + 4 * mt + i) * DZST + 16 * gt + r16] =
+                                        (uint16_t)(pack_bf16(dz[mt][gt][i], 0.f) & 0xffffu);
                     }
                     if constexpr (MODE == STEP_DW) {
                         // dW_k += dZ_chunk^T H_chunk; A = dZ^T (label r16, rows 8q + e),
@@ -412,6 +458,10 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                             }
                         }
                     }
+                }
+                if constexpr (STORE_Z || STORE_DZ) {
+                    pend_zk = k;
+                    pend_zc = c;
                 }
                 wave_sync();
             }
@@ -436,27 +486,42 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         }
 
         if constexpr (DW) {
-            // result lane (slot 16t + r16, q) holds labels 16gt + 4q + i; through
-            // LDS per 16-label tile so the stores are contiguous 16-byte pieces
-            float* so = sO[wv];
-            constexpr int NP = (4 * F + 63) / 64;
+            // result lane (slot 16t + r16, q) holds labels 16gt + 4q + i; staged in
+            // LDS so the stores are contiguous 16-byte pieces
+            float* so = sWo[wv];
+            if constexpr (DEFER_DW) {
 #pragma unroll
-            for (int gt = 0; gt < GT; ++gt) {
+                for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
+                    for (int t = 0; t < NT; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        so[(4 * q + i) * WST + 16 * t + r16] = dw[gt][t][i];
-                wave_sync();
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) {
-                    const int u = lane + 64 * pp;
-                    const int g = u / (F / 4), cc = u % (F / 4);
-                    if (u < 4 * F)
-                        *reinterpret_cast<f32x4_t*>(a.dW + (k * G + 16 * gt + g) * F + 4 * cc) =
-                            *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                        for (int i = 0; i < 4; ++i)
+                            so[(16 * gt + 4 * q + i) * WST + 16 * t + r16] = dw[gt][t][i];
+                pend_dw = k;
+            } else {
+                if constexpr (ALIAS_WZ) {
+                    wave_sync();
+                    flush_z();
                 }
-                wave_sync();
+                constexpr int NP = (4 * F + 63) / 64;
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            so[(4 * q + i) * WST + 16 * t + r16] = dw[gt][t][i];
+                    wave_sync();
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) {
+                        const int u = lane + 64 * pp;
+                        const int g = u / (F / 4), cc = u % (F / 4);
+                        if (u < 4 * F)
+                            *reinterpret_cast<f32x4_t*>(a.dW + (k * G + 16 * gt + g) * F + 4 * cc) =
+                                *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                    }
+                    wave_sync();
+                }
             }
         }
 #pragma unroll
@@ -464,6 +529,9 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             col[t] = col_n[t];
         rows_of(col, gp);
     }
+    wave_sync();
+    flush_z();
+    flush_dw();
 
     if constexpr (LOSS) {
         const float tot = wave_sum(lsum);
