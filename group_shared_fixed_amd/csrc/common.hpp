@@ -80,6 +80,17 @@ __device__ __forceinline__ u32x4_t ldg16(const void* p)
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// 16-byte store of a streamed output (written once, not read again soon):
+// non-temporal, so it does not displace cached inputs.
+__device__ __forceinline__ void stg_stream(float* p, f32x4_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void stg_stream(uint16_t* p, u32x4_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

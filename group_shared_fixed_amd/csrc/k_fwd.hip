@@ -30,6 +30,8 @@
 // Each chunk therefore first waits for its own rows, then issues the stores
 // deferred from the previous chunk or group (staged in LDS), then the loads
 // of the next chunk and, once per group, the next group's weights.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -167,9 +169,14 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 for (int pp = 0; pp < NP; ++pp) {
                     const int u = lane + 64 * pp;
                     const int g = u / (F / 4), cc = u % (F / 4);
-                    if (u < G * F / 4)
-                        *reinterpret_cast<f32x4_t*>(a.dW + (pend_dw * G + g) * F + 4 * cc) =
-                            *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                    if (u < G * F / 4) {
+                        float* dst = a.dW + (pend_dw * G + g) * F + 4 * cc;
+                        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                        // the fused step's dh kernel runs next and gains from
+                        // the cached lines; the standalone call streams
+                        if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(dst) = v;
+                        else stg_stream(dst, v);
+                    }
                 }
                 pend_dw = -1;
             }
@@ -188,8 +195,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         const int lr = u / (G / 4), cc = u % (G / 4);
                         const int64_t b = 32 * pend_zc + lr;
                         if (u < 8 * G && b < a.B)
-                            *reinterpret_cast<f32x4_t*>(a.Z + b * L + pend_zk * G + 4 * cc) =
-                                *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc);
+                            stg_stream(a.Z + b * L + pend_zk * G + 4 * cc,
+                                       *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc));
                     }
                 }
                 if constexpr (STORE_DZ) {
@@ -202,8 +209,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         const int lr = u / (G / 8), cc = u % (G / 8);
                         const int64_t b = 32 * pend_zc + lr;
                         if (u < 4 * G && b < a.B)
-                            *reinterpret_cast<u32x4_t*>(a.dZ + b * L + pend_zk * G + 8 * cc) =
-                                *reinterpret_cast<const u32x4_t*>(so + lr * DZST + 8 * cc);
+                            stg_stream(a.dZ + b * L + pend_zk * G + 8 * cc,
+                                       *reinterpret_cast<const u32x4_t*>(so + lr * DZST + 8 * cc));
                     }
                 }
                 pend_zk = -1;
@@ -284,8 +291,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
 
         // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W); the
         // next chunk's inputs go to hn / dn
-        auto chunk = [&](int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT], u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1],
-                         u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1]) {
+        auto chunk = [&](auto first, int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT],
+                         u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1], u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1]) {
             // 1. this chunk's rows into the wave's LDS tile [slot][32 batch rows]
             //    (the wait for the chunk's loads)
 #pragma unroll
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             }
             // 2. stores deferred from the previous chunk / group
             flush_z();
-            if (c == 0) flush_dw();
+            if constexpr (decltype(first)::value) flush_dw();
             // 3. requests: the next chunk (or the next group's first chunk), and
             //    once per group the next group's weights and index entries
             if (c + 1 < nchunk) {
@@ -467,14 +474,21 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             }
         };
 
-        // chunks in pairs so the register buffers alternate without copies
-        int c = 0;
+        // Chunk 0 (which issues the deferred dW stores) is peeled off, so the
+        // chunk loop holds no stores and its waits stay exact; the rest run in
+        // pairs so the register buffers alternate without copies.
+        const std::true_type first;
+        const std::false_type later;
+        chunk(first, 0, hA, hB, dA, dB);
+        int c = 1;
         for (; c + 1 < nchunk; c += 2) {
-            chunk(c, hA, hB, dA, dB);
-            chunk(c + 1, hB, hA, dB, dA);
+            chunk(later, c, hB, hA, dB, dA);
+            chunk(later, c + 1, hA, hB, dA, dB);
         }
         if (c < nchunk) {
-            chunk(c, hA, hB, dA, dB);
+            chunk(later, c, hB, hA, dB, dA);
+        } else {
+            // odd chunk count: the next group's first rows landed in the B set
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 hA[t] = hB[t];
@@ -516,9 +530,12 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     for (int pp = 0; pp < NP; ++pp) {
                         const int u = lane + 64 * pp;
                         const int g = u / (F / 4), cc = u % (F / 4);
-                        if (u < 4 * F)
-                            *reinterpret_cast<f32x4_t*>(a.dW + (k * G + 16 * gt + g) * F + 4 * cc) =
-                                *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                        if (u < 4 * F) {
+                            float* dst = a.dW + (k * G + 16 * gt + g) * F + 4 * cc;
+                            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
+                            if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(dst) = v;
+                            else stg_stream(dst, v);
+                        }
                     }
                     wave_sync();
                 }
