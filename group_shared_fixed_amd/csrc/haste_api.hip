@@ -164,8 +164,7 @@ int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, 
     const Layout l = layout(HASTE_OP_FWD_BCE, B, H, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
-    launch_transpose_h(h, hT, B, H, l.Bp, stream);
-    if (loss) launch_fill_f64(loss, 1, stream);
+    launch_transpose_h(h, hT, B, H, l.Bp, stream, nullptr, 0, loss);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;
     a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dZ = dZ; a.loss = loss;
@@ -196,9 +195,7 @@ int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
         if (events) (void)hipEventRecord(events[i], stream);
     };
     mark(0);
-    launch_transpose_h(h, hT, B, H, l.Bp, stream);
-    if (loss) launch_fill_f64(loss, 1, stream);
-    if (!det) launch_fill_f32(dh, B * H, stream);
+    launch_transpose_h(h, hT, B, H, l.Bp, stream, det ? nullptr : dh, B * H, loss);
     mark(1);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;

@@ -5,21 +5,52 @@
 namespace haste {
 
 // hT[j, b] = h[b, j] for b < B, 0 for B <= b < Bp (64 x 64 tiles via LDS).
+// Also clears the optional outputs zf[0, nzf) and *zd that later kernels of
+// the same call accumulate into (saves separate launches).
 __global__ __launch_bounds__(256) void k_transpose_h(const uint16_t* __restrict__ h, uint16_t* __restrict__ hT,
-                                                     int64_t B, int64_t H, int64_t Bp)
+                                                     int64_t B, int64_t H, int64_t Bp, float* __restrict__ zf,
+                                                     int64_t nzf, double* __restrict__ zd)
 {
-    __shared__ uint16_t t[64][66];
-    const int64_t j0 = (int64_t)blockIdx.x * 64, b0 = (int64_t)blockIdx.y * 64;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int r = i >> 6, c = i & 63;
-        const int64_t b = b0 + r, j = j0 + c;
-        t[r][c] = (b < B && j < H) ? h[b * H + j] : (uint16_t)0;
+    {
+        const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * 256;
+        const int64_t tid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+        for (int64_t i = tid; i < nzf; i += nthreads)
+            zf[i] = 0.f;
+        if (zd && tid == 0) *zd = 0.0;
+    }
+    // tile of 32 batch rows x 64 features; each thread moves one 16-byte
+    // piece in (row b, features j .. j+8) and one out (feature j, rows b .. b+8)
+    __shared__ uint16_t t[64][32 + 2];
+    const int64_t j0 = (int64_t)blockIdx.x * 64, b0 = (int64_t)blockIdx.y * 32;
+    {
+        const int r = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
+        const int64_t b = b0 + r, j = j0 + c8;
+        uint16_t v[8];
+        if (b < B && j + 8 <= H && (H & 7) == 0) {
+            const uint4 x = *reinterpret_cast<const uint4*>(h + b * H + j);
+            v[0] = x.x & 0xffff; v[1] = x.x >> 16; v[2] = x.y & 0xffff; v[3] = x.y >> 16;
+            v[4] = x.z & 0xffff; v[5] = x.z >> 16; v[6] = x.w & 0xffff; v[7] = x.w >> 16;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (b < B && j + e < H) ? h[b * H + j + e] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            t[c8 + e][r] = v[e];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int r = i >> 6, c = i & 63;
-        const int64_t j = j0 + r, b = b0 + c;
-        if (j < H && b < Bp) hT[j * Bp + b] = t[c][r];
+    {
+        const int jl = threadIdx.x >> 2, bc = (threadIdx.x & 3) * 8;
+        const int64_t j = j0 + jl, b = b0 + bc;
+        if (j < H && b < Bp) {
+            uint4 x;
+            x.x = t[jl][bc + 0] | ((uint32_t)t[jl][bc + 1] << 16);
+            x.y = t[jl][bc + 2] | ((uint32_t)t[jl][bc + 3] << 16);
+            x.z = t[jl][bc + 4] | ((uint32_t)t[jl][bc + 5] << 16);
+            x.w = t[jl][bc + 6] | ((uint32_t)t[jl][bc + 7] << 16);
+            *reinterpret_cast<uint4*>(hT + j * Bp + b) = x;
+        }
     }
 }
 
@@ -72,10 +103,12 @@ static unsigned fill_grid(int64_t n)
     return (unsigned)(g < 1 ? 1 : (g > 4096 ? 4096 : g));
 }
 
-void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s)
+void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s,
+                        float* zero_f, int64_t n_zero_f, double* zero_d)
 {
-    const dim3 grid((unsigned)((H + 63) / 64), (unsigned)((Bp + 63) / 64));
-    hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, h, hT, B, H, Bp);
+    const dim3 grid((unsigned)((H + 63) / 64), (unsigned)(Bp / 32));   // Bp is a multiple of 32
+    hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, h, hT, B, H, Bp, zero_f, zero_f ? n_zero_f : 0,
+                       zero_d);
 }
 
 void launch_fill_f32(float* p, int64_t n, hipStream_t s)

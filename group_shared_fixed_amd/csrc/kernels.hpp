@@ -71,7 +71,9 @@ void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nc
 bool launch_fixed_fwd(int F, const FixedArgs& a, int grid, hipStream_t s);
 bool launch_fixed_bwd_w(int F, const FixedArgs& a, int grid, hipStream_t s);
 bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s);
-void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s);
+// h (B x H) -> hT (H x Bp, zero padded); optionally clears zero_f[0, n) and *zero_d
+void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s,
+                        float* zero_f = nullptr, int64_t n_zero_f = 0, double* zero_d = nullptr);
 void launch_fill_f32(float* p, int64_t n, hipStream_t s);
 void launch_fill_f64(double* p, int64_t n, hipStream_t s);
 void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
