@@ -22,6 +22,7 @@ struct Layout {
     size_t hT_bytes;     // H x Bp bf16
     size_t part_bytes;   // deterministic dh partials
     int nchunks, ntiles; // dh split: label chunks x batch tiles
+    int rows;            // batch rows per dh tile
     size_t total;
 };
 
@@ -33,16 +34,21 @@ bool op_needs_hT(int op)
 
 bool op_has_dh(int op) { return op == HASTE_OP_BWD_H || op == HASTE_OP_STEP || op == HASTE_OP_FIXED_BWD_H; }
 
-Layout layout(int op, int64_t B, int64_t H, int dh_mode)
+Layout layout(int op, int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
 {
     Layout l{};
     l.Bp = round_up(B, 32);
-    l.ntiles = (int)((B + kDhRows - 1) / kDhRows);
-    int nc = (512 / l.ntiles) / 8 * 8;
+    // grouped dh kernels pick their tile height by shape; the G = 1 baseline uses 16 rows.
+    // About two workgroups per CU for 16-row tiles, one for 32-row tiles; the
+    // chunk count is a multiple of the 8 XCDs.
+    l.rows = (op == HASTE_OP_BWD_H || op == HASTE_OP_STEP) ? dh_tile_rows((int)G, (int)F, H) : kDhRows;
+    l.ntiles = (int)((B + l.rows - 1) / l.rows);
+    const int target = l.rows == 32 ? 256 : 512;
+    int nc = (target / l.ntiles) / 8 * 8;
     l.nchunks = nc < 8 ? 8 : nc;
     l.hT_bytes = op_needs_hT(op) ? align256((size_t)H * (size_t)l.Bp * 2) : 0;
     l.part_bytes = (op_has_dh(op) && dh_mode == HASTE_DH_DETERMINISTIC)
-                       ? align256((size_t)l.nchunks * l.ntiles * kDhRows * (size_t)H * 4)
+                       ? align256((size_t)l.nchunks * l.ntiles * l.rows * (size_t)H * 4)
                        : 0;
     l.total = l.hT_bytes + l.part_bytes;
     return l;
@@ -91,10 +97,9 @@ extern "C" {
 size_t haste_workspace_size(int op, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode)
 {
     (void)K;
-    (void)G;
     (void)F;
     if (op < HASTE_OP_FWD || op > HASTE_OP_FIXED_BWD_H || B < 1 || H < 1) return 0;
-    return layout(op, B, H, dh_mode).total;
+    return layout(op, B, H, G, F, dh_mode).total;
 }
 
 int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, float* Z, int64_t B, int64_t H,
@@ -103,7 +108,7 @@ int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, floa
     if (!h || !idx || !W || !Z) return HASTE_ERR_NULL;
     HASTE_TRY(check_shape(B, H, K, G, F, false));
     if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_FWD, B, H, 0);
+    const Layout l = layout(HASTE_OP_FWD, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
@@ -119,7 +124,7 @@ int haste_bwd_w(const haste_bf16* h, const int32_t* idx, const haste_bf16* dZ, f
     if (!h || !idx || !dZ || !dW) return HASTE_ERR_NULL;
     HASTE_TRY(check_shape(B, H, K, G, F, false));
     if (!aligned16(h) || !aligned16(idx) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_BWD_W, B, H, 0);
+    const Layout l = layout(HASTE_OP_BWD_W, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
@@ -138,7 +143,7 @@ int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, f
     HASTE_TRY(check_shape(B, H, K, G, F, false));
     if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
     if (!aligned16(dZ) || !aligned16(idx) || !aligned16(W) || !aligned16(dh)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_BWD_H, B, H, dh_mode);
+    const Layout l = layout(HASTE_OP_BWD_H, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
     DhArgs a{};
@@ -146,7 +151,7 @@ int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, f
     a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
     if (!det) launch_fill_f32(dh, B * H, stream);
     if (!launch_dh((int)G, (int)F, DH_FROM_DZ, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
-    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
     return hip_status();
 }
 
@@ -161,7 +166,7 @@ int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, 
     if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) ||
         !aligned16(dZ) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
         return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_FWD_BCE, B, H, 0);
+    const Layout l = layout(HASTE_OP_FWD_BCE, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream, nullptr, 0, loss);
@@ -186,7 +191,7 @@ int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
     if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) ||
         !aligned16(dW) || !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
         return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_STEP, B, H, dh_mode);
+    const Layout l = layout(HASTE_OP_STEP, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
     uint16_t* hT = (uint16_t*)workspace;
@@ -209,7 +214,7 @@ int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
     d.nchunks = l.nchunks; d.ntiles = l.ntiles; d.dh = dh; d.part = part;
     if (!launch_dh((int)G, (int)F, DH_FROM_LABELS, det, d, stream)) return HASTE_ERR_UNSUPPORTED;
     mark(3);
-    if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
     mark(4);
     return hip_status();
 }
@@ -229,7 +234,7 @@ int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* 
     if (!h || !idx1 || !W || !Z) return HASTE_ERR_NULL;
     HASTE_TRY(check_shape(B, H, L, 1, F, true));
     if (!aligned16(h) || !aligned16(idx1) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_FIXED_FWD, B, H, 0);
+    const Layout l = layout(HASTE_OP_FIXED_FWD, B, H, 1, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
@@ -245,7 +250,7 @@ int haste_fixed_bwd_w(const haste_bf16* h, const int32_t* idx1, const haste_bf16
     if (!h || !idx1 || !dZ || !dW) return HASTE_ERR_NULL;
     HASTE_TRY(check_shape(B, H, L, 1, F, true));
     if (!aligned16(h) || !aligned16(idx1) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_FIXED_BWD_W, B, H, 0);
+    const Layout l = layout(HASTE_OP_FIXED_BWD_W, B, H, 1, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
@@ -263,7 +268,7 @@ int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf1
     HASTE_TRY(check_shape(B, H, L, 1, F, true));
     if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
     if (!aligned16(dZ) || !aligned16(idx1) || !aligned16(W) || !aligned16(dh)) return HASTE_ERR_ALIGN;
-    const Layout l = layout(HASTE_OP_FIXED_BWD_H, B, H, dh_mode);
+    const Layout l = layout(HASTE_OP_FIXED_BWD_H, B, H, 1, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
     FixedArgs a{};
@@ -271,7 +276,7 @@ int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf1
     a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
     if (!det) launch_fill_f32(dh, B * H, stream);
     if (!launch_fixed_bwd_h((int)F, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
-    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * kDhRows, stream);
+    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
     return hip_status();
 }
 

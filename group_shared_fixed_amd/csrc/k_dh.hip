@@ -398,6 +398,359 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     }
 }
 
+// Offset (floats) of (batch row r < 32, column j) in the 32-row accumulator:
+// 32 floats per column, 4-row quads XORed with (j / 2) % 8 so the 16-byte
+// read-add-writes of one instruction (random columns) use all bank groups.
+__device__ __forceinline__ int acc32_off(int j, int r)
+{
+    return j * 32 + ((((r >> 2) ^ (j >> 1)) & 7) << 2) + (r & 3);
+}
+
+// Variant with 32 batch rows per workgroup and eight waves: each wave runs
+// a group for both 16-row matrix-core tiles, so the W_k staging, its
+// transposed operand reads, the index loads and the accumulator addressing
+// serve twice the rows.  One workgroup per CU (accumulator 32 x H fp32 plus
+// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768.
+template <int G, int F, int SRC, bool DET>
+__global__ __launch_bounds__(512, 1) void k_group_dh32(DhArgs a)
+{
+    constexpr int NT = F / 16;          // output slot tiles of P
+    constexpr int KSF = F / 32;         // contraction steps of Z^T = W H^T
+    constexpr int GT = G / 16;          // label tiles
+    constexpr int KSG = (G + 31) / 32;  // contraction steps of P = dZ W
+    constexpr int R = 32;
+    constexpr int NWV = 8;              // waves per workgroup
+    constexpr bool LAB = (SRC == DH_FROM_LABELS);
+    constexpr int NWP = (G * F / 8 + 63) / 64;   // 16-byte pieces of W_k per lane
+    constexpr int NHH = F / 32;                  // gathered 16-byte pieces per lane per 16-row half
+    constexpr int DCH = G / 8;                   // 16-byte chunks of a dZ row
+    constexpr int NDH = (16 * DCH + 63) / 64;    // dZ pieces per lane per 16-row half
+    static_assert(G * F <= 2048 && F <= 64, "per-wave tiles sized for eight waves");
+
+    extern __shared__ __attribute__((aligned(16))) float acc[];   // acc[j * 32 + row], quads swizzled
+    __shared__ __attribute__((aligned(16))) uint16_t sW[NWV][G * F];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[NWV][LAB ? F * 16 : 16 * G];   // one 16-row half
+    __shared__ int sTurn[2];                  // accumulator hand-off counters, one per 16-row half
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int r16 = lane & 15;
+    const int q = lane >> 4;
+    const int tr_r = r16 >> 2, tr_c = r16 & 3;   // transposing-read source position
+
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int tile = slot % a.ntiles;
+    const int chunk = (slot / a.ntiles) * 8 + xcd;
+    const int64_t kc0 = (int64_t)chunk * a.K / a.nchunks;
+    const int64_t kc1 = (int64_t)(chunk + 1) * a.K / a.nchunks;
+    const int64_t b0 = (int64_t)tile * R;
+    const int64_t L = a.K * G;
+    const int64_t H = a.H;
+
+    for (int64_t i = threadIdx.x; i < R * H; i += 512)
+        acc[i] = 0.f;
+    if (threadIdx.x < 2) sTurn[threadIdx.x] = 0;
+
+    // each lane's A rows: b0 + r16 (tile 0) and b0 + 16 + r16 (tile 1)
+    LabelCursor cur[2];
+    if constexpr (LAB) {
+        cur[0].init(a.y_rowptr, a.y_col, b0 + r16, a.B, kc0 * G);
+        cur[1].init(a.y_rowptr, a.y_col, b0 + 16 + r16, a.B, kc0 * G);
+    }
+    const float scale = a.scale;
+    const float inv_s = 1.0f / a.scale;
+    const bool tile_full = b0 + R <= a.B;
+
+    uint16_t* wt = sW[wv];
+    uint16_t* tt = sT[wv];
+
+    // Inputs of one round as loaded from global memory.
+    struct In {
+        u32x4_t w[NWP];                  // W_k (G x F, contiguous) as 16-byte pieces lane + 64 p
+        u32x4_t h[LAB ? 2 : 1][NHH];     // gathered pieces, per 16-row half
+        u32x4_t d[LAB ? 1 : 2][NDH];     // dZ tile pieces, per 16-row half
+        int col[NT];                     // accumulator columns I_k[16t + r16]
+    };
+    // W_k as contiguous 16-byte pieces (four consecutive lanes read 64 bytes)
+    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
+#pragma unroll
+        for (int p = 0; p < NWP; ++p)
+            if (lane + 64 * p < G * F / 8) wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+    };
+    auto load_col = [&](int64_t kk, int (&cl)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            cl[t] = a.idx[kk * F + 16 * t + r16];
+    };
+    // gathered half tile: piece lane + 64 u is slot lane/2 + 32 u, batch rows
+    // b0 + 16 hf + 8 (lane % 2) .. +8
+    auto load_gcol = [&](int64_t kk, int (&gc)[NHH]) {
+#pragma unroll
+        for (int u = 0; u < NHH; ++u)
+            gc[u] = a.idx[kk * F + (lane >> 1) + 32 * u];
+    };
+    auto gather = [&](const int (&gc)[NHH], u32x4_t (&hv)[2][NHH]) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int u = 0; u < NHH; ++u)
+                hv[hf][u] = ldg16(a.hT + ((uint32_t)gc[u] * (uint32_t)a.Bp +
+                                          (uint32_t)(b0 + 16 * hf + 8 * (lane & 1))));
+    };
+    // dZ half tile: piece pc = lane + 64 u is batch row b0 + 16 hf + pc / DCH, labels 8 (pc % DCH) ..
+    auto load_dz = [&](int64_t kk, u32x4_t (&dv)[2][NDH]) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int u = 0; u < NDH; ++u) {
+                const int pc = lane + 64 * u;
+                const int64_t b = b0 + 16 * hf + pc / DCH;
+                dv[hf][u] = u32x4_t{0u, 0u, 0u, 0u};
+                if (pc < 16 * DCH && b < a.B) dv[hf][u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
+            }
+    };
+
+    const int64_t ng = kc1 - kc0;
+    const int64_t nrounds = (ng + NWV - 1) / NWV;
+    auto group_of = [&](int64_t rd) {
+        const int64_t kk = kc0 + NWV * rd + wv;
+        return kk < kc1 ? kk : kc1 - 1;       // idle waves reload a valid group
+    };
+
+    // Software pipeline as in the 16-row kernel: round rd consumes inputs
+    // issued in round rd - 1 and issues the gather for round rd + 1 (its
+    // index entries arrived during round rd - 1), the gather indices for
+    // round rd + 2 and the columns and weights for round rd + 1.
+    In sa, sb;
+    int gcn[LAB ? NHH : 1];
+    if (ng > 0) {
+        const int64_t kk = group_of(0);
+        if constexpr (LAB) {
+            load_gcol(kk, gcn);
+            gather(gcn, sa.h);
+            load_gcol(group_of(1), gcn);
+        } else {
+            load_dz(kk, sa.d);
+        }
+        load_col(kk, sa.col);
+        load_w(kk, sa.w);
+    }
+
+    __syncthreads();
+
+    // One round: this wave's group k = kc0 + 8 rd + wv, up to P for both tiles.
+    auto round = [&](int64_t rd, const In& c, In& n, f32x4_t (&p)[2][NT]) {
+        const int64_t k = kc0 + NWV * rd + wv;
+        const bool active = k < kc1;
+        const int64_t kn = group_of(rd + 1);
+        if constexpr (LAB) {
+            gather(gcn, n.h);
+            load_gcol(group_of(rd + 2), gcn);
+        } else {
+            load_dz(kn, n.d);
+        }
+        load_col(kn, n.col);
+        load_w(kn, n.w);
+        if (!active) return;
+
+        // W_k rows into LDS (the contraction over labels reads them transposed)
+#pragma unroll
+        for (int pp = 0; pp < NWP; ++pp) {
+            const int u = lane + 64 * pp;
+            if (u < G * F / 8)
+                *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = c.w[pp];
+        }
+        u32x4_t ahi[2][KSG], alo[2][KSG];
+        if constexpr (!LAB) {
+            // A of P = given dZ rows, one 16-row half at a time through the tile
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int u = 0; u < NDH; ++u) {
+                    const int pc = lane + 64 * u;
+                    if (pc < 16 * DCH)
+                        *reinterpret_cast<u32x4_t*>(tt + dz_off<G>(pc / DCH, pc % DCH)) = c.d[hf][u];
+                }
+                wave_sync();
+#pragma unroll
+                for (int s = 0; s < KSG; ++s) {
+                    const int cc = 4 * s + q;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tt + dz_off<G>(r16, cc < DCH ? cc : 0));
+                    ahi[hf][s] = cc < DCH ? v : u32x4_t{0u, 0u, 0u, 0u};
+                    alo[hf][s] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+                wave_sync();
+            }
+        } else {
+            // B of Z^T = H^T read transposed, per 16-row half: lane (row r16, q)
+            // gets slots 32s + 8q + e
+            u32x4_t bz[2][KSF];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int u = 0; u < NHH; ++u)
+                    *reinterpret_cast<u32x4_t*>(tt + ht_off((lane >> 1) + 32 * u, 8 * (lane & 1))) = c.h[hf][u];
+                wave_sync();
+#pragma unroll
+                for (int s = 0; s < KSF; ++s) {
+                    const int f0 = 32 * s + 8 * q + tr_r;
+                    bz[hf][s] = cat(lds_tr16(tt + ht_off(f0, 4 * tr_c)), lds_tr16(tt + ht_off(f0 + 4, 4 * tr_c)));
+                }
+                wave_sync();
+            }
+            // Z^T = W_k H^T for both tiles; A = W_k rows (lane (label 16gt + r16, q):
+            // slots 32s + 8q ..).  Result lane (row r16, q) holds labels 16gt + 4q + i.
+            f32x4_t zt[2][GT];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt)
+                    zt[hf][gt] = zero4();
+#pragma unroll
+            for (int s = 0; s < KSF; ++s)
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt) {
+                    const u32x4_t wa =
+                        *reinterpret_cast<const u32x4_t*>(wt + wt_off<F>(16 * gt + r16, 32 * s + 8 * q));
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        zt[hf][gt] = mfma16(wa, bz[hf][s], zt[hf][gt]);
+                }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                // labels of this row for this group
+                const uint64_t mrow = cur[hf].take(k * G, G, a.y_col);
+                const bool brow_ok = b0 + 16 * hf + r16 < a.B;
+                float dz[GT][4];
+                // s * sigmoid(z) = 1 / ((1 + e^-z) / s); e^-z = +inf gives 0
+#pragma unroll
+                for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float t = __builtin_amdgcn_exp2f(-zt[hf][gt][i] * kLog2e);
+                        dz[gt][i] = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
+                    }
+                if (__any(mrow != 0) || !tile_full) {   // rare: positives or padding rows
+#pragma unroll
+                    for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float d = dz[gt][i];
+                            if ((mrow >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
+                            dz[gt][i] = brow_ok ? d : 0.f;
+                        }
+                }
+                // contraction element e of step s <-> label 32s + 16*(e/4) + 4q + e%4
+#pragma unroll
+                for (int s = 0; s < KSG; ++s) {
+                    const int g0 = 2 * s, g1 = 2 * s + 1;
+                    const float x0 = dz[g0][0], x1 = dz[g0][1], x2 = dz[g0][2], x3 = dz[g0][3];
+                    const float y0 = g1 < GT ? dz[g1 < GT ? g1 : 0][0] : 0.f;
+                    const float y1 = g1 < GT ? dz[g1 < GT ? g1 : 0][1] : 0.f;
+                    const float y2 = g1 < GT ? dz[g1 < GT ? g1 : 0][2] : 0.f;
+                    const float y3 = g1 < GT ? dz[g1 < GT ? g1 : 0][3] : 0.f;
+                    { const u32x2_t _p = split_pair(x0, x1); ahi[hf][s][0] = _p[0]; alo[hf][s][0] = _p[1]; }
+                    { const u32x2_t _p = split_pair(x2, x3); ahi[hf][s][1] = _p[0]; alo[hf][s][1] = _p[1]; }
+                    { const u32x2_t _p = split_pair(y0, y1); ahi[hf][s][2] = _p[0]; alo[hf][s][2] = _p[1]; }
+                    { const u32x2_t _p = split_pair(y2, y3); ahi[hf][s][3] = _p[0]; alo[hf][s][3] = _p[1]; }
+                }
+            }
+        }
+        // P = dZ_tile W_k with B = W_k read transposed (shared by both tiles):
+        // lane (slot 16t + r16, q) gets the labels of contraction elements e.
+        // Result lane (slot 16t + r16, q) holds batch rows 16 hf + 4q + i.
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int fc = 16 * t + 4 * tr_c;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                p[hf][t] = zero4();
+#pragma unroll
+            for (int s = 0; s < KSG; ++s) {
+                // Transposing reads run with the whole wave active (under a
+                // partial EXEC mask they overwrite the inactive lanes'
+                // registers); rows past G read a valid row and are zeroed.
+                u32x2_t lo2, hi2;
+                const u32x2_t z2 = u32x2_t{0u, 0u};
+                if constexpr (!LAB) {
+                    const int g = 32 * s + 8 * q;          // elements e <-> g + e
+                    const bool ok = g < G;
+                    const int gr = ok ? g : 0;
+                    lo2 = lds_tr16(wt + wt_off<F>(gr + tr_r, fc));
+                    hi2 = lds_tr16(wt + wt_off<F>(gr + 4 + tr_r, fc));
+                    lo2 = ok ? lo2 : z2;
+                    hi2 = ok ? hi2 : z2;
+                } else {
+                    const int ga = 32 * s + 4 * q;         // e < 4 <-> ga + e
+                    const int gb = ga + 16;                // e >= 4 <-> gb + e - 4
+                    lo2 = lds_tr16(wt + wt_off<F>(ga + tr_r, fc));
+                    if constexpr (G > 16) hi2 = lds_tr16(wt + wt_off<F>(gb + tr_r, fc));
+                    else hi2 = z2;
+                }
+                const u32x4_t bv = cat(lo2, hi2);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    p[hf][t] = mfma16(ahi[hf][s], bv, p[hf][t]);
+                    if constexpr (LAB)
+                        p[hf][t] = mfma16(alo[hf][s], bv, p[hf][t]);
+                }
+            }
+        }
+    };
+
+    // Scatter-add P into the accumulator columns I_k with 16-byte
+    // read-add-writes (rows 16 hf + 4q .. +3 of column col[t] are adjacent).
+    // Inside one wave the index set is duplicate-free, so no two lanes touch
+    // the same cell.  Each 16-row half of the accumulator has its own turn
+    // counter; waves take turns on a half in the fixed order (pair of rounds,
+    // wave), two groups per turn, so one wave can update one half while the
+    // next updates the other.
+    auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&col)[NT]) {
+        f32x4_t v[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q)) = v[t] + p[hf][t];
+    };
+    const int64_t npairs = (nrounds + 1) / 2;
+    for (int64_t i = 0; i < npairs; ++i) {
+        const int64_t rd = 2 * i;
+        f32x4_t pa[2][NT], pb[2][NT];
+        int ca[NT];
+        round(rd, sa, sb, pa);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            ca[t] = sa.col[t];
+        const bool second = rd + 1 < nrounds;
+        if (second) round(rd + 1, sb, sa, pb);
+        const bool act_a = kc0 + NWV * rd + wv < kc1;
+        const bool act_b = second && kc0 + NWV * (rd + 1) + wv < kc1;
+        const int turn = (int)(NWV * i) + wv;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            wait_turn(&sTurn[hf], turn);
+            if (act_a) rmw(hf, pa, ca);
+            if (act_b) rmw(hf, pb, sb.col);
+            pass_turn(&sTurn[hf], turn);
+        }
+    }
+    __syncthreads();
+
+    if constexpr (DET) {
+        float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
+        for (int64_t i = threadIdx.x; i < R * H; i += 512)
+            dst[i] = acc[acc32_off((int)(i % H), (int)(i / H))];
+    } else {
+        for (int64_t i = threadIdx.x; i < R * H; i += 512) {
+            const int64_t b = b0 + i / H;
+            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc32_off((int)(i % H), (int)(i / H))]);
+        }
+    }
+}
+
 // dh[b, j] = sum over chunks c (in order) of part[c, b, j]
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, float* __restrict__ dh,
                                                    int64_t B, int64_t H, int nchunks, int rows_per_chunk)
@@ -414,8 +767,9 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 template <int G, int F>
 static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
 {
-    const size_t lds = (size_t)kDhRows * a.H * sizeof(float);
-    const dim3 grid(a.nchunks * a.ntiles), blk(256);
+    const int rows = dh_tile_rows((int)G, (int)F, a.H);
+    const size_t lds = (size_t)rows * a.H * sizeof(float);
+    const dim3 grid(a.nchunks * a.ntiles), blk(rows == 32 ? 512 : 256);
     auto go = [&](auto kern) {
         static bool attr = false;
         if (!attr) {
@@ -424,6 +778,17 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
         }
         hipLaunchKernelGGL(kern, grid, blk, lds, s, a);
     };
+    if constexpr (G * F <= 2048 && F <= 64) {
+        if (rows == 32) {
+            if (src == DH_FROM_DZ) {
+                if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true>); else go(k_group_dh32<G, F, DH_FROM_DZ, false>);
+            } else {
+                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true>);
+                else go(k_group_dh32<G, F, DH_FROM_LABELS, false>);
+            }
+            return true;
+        }
+    }
     if (src == DH_FROM_DZ) {
         if (det) go(k_group_dh<G, F, DH_FROM_DZ, true>); else go(k_group_dh<G, F, DH_FROM_DZ, false>);
     } else {

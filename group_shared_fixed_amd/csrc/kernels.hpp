@@ -65,6 +65,12 @@ struct FixedArgs {
 
 // Each launcher returns false when no kernel exists for (G, F).
 bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s);
+// Batch rows per feature-gradient workgroup: 32 (eight waves, one workgroup
+// per CU) when the per-wave tiles and a 32 x H accumulator fit in LDS, else 16.
+inline int dh_tile_rows(int G, int F, int64_t H)
+{
+    return (G * F <= 2048 && F <= 64 && H <= 768) ? 32 : kDhRows;
+}
 bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s);
 void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
                       hipStream_t s);
