@@ -398,6 +398,13 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     }
 }
 
+// Waves per 32-row workgroup when dZ is given: twelve when their tiles fit
+// next to the largest accumulator (32 x 768 fp32), else eight.
+constexpr int dh32_waves_dz(int G, int F)
+{
+    return (2 * G * F + 32 * G) * 12 + 32 * 768 * 4 + 64 <= 160 * 1024 ? 12 : 8;
+}
+
 // Offset (floats) of (batch row r < 32, column j) in the 32-row accumulator:
 // 32 floats per column, 4-row quads XORed with (j / 2) % 8 so the 16-byte
 // read-add-writes of one instruction (random columns) use all bank groups.
@@ -406,20 +413,22 @@ __device__ __forceinline__ int acc32_off(int j, int r)
     return j * 32 + ((((r >> 2) ^ (j >> 1)) & 7) << 2) + (r & 3);
 }
 
-// Variant with 32 batch rows per workgroup and eight waves: each wave runs
-// a group for both 16-row matrix-core tiles, so the W_k staging, its
+// Variant with 32 batch rows per workgroup and NWV waves: each wave runs a
+// group for both 16-row matrix-core tiles, so the W_k staging, its
 // transposed operand reads, the index loads and the accumulator addressing
 // serve twice the rows.  One workgroup per CU (accumulator 32 x H fp32 plus
-// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768.
-template <int G, int F, int SRC, bool DET>
-__global__ __launch_bounds__(512, 1) void k_group_dh32(DhArgs a)
+// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768, with eight
+// waves when the logits are recomputed and twelve (three per SIMD, the
+// register budget allows it) when dZ is given.
+template <int G, int F, int SRC, bool DET, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 {
     constexpr int NT = F / 16;          // output slot tiles of P
     constexpr int KSF = F / 32;         // contraction steps of Z^T = W H^T
     constexpr int GT = G / 16;          // label tiles
     constexpr int KSG = (G + 31) / 32;  // contraction steps of P = dZ W
     constexpr int R = 32;
-    constexpr int NWV = 8;              // waves per workgroup
+    constexpr int NT_ = 64 * NWV;       // threads per workgroup
     constexpr bool LAB = (SRC == DH_FROM_LABELS);
     constexpr int NWP = (G * F / 8 + 63) / 64;   // 16-byte pieces of W_k per lane
     constexpr int NHH = F / 32;                  // gathered 16-byte pieces per lane per 16-row half
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(512, 1) void k_group_dh32(DhArgs a)
     const int64_t L = a.K * G;
     const int64_t H = a.H;
 
-    for (int64_t i = threadIdx.x; i < R * H; i += 512)
+    for (int64_t i = threadIdx.x; i < R * H; i += NT_)
         acc[i] = 0.f;
     if (threadIdx.x < 2) sTurn[threadIdx.x] = 0;
 
@@ -741,10 +750,10 @@ __global__ __launch_bounds__(512, 1) void k_group_dh32(DhArgs a)
 
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
-        for (int64_t i = threadIdx.x; i < R * H; i += 512)
+        for (int64_t i = threadIdx.x; i < R * H; i += NT_)
             dst[i] = acc[acc32_off((int)(i % H), (int)(i / H))];
     } else {
-        for (int64_t i = threadIdx.x; i < R * H; i += 512) {
+        for (int64_t i = threadIdx.x; i < R * H; i += NT_) {
             const int64_t b = b0 + i / H;
             if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc32_off((int)(i % H), (int)(i / H))]);
         }
@@ -781,10 +790,22 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
     if constexpr (G * F <= 2048 && F <= 64) {
         if (rows == 32) {
             if (src == DH_FROM_DZ) {
-                if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true>); else go(k_group_dh32<G, F, DH_FROM_DZ, false>);
+                constexpr int NW = dh32_waves_dz(G, F);
+                const dim3 blk12(64 * NW);
+                auto go12 = [&](auto kern) {
+                    static bool attr = false;
+                    if (!attr) {
+                        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  96 * 1024);
+                        attr = true;
+                    }
+                    hipLaunchKernelGGL(kern, grid, blk12, lds, s, a);
+                };
+                if (det) go12(k_group_dh32<G, F, DH_FROM_DZ, true, NW>);
+                else go12(k_group_dh32<G, F, DH_FROM_DZ, false, NW>);
             } else {
-                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true>);
-                else go(k_group_dh32<G, F, DH_FROM_LABELS, false>);
+                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8>);
+                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8>);
             }
             return true;
         }
