@@ -11,7 +11,8 @@ Prints ONE JSON line.  Besides the required fields it carries
   roofline      the kernel with the larger share of the step (forward + BCE +
                 dW, or the feature-gradient kernel) against HBM bandwidth:
                 algorithmic bytes per launch over its average duration, from
-                HIP events recorded around it on its stream; `traffic` is the
+                HIP events recorded around it on its stream (in a second pass
+                of the same steps, so the timed region holds no events); `traffic` is the
                 HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE
                 counters read for it, each scaled by what the same counter
                 reads for a plain copy of known size (taken from the counter
@@ -213,13 +214,83 @@ def cpu_baseline(w, d, seconds):
             "seconds_per_step": round(t_full, 3)}
 
 
+def sweep_g(args):
+    """Per-G kernel times on the tail of the head-tail split (L = 2,910,848
+    tail labels, F = 64, H = 768, B = 128, ~36 positives per sample): the
+    fused step and the unfused calls for G = 16, 32, 64, and the per-label
+    baseline (G = 1).  Same h and W for every G; index sets drawn per G."""
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import get_workload, make_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ev = HipEvents(8)
+    reps = 10
+    out = {"metric": "tail-layer kernel time per G (head-tail split, 3M)", "unit": "us", "n_gpus": 1,
+           "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+           "config": {"workload": "ht3m_tail_shaped", "L": 2910848, "F": 64, "H": 768, "B": 128,
+                      "dh_mode": args.mode}, "per_G": {}}
+    for G in (16, 32, 64, 1):
+        w = get_workload("ht3m_tail_shaped", G=max(G, 16))
+        log(f"[sweep] G={G}: generating")
+        d = make_inputs(w, dZ=True, idx1=(G == 1))
+        B, H, F, L = w.B, w.H, w.F, w.L
+        K = L // max(G, 1)
+        h, W, dZ = bf16_dev(d["h"], dev), bf16_dev(d["W"], dev), bf16_dev(d["dZ"], dev)
+        rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+        Z = torch.empty(B, L, dtype=torch.float32, device=dev)
+        dW = torch.empty(L, F, dtype=torch.float32, device=dev)
+        dh = torch.empty(B, H, dtype=torch.float32, device=dev)
+        r = {}
+        if G == 1:
+            idx1 = i32_dev(d["idx1"], dev)
+            ws = torch.empty(max(256, hs.workspace_size("fixed_bwd_h", B, H, L, 1, F, "det")),
+                             dtype=torch.uint8, device=dev)
+            r["fwd_us"] = 1e3 * time_call(lambda: hs.fixed_fwd(h, idx1, W, Z=Z, workspace=ws), reps, sh, ev)
+            r["bwd_w_us"] = 1e3 * time_call(lambda: hs.fixed_bwd_w(h, idx1, dZ, dW=dW, workspace=ws), reps, sh, ev)
+            r["bwd_h_us"] = 1e3 * time_call(lambda: hs.fixed_bwd_h(dZ, idx1, W, H, mode=args.mode, dh=dh,
+                                                                   workspace=ws), reps, sh, ev)
+        else:
+            idx = i32_dev(d["idx"], dev)
+            ws = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, "det")), dtype=torch.uint8,
+                             device=dev)
+            o = {"dW": dW, "dh": dh, "Z": None, "loss": None}
+            r["step_us"] = 1e3 * time_call(lambda: hs.step(h, idx, W, rp, col, 1.0 / B, G, mode=args.mode, out=o,
+                                                           workspace=ws), reps, sh, ev)
+            r["fwd_us"] = 1e3 * time_call(lambda: hs.fwd(h, idx, W, G, Z=Z, workspace=ws), reps, sh, ev)
+            r["bwd_w_us"] = 1e3 * time_call(lambda: hs.bwd_w(h, idx, dZ, G, dW=dW, workspace=ws), reps, sh, ev)
+            r["bwd_h_us"] = 1e3 * time_call(lambda: hs.bwd_h(dZ, idx, W, G, H, mode=args.mode, dh=dh,
+                                                             workspace=ws), reps, sh, ev)
+            r["step_samples_per_s"] = round(B / (r["step_us"] * 1e-6), 1)
+        out["per_G"][str(G)] = {k: round(v, 2) if isinstance(v, float) else v for k, v in r.items()}
+        log(f"[sweep] G={G}: {out['per_G'][str(G)]}")
+        del Z, dW, dh, d
+        torch.cuda.empty_cache()
+    base = out["per_G"]["1"]
+    for G in ("16", "32", "64"):
+        g = out["per_G"][G]
+        g["speedup_fwd_vs_G1"] = round(base["fwd_us"] / g["fwd_us"], 2)
+        g["speedup_bwd_vs_G1"] = round((base["bwd_w_us"] + base["bwd_h_us"]) / (g["bwd_w_us"] + g["bwd_h_us"]), 2)
+    ev.close()
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="amazon3m_shaped")
-    ap.add_argument("--mode", default="atomic", choices=["atomic", "det"], help="dh reduction")
+    ap.add_argument("--mode", default="det", choices=["atomic", "det"],
+                    help="dh reduction (deterministic is the default: bitwise reproducible and, with the "
+                         "split-K partials written once and summed in order, faster than fp32 atomics)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip unfused calls and the G=1 baseline")
@@ -229,11 +300,17 @@ def main():
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the counter file under profiles/ from the two --counter-run counter CSVs")
     ap.add_argument("--commands", default="", help="with --ingest: the profiling commands, recorded in the file")
+    ap.add_argument("--sweep-g", action="store_true",
+                    help="tail of the head-tail split at 3M (2,910,848 labels): per-G timings for G in "
+                         "{16, 32, 64} and the G = 1 baseline, one JSON line")
     args = ap.parse_args()
 
     if args.ingest:
         ingest_counters(args.ingest[0], args.ingest[1], args.workload, args.commands)
         return
+
+    if args.sweep_g:
+        return sweep_g(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and measured on a single MI355X; "
@@ -285,12 +362,17 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    # timed region: plain steps, no events inside
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
+    for _ in range(args.steps):
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
+    # phase breakdown: the same steps again with HIP events between the kernels
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
 
     def avg(a, b):
         return sum(ev.ms(5 * i + a, 5 * i + b) for i in range(args.steps)) / args.steps

@@ -760,17 +760,42 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     }
 }
 
-// dh[b, j] = sum over chunks c (in order) of part[c, b, j]
+// dh[b, j] = sum over chunks c of part[c, b, j], in a fixed order: four lanes
+// per 4 consecutive outputs each add every fourth chunk (c = lane % 4 + 4i,
+// in i order), then the four partial sums are combined as (s0 + s1) + (s2 + s3).
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, float* __restrict__ dh,
                                                    int64_t B, int64_t H, int nchunks, int rows_per_chunk)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= B * H) return;
-    const int64_t b = i / H, j = i % H;
-    float s = 0.f;
-    for (int c = 0; c < nchunks; ++c)
-        s += part[((int64_t)c * rows_per_chunk + b) * H + j];
-    dh[i] = s;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t o4 = t >> 2;               // index of 4 consecutive outputs
+    const int sub = (int)(t & 3);
+    const int64_t n = B * H;
+    const int64_t i0 = 4 * o4;
+    const bool ok = i0 < n;
+    const int64_t b = ok ? i0 / H : 0, j = ok ? i0 % H : 0;
+    const int64_t stride = (int64_t)rows_per_chunk * H;
+    f32x4_t s = zero4();
+    if (ok) {
+        const float* p = part + b * H + j;
+        for (int c = sub; c < nchunks; c += 4)
+            s += *reinterpret_cast<const f32x4_t*>(p + c * stride);
+    }
+    // combine the four lanes of this output quad in a fixed pattern
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x1 = __shfl_xor(s[e], 1, 64);
+        const float y = (sub & 1) ? x1 + s[e] : s[e] + x1;   // s0+s1 / s2+s3 in lane order
+        const float y2 = __shfl_xor(y, 2, 64);
+        s[e] = (sub & 2) ? y2 + y : y + y2;
+    }
+    if (ok && sub == 0) {
+        if (i0 + 4 <= n) {
+            *reinterpret_cast<f32x4_t*>(dh + i0) = s;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (i0 + e < n) dh[i0 + e] = s[e];
+        }
+    }
 }
 
 template <int G, int F>
@@ -842,9 +867,11 @@ bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s)
 void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
                       hipStream_t s)
 {
-    const int64_t n = B * H;
-    hipLaunchKernelGGL(k_dh_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, dh, B, H, nchunks,
-                       rows_per_chunk);
+    // four threads per four consecutive outputs (the partials of a chunk hold
+    // at least B rows, so a last partial quad stays inside them)
+    const int64_t nthreads = (B * H + 3) / 4 * 4;
+    hipLaunchKernelGGL(k_dh_reduce, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, part, dh, B, H,
+                       nchunks, rows_per_chunk);
 }
 
 }  // namespace haste
