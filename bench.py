@@ -397,7 +397,7 @@ def main():
                 "algorithmic_bytes": nbytes, "avg_us": round(us, 2)}
 
     ra = roof("k_group_fwd", "k_group_fwd<STEP_DW> (forward + BCE + dW)", bytes_a, ph["fwd_bce_dw_us"])
-    rb = roof("k_group_dh", "k_group_dh<DH_FROM_LABELS> (feature gradient, logits recomputed)", bytes_b,
+    rb = roof("k_group_dh", "k_group_dh32 / k_group_dh, from labels (feature gradient, logits recomputed)", bytes_b,
               ph["dh_us"])
     dom, other = (rb, ra) if ph["dh_us"] >= ph["fwd_bce_dw_us"] else (ra, rb)
     res = {
