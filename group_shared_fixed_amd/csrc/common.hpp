@@ -75,6 +75,13 @@ __device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p)
 
 __device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return u32x4_t{a[0], a[1], b[0], b[1]}; }
 
+// An empty use of registers filled by loads: every path through this point
+// has waited for those loads, so code further on that reuses the registers
+// needs no wait (without it, a path that skipped the use leaves the loads
+// pending and the compiler drains all outstanding loads before the reuse).
+__device__ __forceinline__ void settle(const u32x4_t& v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void settle(int v) { asm volatile("" ::"v"(v)); }
+
 __device__ __forceinline__ u32x4_t ldg16(const void* p)
 {
     return *reinterpret_cast<const u32x4_t*>(p);
@@ -105,21 +112,25 @@ __device__ __forceinline__ float wave_sum(float v)
 // LDS writes a wave made before pass_turn are visible to the wave that next
 // sees the counter move; only the compiler has to be kept from reordering
 // them.  The wait is bounded (2^24 polls); a caller whose turn sequence is
-// complete never reaches the bound.
+// complete never reaches the bound.  While it holds the turn the wave runs
+// at a raised issue priority, so the waves queued behind it (and spinning
+// on the counter) do not slow it down.
 __device__ __forceinline__ void wait_turn(const int* t, int v)
 {
 #pragma unroll 1
     for (int spin = 0; spin < (1 << 24); ++spin) {
         const int cur = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(t, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (cur == v) return;
+        if (cur == v) break;
     }
+    __builtin_amdgcn_s_setprio(2);
 }
 
 __device__ __forceinline__ void pass_turn(int* t, int v)
 {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __hip_atomic_store(t, v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // XOR swizzle of 16-byte chunks inside a row of an LDS tile so that the

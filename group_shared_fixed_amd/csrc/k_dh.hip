@@ -561,7 +561,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         }
         load_col(kn, n.col);
         load_w(kn, n.w);
-        if (!active) return;
+        if (!active) {
+            // the inputs of an idle round still count as consumed (see settle)
+#pragma unroll
+            for (int pp = 0; pp < NWP; ++pp) settle(c.w[pp]);
+#pragma unroll
+            for (int hf = 0; hf < (LAB ? 2 : 1); ++hf)
+#pragma unroll
+                for (int u = 0; u < NHH; ++u) settle(c.h[hf][u]);
+#pragma unroll
+            for (int hf = 0; hf < (LAB ? 1 : 2); ++hf)
+#pragma unroll
+                for (int u = 0; u < NDH; ++u) settle(c.d[hf][u]);
+            return;
+        }
 
         // W_k rows into LDS (the contraction over labels reads them transposed)
 #pragma unroll
@@ -733,10 +746,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             ca[t] = sa.col[t];
-        const bool second = rd + 1 < nrounds;
-        if (second) round(rd + 1, sb, sa, pb);
+        // the second round always runs (past the last round it only issues
+        // clamped loads), so every path reaches the hand-off with the same
+        // loads outstanding
+        round(rd + 1, sb, sa, pb);
         const bool act_a = kc0 + NWV * rd + wv < kc1;
-        const bool act_b = second && kc0 + NWV * (rd + 1) + wv < kc1;
+        const bool act_b = kc0 + NWV * (rd + 1) + wv < kc1;
         const int turn = (int)(NWV * i) + wv;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
