@@ -398,13 +398,6 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     }
 }
 
-// Waves per 32-row workgroup when dZ is given: twelve when their tiles fit
-// next to the largest accumulator (32 x 768 fp32), else eight.
-constexpr int dh32_waves_dz(int G, int F)
-{
-    return (2 * G * F + 32 * G) * 12 + 32 * 768 * 4 + 64 <= 160 * 1024 ? 12 : 8;
-}
-
 // Offset (floats) of (batch row r < 32, column j) in the 32-row accumulator:
 // 32 floats per column, 4-row quads XORed with (j / 2) % 8 so the 16-byte
 // read-add-writes of one instruction (random columns) use all bank groups.
@@ -417,10 +410,11 @@ __device__ __forceinline__ int acc32_off(int j, int r)
 // group for both 16-row matrix-core tiles, so the W_k staging, its
 // transposed operand reads, the index loads and the accumulator addressing
 // serve twice the rows.  One workgroup per CU (accumulator 32 x H fp32 plus
-// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768, with eight
-// waves when the logits are recomputed and twelve (three per SIMD, the
-// register budget allows it) when dZ is given.
-template <int G, int F, int SRC, bool DET, int NWV>
+// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768.  A wave
+// takes its turn on the accumulator once per RPT rounds (RPT groups per
+// turn): four when dZ is given (the turn hand-offs bound that kernel, and
+// its per-group registers are few), two when the logits are recomputed.
+template <int G, int F, int SRC, bool DET, int NWV, int RPT>
 __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 {
     constexpr int NT = F / 16;          // output slot tiles of P
@@ -725,9 +719,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     // read-add-writes (rows 16 hf + 4q .. +3 of column col[t] are adjacent).
     // Inside one wave the index set is duplicate-free, so no two lanes touch
     // the same cell.  Each 16-row half of the accumulator has its own turn
-    // counter; waves take turns on a half in the fixed order (pair of rounds,
-    // wave), two groups per turn, so one wave can update one half while the
-    // next updates the other.
+    // counter; waves take turns on a half in the fixed order (batch of RPT
+    // rounds, wave), RPT groups per turn in round order, so one wave can
+    // update one half while the next updates the other.
     auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&col)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
@@ -737,27 +731,32 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q)) = v[t] + p[hf][t];
     };
-    const int64_t npairs = (nrounds + 1) / 2;
-    for (int64_t i = 0; i < npairs; ++i) {
-        const int64_t rd = 2 * i;
-        f32x4_t pa[2][NT], pb[2][NT];
-        int ca[NT];
-        round(rd, sa, sb, pa);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            ca[t] = sa.col[t];
-        // the second round always runs (past the last round it only issues
+    static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
+    const int64_t nbatch = (nrounds + RPT - 1) / RPT;
+    for (int64_t i = 0; i < nbatch; ++i) {
+        const int64_t rd = RPT * i;
+        f32x4_t p[RPT][2][NT];
+        int cl[RPT][NT];
+        // every round of the batch runs (past the last round it only issues
         // clamped loads), so every path reaches the hand-off with the same
-        // loads outstanding
-        round(rd + 1, sb, sa, pb);
-        const bool act_a = kc0 + NWV * rd + wv < kc1;
-        const bool act_b = kc0 + NWV * (rd + 1) + wv < kc1;
+        // loads outstanding; a round's columns are kept before the round
+        // after it overwrites its input set
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            In& c = (r % 2 == 0) ? sa : sb;
+            In& n = (r % 2 == 0) ? sb : sa;
+            round(rd + r, c, n, p[r]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                cl[r][t] = c.col[t];
+        }
         const int turn = (int)(NWV * i) + wv;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             wait_turn(&sTurn[hf], turn);
-            if (act_a) rmw(hf, pa, ca);
-            if (act_b) rmw(hf, pb, sb.col);
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                if (kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p[r], cl[r]);
             pass_turn(&sTurn[hf], turn);
         }
     }
@@ -830,22 +829,11 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
     if constexpr (G * F <= 2048 && F <= 64) {
         if (rows == 32) {
             if (src == DH_FROM_DZ) {
-                constexpr int NW = dh32_waves_dz(G, F);
-                const dim3 blk12(64 * NW);
-                auto go12 = [&](auto kern) {
-                    static bool attr = false;
-                    if (!attr) {
-                        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  96 * 1024);
-                        attr = true;
-                    }
-                    hipLaunchKernelGGL(kern, grid, blk12, lds, s, a);
-                };
-                if (det) go12(k_group_dh32<G, F, DH_FROM_DZ, true, NW>);
-                else go12(k_group_dh32<G, F, DH_FROM_DZ, false, NW>);
+                if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true, 8, 4>);
+                else go(k_group_dh32<G, F, DH_FROM_DZ, false, 8, 4>);
             } else {
-                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8>);
-                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8>);
+                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8, 2>);
+                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8, 2>);
             }
             return true;
         }
