@@ -129,17 +129,36 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
         }
     };
+    // W_k straight into the wave's LDS staging tile with direct-to-LDS loads
+    // (no registers), in the layout the staging writes below produce: LDS
+    // piece v = lane + 64 p holds global piece u with v's row and piece index
+    // (v % PR) ^ row.
+    auto load_w_lds = [&](int64_t kk) {
+        if constexpr (FWD) {
+            constexpr int PR = F / 8;
+            static_assert((G * PR) % 64 == 0, "whole instructions");
+#pragma unroll
+            for (int p = 0; p < NWP; ++p) {
+                const int v = lane + 64 * p;
+                const int row = v / PR;
+                const int u = row * PR + (((v % PR) ^ row) & (PR - 1));
+                __builtin_amdgcn_global_load_lds(a.W + kk * G * F + 8 * u,
+                                                 (__attribute__((address_space(3))) void*)(sWk[wv] + 512 * p), 16, 0, 0);
+            }
+        }
+    };
     // gather: lane (slot 16t + qr, quad position qc) <- h[32c + 8qc .. +8, I_k[slot]];
     // the row pointers of a group are formed once and reused for its chunks
-    auto rows_of = [&](const int (&cl)[NT], const uint16_t* (&gp)[NT]) {
+    // (as 32-bit byte offsets into hT, which holds H x Bp < 2^31 bytes)
+    auto rows_of = [&](const int (&cl)[NT], uint32_t (&gp)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            gp[t] = a.hT + (int64_t)cl[t] * a.Bp + 8 * qc;
+            gp[t] = 2u * ((uint32_t)cl[t] * (uint32_t)a.Bp + 8u * (uint32_t)qc);
     };
-    auto gather = [&](const uint16_t* const (&gp)[NT], int c, u32x4_t (&hr)[NT]) {
+    auto gather = [&](const uint32_t (&gp)[NT], int c, u32x4_t (&hr)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            hr[t] = ldg16(gp[t] + 32 * c);
+            hr[t] = ldg16(reinterpret_cast<const char*>(a.hT) + (gp[t] + 64u * (uint32_t)c));
     };
     // BWD_W: lane's 16-byte pieces of the chunk's dZ rows (piece ci = lane + 64 it:
     // row ci / (G/8), labels 8 (ci % (G/8)) .. +8 of the group)
@@ -219,17 +238,28 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     };
 
     int col[NT], col_n[NT];
-    const uint16_t* gp[NT];
+    uint32_t gp[NT];
     u32x4_t wraw[NWP];                      // weights as loaded
     u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
-    u32x4_t hA[NT], hB[NT];
-    u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1];
+    // Modes without per-chunk outputs run chunks in pairs: a pair's inputs
+    // are requested a whole pair ahead (sets A2 / B2 hold the second chunk),
+    // the next group's weights at the group's first pair, and a group's dW
+    // goes out after the wait of the next group's last pair.  Each load so
+    // gets two chunks (the weights a group) before the wait that needs it:
+    // vector memory operations retire in issue order, so a wait for a
+    // chunk's rows also waits for every older load.
+    constexpr bool PAIRS = (MODE == STEP_DW) && !WZ && !LOSS && PF_W && fwd_min_blocks(G, F, MODE) == 2;
+    constexpr int NT2 = NT, NDZ2 = MODE == BWD_W ? NDZ : 1;   // second-chunk sets (unused without pairs)
+    u32x4_t hA[NT], hB[NT], hA2[NT2], hB2[NT2];
+    u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1], dA2[NDZ2], dB2[NDZ2];
     if (k0 < k1) {
         load_col(k0, col);
-        load_w(k0, wraw);
+        if constexpr (!PAIRS) load_w(k0, wraw);
         rows_of(col, gp);
         gather(gp, 0, hA);
         if constexpr (MODE == BWD_W) load_dz(k0, 0, dA);
+        if (PAIRS && nchunk == 4) gather(gp, 1, hA2);
+        if constexpr (PAIRS) load_w(k0, wraw);
     }
 
     for (int64_t k = k0; k < k1; ++k) {
@@ -289,10 +319,18 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     dw[gt][t] = zero4();
         }
 
-        // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W); the
-        // next chunk's inputs go to hn / dn
-        auto chunk = [&](auto first, int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT],
-                         u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1], u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1]) {
+        // one 32-row chunk: rows in hc (and dZ pieces in dc for BWD_W).  Kind
+        // 0 / 1: single-chunk schedule (0 issues the deferred dW stores), the
+        // next chunk's inputs go to hn / dn.  Kind 3: second chunk of a pair.
+        // Kinds 5 and 6: first chunk of the first / last pair of a four-chunk
+        // group; the pair's second chunk sits in hc2 and the next pair's
+        // inputs go to (hn, hn2): chunks 2, 3 of this group and the next
+        // group's weights (5), or chunks 0, 1 of the next group after the
+        // deferred dW stores (6).
+        auto chunk = [&](auto kind, int c, u32x4_t (&hc)[NT], u32x4_t (&hn)[NT],
+                         u32x4_t (&dc)[MODE == BWD_W ? NDZ : 1], u32x4_t (&dn)[MODE == BWD_W ? NDZ : 1],
+                         u32x4_t (&hc2)[NT2], u32x4_t (&hn2)[NT2], u32x4_t (&dc2)[NDZ2], u32x4_t (&dn2)[NDZ2]) {
+            constexpr int KIND = decltype(kind)::value;
             // 1. this chunk's rows into the wave's LDS tile [slot][32 batch rows]
             //    (the wait for the chunk's loads)
 #pragma unroll
@@ -311,22 +349,39 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     }
                 }
             }
+            if constexpr (KIND >= 5) {
+                // the pair's second chunk counts as arrived here, before any
+                // store is issued (see settle)
+#pragma unroll
+                for (int t = 0; t < NT2; ++t) settle(hc2[t]);
+            }
             // 2. stores deferred from the previous chunk / group
             flush_z();
-            if constexpr (decltype(first)::value) flush_dw();
-            // 3. requests: the next chunk (or the next group's first chunk), and
-            //    once per group the next group's weights and index entries
-            if (c + 1 < nchunk) {
-                gather(gp, c + 1, hn);
-                if constexpr (MODE == BWD_W) load_dz(k, c + 1, dn);
-            } else {
-                const uint16_t* gpn[NT];
+            if constexpr (KIND == 0 || KIND == 6) flush_dw();
+            // 3. requests: the next chunk or pair (or the next group's first),
+            //    and once per group the next group's weights
+            if constexpr (KIND < 2) {
+                if (c + 1 < nchunk) {
+                    gather(gp, c + 1, hn);
+                    if constexpr (MODE == BWD_W) load_dz(k, c + 1, dn);
+                } else {
+                    uint32_t gpn[NT];
+                    rows_of(col_n, gpn);
+                    gather(gpn, 0, hn);
+                    if constexpr (MODE == BWD_W) load_dz(kn, 0, dn);
+                }
+                if constexpr (PF_W) {
+                    if (c == wchunk) load_w(kn, wraw);
+                }
+            } else if constexpr (KIND == 5) {
+                gather(gp, 2, hn);
+                gather(gp, 3, hn2);
+                load_w(kn, wraw);
+            } else if constexpr (KIND == 6) {
+                uint32_t gpn[NT];
                 rows_of(col_n, gpn);
                 gather(gpn, 0, hn);
-                if constexpr (MODE == BWD_W) load_dz(kn, 0, dn);
-            }
-            if constexpr (PF_W) {
-                if (c == wchunk) load_w(kn, wraw);
+                gather(gpn, 1, hn2);
             }
             wave_sync();
             // B operand of the weight-gradient product: lane (slot 16t + r16, q)
@@ -474,28 +529,40 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             }
         };
 
-        // Chunk 0 (which issues the deferred dW stores) is peeled off, so the
-        // chunk loop holds no stores and its waits stay exact; the rest run in
-        // pairs so the register buffers alternate without copies.
-        const std::true_type first;
-        const std::false_type later;
-        chunk(first, 0, hA, hB, dA, dB);
-        int c = 1;
-        for (; c + 1 < nchunk; c += 2) {
-            chunk(later, c, hB, hA, dB, dA);
-            chunk(later, c + 1, hA, hB, dA, dB);
-        }
-        if (c < nchunk) {
-            chunk(later, c, hB, hA, dB, dA);
+        if (PAIRS && nchunk == 4) {
+            // four chunks in two pairs: (0, 1) from the A sets requests (2, 3)
+            // into the B sets, (2, 3) requests the next group's (0, 1) into A
+            const std::integral_constant<int, 5> pfirst;
+            const std::integral_constant<int, 6> plast;
+            const std::integral_constant<int, 3> psecond;
+            chunk(pfirst, 0, hA, hB, dA, dB, hA2, hB2, dA2, dB2);
+            chunk(psecond, 1, hA2, hB, dA2, dB, hA2, hB2, dA2, dB2);
+            chunk(plast, 2, hB, hA, dB, dA, hB2, hA2, dB2, dA2);
+            chunk(psecond, 3, hB2, hA, dB2, dA, hB2, hA2, dB2, dA2);
         } else {
-            // odd chunk count: the next group's first rows landed in the B set
+            // Chunk 0 (which issues the deferred dW stores) is peeled off, so
+            // the chunk loop holds no stores and its waits stay exact; the rest
+            // run in pairs so the register buffers alternate without copies.
+            const std::integral_constant<int, 0> first;
+            const std::integral_constant<int, 1> later;
+            chunk(first, 0, hA, hB, dA, dB, hA2, hB2, dA2, dB2);
+            int c = 1;
+            for (; c + 1 < nchunk; c += 2) {
+                chunk(later, c, hB, hA, dB, dA, hA2, hB2, dA2, dB2);
+                chunk(later, c + 1, hA, hB, dA, dB, hA2, hB2, dA2, dB2);
+            }
+            if (c < nchunk) {
+                chunk(later, c, hB, hA, dB, dA, hA2, hB2, dA2, dB2);
+            } else {
+                // odd chunk count: the next group's first rows landed in the B set
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                hA[t] = hB[t];
-            if constexpr (MODE == BWD_W) {
+                for (int t = 0; t < NT; ++t)
+                    hA[t] = hB[t];
+                if constexpr (MODE == BWD_W) {
 #pragma unroll
-                for (int it = 0; it < NDZ; ++it)
-                    dA[it] = dB[it];
+                    for (int it = 0; it < NDZ; ++it)
+                        dA[it] = dB[it];
+                }
             }
         }
 

@@ -103,8 +103,13 @@ def test_step_fullsize_sampled(name):
     # the two modes add the same fp32 partials in different orders: they agree
     # to a few fp32 ulps of the largest |dh|, far inside the oracle tolerance
     assert_parity(dh_at, dh, "dh atomic vs det", rel=1e-5, mabs=1e-5 * float(np.abs(dh).max()))
-    dh2 = to_host(hs.step(h, idx, W, rp, col, s, G, mode="det")["dh"])
+    out2 = hs.step(h, idx, W, rp, col, s, G, mode="det")
+    dh2 = to_host(out2["dh"])
     assert (dh2.view(np.uint32) == dh.view(np.uint32)).all(), "deterministic dh not bitwise repeatable"
+    # without the optional Z output the forward kernel runs another chunk
+    # schedule (the one the benchmark times); the arithmetic is the same
+    dW2 = to_host(out2["dW"])
+    assert (dW2.view(np.uint32) == dW.view(np.uint32)).all(), "dW differs without the Z output"
 
 
 @pytest.mark.timeout(900)

@@ -30,6 +30,12 @@ CASES = {
     "g32_f64_many_b100": (100, 768, 3000, 32, 64),
     "g64_f64_many_b70": (70, 768, 1500, 64, 64),
     "g16_f128_many_b130": (130, 768, 1200, 16, 128),
+    # batches of 97..128 rows (four 32-row chunks) with small tiles: the
+    # fused step without optional outputs runs its chunks in pairs there
+    "g32_f64_many_b128": (128, 768, 2000, 32, 64),
+    "g16_f64_many_b120": (120, 512, 2500, 16, 64),
+    "g32_f32_b97": (97, 256, 300, 32, 32),
+    "g16_f32_b128": (128, 128, 40, 16, 32),
 }
 
 _cache = {}
@@ -137,7 +143,8 @@ def test_step(name, mode):
     assert abs(lg - ref["loss"]) <= 1e-5 * abs(ref["loss"])
 
 
-@pytest.mark.parametrize("name", ["tiny_4k", "g32_f64_b77", "g16_f128_b256"])
+@pytest.mark.parametrize("name", ["tiny_4k", "g32_f64_b77", "g16_f128_b256", "g32_f64_many_b128",
+                                  "g16_f64_many_b120", "g32_f32_b97", "g16_f32_b128", "g32_f64_many_b100"])
 def test_step_without_optional_outputs(name):
     d = case(name)
     say(f"  step(no Z, no loss) {name}")
