@@ -129,24 +129,6 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
         }
     };
-    // W_k straight into the wave's LDS staging tile with direct-to-LDS loads
-    // (no registers), in the layout the staging writes below produce: LDS
-    // piece v = lane + 64 p holds global piece u with v's row and piece index
-    // (v % PR) ^ row.
-    auto load_w_lds = [&](int64_t kk) {
-        if constexpr (FWD) {
-            constexpr int PR = F / 8;
-            static_assert((G * PR) % 64 == 0, "whole instructions");
-#pragma unroll
-            for (int p = 0; p < NWP; ++p) {
-                const int v = lane + 64 * p;
-                const int row = v / PR;
-                const int u = row * PR + (((v % PR) ^ row) & (PR - 1));
-                __builtin_amdgcn_global_load_lds(a.W + kk * G * F + 8 * u,
-                                                 (__attribute__((address_space(3))) void*)(sWk[wv] + 512 * p), 16, 0, 0);
-            }
-        }
-    };
     // gather: lane (slot 16t + qr, quad position qc) <- h[32c + 8qc .. +8, I_k[slot]];
     // the row pointers of a group are formed once and reused for its chunks
     // (as 32-bit byte offsets into hT, which holds H x Bp < 2^31 bytes)
@@ -241,14 +223,16 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     uint32_t gp[NT];
     u32x4_t wraw[NWP];                      // weights as loaded
     u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
-    // Modes without per-chunk outputs run chunks in pairs: a pair's inputs
+    // Modes without per-chunk outputs (and registers to spare) run four-chunk
+    // groups as two chunk pairs: a pair's inputs
     // are requested a whole pair ahead (sets A2 / B2 hold the second chunk),
     // the next group's weights at the group's first pair, and a group's dW
     // goes out after the wait of the next group's last pair.  Each load so
     // gets two chunks (the weights a group) before the wait that needs it:
     // vector memory operations retire in issue order, so a wait for a
     // chunk's rows also waits for every older load.
-    constexpr bool PAIRS = (MODE == STEP_DW) && !WZ && !LOSS && PF_W && fwd_min_blocks(G, F, MODE) == 2;
+    constexpr bool PAIRS = ((MODE == STEP_DW && !WZ && !LOSS && PF_W) || (MODE == BWD_W && G * F <= 2048)) &&
+                           fwd_min_blocks(G, F, MODE) == 2;
     constexpr int NT2 = NT, NDZ2 = MODE == BWD_W ? NDZ : 1;   // second-chunk sets (unused without pairs)
     u32x4_t hA[NT], hB[NT], hA2[NT2], hB2[NT2];
     u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1], dA2[NDZ2], dB2[NDZ2];
@@ -258,7 +242,10 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         rows_of(col, gp);
         gather(gp, 0, hA);
         if constexpr (MODE == BWD_W) load_dz(k0, 0, dA);
-        if (PAIRS && nchunk == 4) gather(gp, 1, hA2);
+        if (PAIRS && nchunk == 4) {
+            gather(gp, 1, hA2);
+            if constexpr (MODE == BWD_W) load_dz(k0, 1, dA2);
+        }
         if constexpr (PAIRS) load_w(k0, wraw);
     }
 
@@ -354,6 +341,10 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 // store is issued (see settle)
 #pragma unroll
                 for (int t = 0; t < NT2; ++t) settle(hc2[t]);
+                if constexpr (MODE == BWD_W) {
+#pragma unroll
+                    for (int it = 0; it < NDZ2; ++it) settle(dc2[it]);
+                }
             }
             // 2. stores deferred from the previous chunk / group
             flush_z();
@@ -376,12 +367,20 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             } else if constexpr (KIND == 5) {
                 gather(gp, 2, hn);
                 gather(gp, 3, hn2);
-                load_w(kn, wraw);
+                if constexpr (MODE == BWD_W) {
+                    load_dz(k, 2, dn);
+                    load_dz(k, 3, dn2);
+                }
+                if constexpr (PF_W) load_w(kn, wraw);
             } else if constexpr (KIND == 6) {
                 uint32_t gpn[NT];
                 rows_of(col_n, gpn);
                 gather(gpn, 0, hn);
                 gather(gpn, 1, hn2);
+                if constexpr (MODE == BWD_W) {
+                    load_dz(kn, 0, dn);
+                    load_dz(kn, 1, dn2);
+                }
             }
             wave_sync();
             // B operand of the weight-gradient product: lane (slot 16t + r16, q)
