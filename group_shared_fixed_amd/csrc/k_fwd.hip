@@ -69,6 +69,14 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     // Prefetch the next group's weights only when they are small; wide tiles
     // would push the wave past 256 registers (two waves per SIMD).
     constexpr bool PF_W = FWD && (GT * KS <= 4);
+    // Four-chunk groups run as two chunk pairs where the registers for a
+    // second set of inputs are there (see the chunk loop); with per-chunk
+    // outputs the pair's two chunks are staged in two buffers.
+    constexpr bool PAIRS_Z = (MODE == FWD_Z || (MODE == FWD_BCE && !LOSS && !WZ)) && F <= 64 && G <= 32;
+    constexpr bool PAIRS = (((MODE == STEP_DW && !WZ && !LOSS && PF_W) || (MODE == BWD_W && G * F <= 2048)) &&
+                            fwd_min_blocks(G, F, MODE) == 2) ||
+                           PAIRS_Z;
+    constexpr int ZB = PAIRS_Z ? 2 : 1;   // Z / dZ staging buffers
     // Output staging in LDS (row strides padded by 4 floats / 8 halves).  A
     // group's whole dW is staged and stored after the next group's first
     // wait when it fits; wide tiles go out per 16-label tile at once.
@@ -85,8 +93,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sD[4][MODE == BWD_W ? 32 * DST : 2];
     __shared__ __attribute__((aligned(16))) float sWo[4][WO_SIZE];
-    __shared__ __attribute__((aligned(16))) float sZo[4][STORE_Z && !ALIAS_WZ ? 32 * ZST : 4];
-    __shared__ __attribute__((aligned(16))) uint16_t sDo[4][STORE_DZ ? 32 * DZST : 8];
+    __shared__ __attribute__((aligned(16))) float sZo[4][ZB][STORE_Z && !ALIAS_WZ ? 32 * ZST : 4];
+    __shared__ __attribute__((aligned(16))) uint16_t sDo[4][ZB][STORE_DZ ? 32 * DZST : 8];
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -183,37 +191,46 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             }
         }
     };
+    // the staged Z / dZ rows of chunk cz of group pend_zk, from buffer zb
+    auto store_zc = [&](int zb, int cz) {
+        if constexpr (STORE_Z || STORE_DZ) {
+            if constexpr (STORE_Z) {
+                // piece u: chunk row u / (G/4), labels 4 (u % (G/4)) ..
+                const float* so = ALIAS_WZ ? sWo[wv] : sZo[wv][zb];
+                constexpr int NP = (8 * G + 63) / 64;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    const int u = lane + 64 * pp;
+                    const int lr = u / (G / 4), cc = u % (G / 4);
+                    const int64_t b = 32 * cz + lr;
+                    if (u < 8 * G && b < a.B)
+                        stg_stream(a.Z + b * L + pend_zk * G + 4 * cc,
+                                   *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc));
+                }
+            }
+            if constexpr (STORE_DZ) {
+                // piece u: chunk row u / (G/8), labels 8 (u % (G/8)) ..
+                const uint16_t* so = sDo[wv][zb];
+                constexpr int NP = (4 * G + 63) / 64;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    const int u = lane + 64 * pp;
+                    const int lr = u / (G / 8), cc = u % (G / 8);
+                    const int64_t b = 32 * cz + lr;
+                    if (u < 4 * G && b < a.B)
+                        stg_stream(a.dZ + b * L + pend_zk * G + 8 * cc,
+                                   *reinterpret_cast<const u32x4_t*>(so + lr * DZST + 8 * cc));
+                }
+            }
+        }
+    };
+    // (with pairs: both chunks of the pending pair, from their two buffers)
     auto flush_z = [&]() {
         if constexpr (STORE_Z || STORE_DZ) {
             if (pend_zk >= 0) {
-                if constexpr (STORE_Z) {
-                    // piece u: chunk row u / (G/4), labels 4 (u % (G/4)) ..
-                    const float* so = ALIAS_WZ ? sWo[wv] : sZo[wv];
-                    constexpr int NP = (8 * G + 63) / 64;
 #pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) {
-                        const int u = lane + 64 * pp;
-                        const int lr = u / (G / 4), cc = u % (G / 4);
-                        const int64_t b = 32 * pend_zc + lr;
-                        if (u < 8 * G && b < a.B)
-                            stg_stream(a.Z + b * L + pend_zk * G + 4 * cc,
-                                       *reinterpret_cast<const f32x4_t*>(so + lr * ZST + 4 * cc));
-                    }
-                }
-                if constexpr (STORE_DZ) {
-                    // piece u: chunk row u / (G/8), labels 8 (u % (G/8)) ..
-                    const uint16_t* so = sDo[wv];
-                    constexpr int NP = (4 * G + 63) / 64;
-#pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) {
-                        const int u = lane + 64 * pp;
-                        const int lr = u / (G / 8), cc = u % (G / 8);
-                        const int64_t b = 32 * pend_zc + lr;
-                        if (u < 4 * G && b < a.B)
-                            stg_stream(a.dZ + b * L + pend_zk * G + 8 * cc,
-                                       *reinterpret_cast<const u32x4_t*>(so + lr * DZST + 8 * cc));
-                    }
-                }
+                for (int zb = 0; zb < ZB; ++zb)
+                    store_zc(zb, pend_zc + zb);
                 pend_zk = -1;
             }
         }
@@ -231,8 +248,6 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     // gets two chunks (the weights a group) before the wait that needs it:
     // vector memory operations retire in issue order, so a wait for a
     // chunk's rows also waits for every older load.
-    constexpr bool PAIRS = ((MODE == STEP_DW && !WZ && !LOSS && PF_W) || (MODE == BWD_W && G * F <= 2048)) &&
-                           fwd_min_blocks(G, F, MODE) == 2;
     constexpr int NT2 = NT, NDZ2 = MODE == BWD_W ? NDZ : 1;   // second-chunk sets (unused without pairs)
     u32x4_t hA[NT], hB[NT], hA2[NT2], hB2[NT2];
     u32x4_t dA[MODE == BWD_W ? NDZ : 1], dB[MODE == BWD_W ? NDZ : 1], dA2[NDZ2], dB2[NDZ2];
@@ -346,8 +361,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     for (int it = 0; it < NDZ2; ++it) settle(dc2[it]);
                 }
             }
-            // 2. stores deferred from the previous chunk / group
-            flush_z();
+            // 2. stores deferred from the previous chunk (pair) / group
+            if constexpr (KIND != 3) flush_z();
             if constexpr (KIND == 0 || KIND == 6) flush_dw();
             // 3. requests: the next chunk or pair (or the next group's first),
             //    and once per group the next group's weights
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 //    chunk outputs are staged for the deferred store (chunk row 8q + 4mt + i)
                 const int64_t bq = 32 * c + 8 * q;
                 if constexpr (STORE_Z) {
-                    float* so = ALIAS_WZ ? sWo[wv] : sZo[wv];
+                    float* so = ALIAS_WZ ? sWo[wv] : sZo[wv][ZB > 1 ? (c & 1) : 0];
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                             }
                     }
                     if constexpr (STORE_DZ) {
-                        uint16_t* so = sDo[wv];
+                        uint16_t* so = sDo[wv][ZB > 1 ? (c & 1) : 0];
 #pragma unroll
                         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -522,7 +537,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                 }
                 if constexpr (STORE_Z || STORE_DZ) {
                     pend_zk = k;
-                    pend_zc = c;
+                    pend_zc = ZB > 1 ? (c & ~1) : c;
                 }
                 wave_sync();
             }

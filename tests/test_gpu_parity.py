@@ -128,6 +128,20 @@ def test_fwd_bce(name):
     assert abs(lg - ref["loss"]) <= 1e-5 * abs(ref["loss"])
 
 
+@pytest.mark.parametrize("name", ["tiny_4k", "g32_f64_b77", "g32_f64_many_b128", "g16_f64_many_b120", "g32_f32_b97",
+                                  "g16_f32_b128", "g16_f128_b256"])
+def test_fwd_bce_without_optional_outputs(name):
+    d = case(name)
+    say(f"  fwd_bce(no Z, no loss) {name} {CASES[name]}")
+    h, idx, W, _, rp, col = dev_inputs(d)
+    dZ, Z, loss = hs.fwd_bce(h, idx, W, rp, col, d["scale"], d["G"])
+    assert Z is None and loss is None
+    ref = O.oracle_step(d["h"], d["idx"], d["W"], d["y_rowptr"], d["y_col"], d["scale"], d["G"],
+                        want_dW=False, want_dh=False)
+    dz = to_host(dZ).astype(np.uint32) << 16
+    assert_parity(dz.view(np.float32), ref["dZ"], "dZ(bf16)")
+
+
 @pytest.mark.parametrize("mode", ["atomic", "det"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_step(name, mode):
