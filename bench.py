@@ -286,7 +286,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="amazon3m_shaped")
     ap.add_argument("--mode", default="det", choices=["atomic", "det"],
                     help="dh reduction (deterministic is the default: bitwise reproducible and, with the "
