@@ -65,7 +65,19 @@ __device__ __forceinline__ int dz_off(int r, int c)
     return r * G + ((((c ^ ((r * G) >> 7))) & (G / 8 - 1)) << 3);
 }
 
-template <int G, int F, int SRC, bool DET>
+// Rounds per batch of the 16-row kernel and whether the batch shares one
+// accumulator turn (else one turn per round): as many groups per turn as
+// the registers for their P tiles allow.
+constexpr int dh16_rpt(int G, int F, int src)
+{
+    return (src == DH_FROM_DZ && F <= 64) ? 4 : 2;
+}
+constexpr bool dh16_turn_per_round(int G, int F, int src)
+{
+    return src == DH_FROM_DZ ? G * F > 4096 : (G * F > 2048 && F > 64);
+}
+
+template <int G, int F, int SRC, bool DET, int RPT>
 __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 {
     constexpr int NT = F / 16;          // output slot tiles of P
@@ -327,6 +339,14 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                         p[t] = mfma16(alo[s], bv, p[t]);
                 }
             }
+        } else {
+            // the inputs of an idle round still count as consumed (see settle)
+#pragma unroll
+            for (int pp = 0; pp < NWP; ++pp) settle(c.w[pp]);
+#pragma unroll
+            for (int u = 0; u < (LAB ? NHP : 1); ++u) settle(c.h[u]);
+#pragma unroll
+            for (int u = 0; u < (LAB ? 1 : NDP); ++u) settle(c.d[u]);
         }
 
     };
@@ -345,44 +365,50 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
     };
 
-    // Rounds in pairs (one for wide index sets, where two P tiles would not
-    // fit in registers): the wave computes P for its groups of rounds 2i and
-    // 2i + 1, then takes its turn on the accumulator.  Turns go in the fixed
-    // order (pair, wave), handed on through an LDS counter, so every cell is
-    // updated by one wave at a time and in a fixed group order.
-    if constexpr (F <= 64) {
-        const int64_t npairs = (nrounds + 1) / 2;
-        for (int64_t i = 0; i < npairs; ++i) {
-            const int64_t rd = 2 * i;
-            f32x4_t pa[NT], pb[NT];
-            int ca[NT];
-            round(rd, sa, sb, pa);
+    // Rounds in batches of RPT: the wave computes P for its groups of the
+    // batch, then takes its turn on the accumulator.  Turns go in the fixed
+    // order (batch, wave), handed on through an LDS counter, so every cell is
+    // updated by one wave at a time and in a fixed group order.  Every round
+    // of a batch runs (past the last round it only issues clamped loads), so
+    // every path reaches the hand-off with the same loads in flight; a
+    // round's columns are kept before the round after it overwrites its
+    // input set.
+    static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
+    const int64_t nbatch = (nrounds + RPT - 1) / RPT;
+    for (int64_t i = 0; i < nbatch; ++i) {
+        const int64_t rd = RPT * i;
+        if constexpr (dh16_turn_per_round(G, F, SRC)) {
+            // wide tiles: each round's P goes into the accumulator at once
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                ca[t] = sa.col[t];
-            const bool second = rd + 1 < nrounds;
-            if (second) round(rd + 1, sb, sa, pb);
+            for (int r = 0; r < RPT; ++r) {
+                Stage& c = (r % 2 == 0) ? sa : sb;
+                Stage& n = (r % 2 == 0) ? sb : sa;
+                f32x4_t p[NT];
+                round(rd + r, c, n, p);
+                const int turn = (int)(4 * (rd + r)) + wv;
+                wait_turn(&sTurn, turn);
+                if (kc0 + 4 * (rd + r) + wv < kc1) rmw(p, c.col);
+                pass_turn(&sTurn, turn);
+            }
+        } else {
+            f32x4_t p[RPT][NT];
+            int cl[RPT][NT];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                Stage& c = (r % 2 == 0) ? sa : sb;
+                Stage& n = (r % 2 == 0) ? sb : sa;
+                round(rd + r, c, n, p[r]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    cl[r][t] = c.col[t];
+            }
             const int turn = (int)(4 * i) + wv;
             wait_turn(&sTurn, turn);
-            if (kc0 + 4 * rd + wv < kc1) rmw(pa, ca);
-            if (second && kc0 + 4 * (rd + 1) + wv < kc1) rmw(pb, sb.col);
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                if (kc0 + 4 * (rd + r) + wv < kc1) rmw(p[r], cl[r]);
             pass_turn(&sTurn, turn);
         }
-    } else {
-        auto one = [&](int64_t rd, const Stage& c, Stage& n) {
-            f32x4_t pa[NT];
-            round(rd, c, n, pa);
-            const int turn = (int)(4 * rd) + wv;
-            wait_turn(&sTurn, turn);
-            if (kc0 + 4 * rd + wv < kc1) rmw(pa, c.col);
-            pass_turn(&sTurn, turn);
-        };
-        int64_t rd = 0;
-        for (; rd + 1 < nrounds; rd += 2) {
-            one(rd, sa, sb);
-            one(rd + 1, sb, sa);
-        }
-        if (rd < nrounds) one(rd, sa, sb);
     }
     __syncthreads();
 
@@ -839,9 +865,12 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
         }
     }
     if (src == DH_FROM_DZ) {
-        if (det) go(k_group_dh<G, F, DH_FROM_DZ, true>); else go(k_group_dh<G, F, DH_FROM_DZ, false>);
+        constexpr int RP = dh16_rpt(G, F, DH_FROM_DZ);
+        if (det) go(k_group_dh<G, F, DH_FROM_DZ, true, RP>); else go(k_group_dh<G, F, DH_FROM_DZ, false, RP>);
     } else {
-        if (det) go(k_group_dh<G, F, DH_FROM_LABELS, true>); else go(k_group_dh<G, F, DH_FROM_LABELS, false>);
+        constexpr int RP = dh16_rpt(G, F, DH_FROM_LABELS);
+        if (det) go(k_group_dh<G, F, DH_FROM_LABELS, true, RP>);
+        else go(k_group_dh<G, F, DH_FROM_LABELS, false, RP>);
     }
     return true;
 }
