@@ -87,6 +87,14 @@ __device__ __forceinline__ u32x4_t ldg16(const void* p)
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// 16-byte load of a streamed input (read once): non-temporal, so it does
+// not displace the gathered feature rows cached in L2.  (Measured per use:
+// a win for the weights in the forward family, a loss for its dZ input.)
+__device__ __forceinline__ u32x4_t ldg16_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // 16-byte store of a streamed output (written once, not read again soon):
 // non-temporal, so it does not displace cached inputs.
 __device__ __forceinline__ void stg_stream(float* p, f32x4_t v)

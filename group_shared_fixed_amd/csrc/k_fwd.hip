@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         if constexpr (FWD) {
 #pragma unroll
             for (int p = 0; p < NWP; ++p)
-                wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+                wr[p] = ldg16_stream(a.W + kk * G * F + 8 * (lane + 64 * p));
         }
     };
     // gather: lane (slot 16t + qr, quad position qc) <- h[32c + 8qc .. +8, I_k[slot]];
