@@ -14,6 +14,10 @@ from .binding import (  # noqa: F401
     fixed_fwd,
     fwd,
     fwd_bce,
+    head_step,
+    head_workspace_size,
+    joint_step,
+    joint_workspace_size,
     step,
     validate_idx,
     validate_labels,

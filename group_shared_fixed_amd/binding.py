@@ -36,6 +36,11 @@ SIGNATURES = {
     "haste_fixed_fwd": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "haste_fixed_bwd_w": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "haste_fixed_bwd_h": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _M, _P, _S, _P]),
+    "haste_head_workspace_size": (_S, [_I, _I, _I]),
+    "haste_head_step": (_M, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _S, _P]),
+    "haste_joint_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _M]),
+    "haste_joint_step": (_M, [_P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _M,
+                              _P, _S, _P]),
     "haste_validate_idx": (_M, [_P, _I, _I, _I, _P, _P]),
     "haste_validate_labels": (_M, [_P, _P, _I, _I, _P, _P]),
     "haste_status_string": (ctypes.c_char_p, [_M]),
@@ -251,6 +256,66 @@ def fixed_bwd_h(dZ, idx1, W, H, mode="atomic", dh=None, workspace=None, stream=N
                                                          _ptr(ws), ws.numel() if ws is not None else 0,
                                                          _stream(dZ, stream)))
     return dh
+
+
+def head_workspace_size(B, H, L_head) -> int:
+    return int(lib().haste_head_workspace_size(B, H, L_head))
+
+
+def head_step(h, W_head, y_rowptr, y_col, scale, want_Z=False, want_loss=False, out=None, workspace=None,
+              stream=None):
+    """Dense head pass: Z = h W^T, BCE gradient, dW, dh.  Returns dict(dW, dh, Z, loss)."""
+    torch = _torch()
+    _bits(h); _bits(W_head); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    L = W_head.shape[0]
+    if W_head.shape[1] != H:
+        raise ValueError("W_head must be L_head x H")
+    if out is None:
+        out = {
+            "dW": torch.empty(L, H, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "Z": torch.empty(B, L, dtype=torch.float32, device=h.device) if want_Z else None,
+            "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
+        }
+    n = head_workspace_size(B, H, L)
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=h.device)
+    _check("haste_head_step", lib().haste_head_step(
+        _ptr(h), _ptr(W_head), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]), _ptr(out["dh"]),
+        _ptr(out.get("Z")), _ptr(out.get("loss")), B, H, L, _ptr(ws), ws.numel(), _stream(h, stream)))
+    return out
+
+
+def joint_workspace_size(B, H, K, G, F, L_head, dh_mode="atomic") -> int:
+    return int(lib().haste_joint_workspace_size(B, H, K, G, F, L_head, DH_MODE[dh_mode]))
+
+
+def joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_col, scale_tail, scale_head, G,
+               mode="atomic", want_loss=False, out=None, workspace=None, stream=None):
+    """Head + tail pass on shared features.  Returns dict(dW_tail, dW_head, dh, loss)."""
+    torch = _torch()
+    _bits(h); _bits(W_tail); _bits(W_head); _i32(idx)
+    _i32(yt_rowptr); _i32(yt_col); _i32(yh_rowptr); _i32(yh_col)
+    B, H = h.shape
+    K, F = idx.shape
+    L = W_head.shape[0]
+    if W_head.shape[1] != H:
+        raise ValueError("W_head must be L_head x H")
+    if out is None:
+        out = {
+            "dW_tail": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dW_head": torch.empty(L, H, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
+        }
+    m = DH_MODE[mode]
+    n = joint_workspace_size(B, H, K, G, F, L, m)
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=h.device)
+    _check("haste_joint_step", lib().haste_joint_step(
+        _ptr(h), _ptr(idx), _ptr(W_tail), _ptr(yt_rowptr), _ptr(yt_col), _ptr(W_head), _ptr(yh_rowptr),
+        _ptr(yh_col), float(scale_tail), float(scale_head), _ptr(out["dW_tail"]), _ptr(out["dW_head"]),
+        _ptr(out["dh"]), _ptr(out.get("loss")), B, H, K, G, F, L, m, _ptr(ws), ws.numel(), _stream(h, stream)))
+    return out
 
 
 def validate_idx(idx, H, stream=None) -> int:

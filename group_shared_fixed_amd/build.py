@@ -56,7 +56,8 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lrocblas",
+           "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     if verbose:

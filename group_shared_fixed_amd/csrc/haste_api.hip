@@ -299,6 +299,107 @@ int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t
     return hip_status();
 }
 
+namespace {
+
+// Head workspace: Z (B x L fp32), stacked dZ hi / lo (2B x L bf16), [h; h]
+// (2B x H bf16), the stacked dh product (2B x H fp32), rocBLAS's workspace.
+struct HeadLayout {
+    size_t z, dz, hcat, dhcat, blas, total;
+    HeadLayout(int64_t B, int64_t H, int64_t L)
+    {
+        const size_t bl = (size_t)B * (size_t)L, bh = (size_t)B * (size_t)H;
+        z = 0;
+        dz = z + align256(bl * 4);
+        hcat = dz + align256(bl * 4);
+        dhcat = hcat + align256(bh * 4);
+        blas = dhcat + align256(bh * 8);
+        total = blas + kHeadBlasWorkspace;
+    }
+};
+
+}  // namespace
+
+size_t haste_head_workspace_size(int64_t B, int64_t H, int64_t L)
+{
+    if (B < 1 || H < 1 || L < 1) return 0;
+    return HeadLayout(B, H, L).total;
+}
+
+namespace {
+
+int check_head(const haste_bf16* h, const haste_bf16* W, const int32_t* y_rowptr, const int32_t* y_col,
+               float scale, const float* dW, const float* dh, const float* Z, const double* loss, int64_t B,
+               int64_t H, int64_t L)
+{
+    if (!h || !W || !y_rowptr || !y_col || !dW || !dh) return HASTE_ERR_NULL;
+    if (B < 1 || H < 1 || L < 1 || !(scale > 0.f)) return HASTE_ERR_DIM;
+    // rocBLAS takes 32-bit sizes and leading dimensions
+    if (L > kMaxLabels || H > (1 << 20) || B > (1 << 24)) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) || !aligned16(dW) ||
+        !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
+        return HASTE_ERR_ALIGN;
+    return HASTE_OK;
+}
+
+// The head pass on the workspace of haste_head_workspace_size.
+int head_pass(const haste_bf16* h, const haste_bf16* W, const int32_t* y_rowptr, const int32_t* y_col,
+              float scale, float* dW, float* dh, float* Z, double* loss, int64_t B, int64_t H, int64_t L,
+              bool accumulate, void* workspace, hipStream_t stream)
+{
+    const HeadLayout l(B, H, L);
+    char* w = (char*)workspace;
+    float* zbuf = Z ? Z : (float*)(w + l.z);
+    if (!run_head(h, W, y_rowptr, y_col, scale, dW, dh, zbuf, loss, B, H, L, accumulate, (uint16_t*)(w + l.dz),
+                  (uint16_t*)(w + l.hcat), (float*)(w + l.dhcat), w + l.blas, kHeadBlasWorkspace, stream))
+        return HASTE_ERR_HIP;
+    return hip_status();
+}
+
+}  // namespace
+
+int haste_head_step(const haste_bf16* h, const haste_bf16* W_head, const int32_t* y_rowptr, const int32_t* y_col,
+                    float scale, float* dW_head, float* dh, float* Z_head, double* loss, int64_t B, int64_t H,
+                    int64_t L_head, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    HASTE_TRY(check_head(h, W_head, y_rowptr, y_col, scale, dW_head, dh, Z_head, loss, B, H, L_head));
+    HASTE_TRY(check_ws(workspace, workspace_bytes, haste_head_workspace_size(B, H, L_head)));
+    if (loss) launch_fill_f64(loss, 1, stream);
+    return head_pass(h, W_head, y_rowptr, y_col, scale, dW_head, dh, Z_head, loss, B, H, L_head, false, workspace,
+                     stream);
+}
+
+size_t haste_joint_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head,
+                                  int dh_mode)
+{
+    const size_t tail = haste_workspace_size(HASTE_OP_STEP, B, H, K, G, F, dh_mode);
+    const size_t head = haste_head_workspace_size(B, H, L_head);
+    if (head == 0) return 0;
+    return tail > head ? tail : head;
+}
+
+int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W_tail, const int32_t* yt_rowptr,
+                     const int32_t* yt_col, const haste_bf16* W_head, const int32_t* yh_rowptr,
+                     const int32_t* yh_col, float scale_tail, float scale_head, float* dW_tail, float* dW_head,
+                     float* dh, double* loss,
+                     int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head, int dh_mode,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!idx || !W_tail || !yt_rowptr || !yt_col || !dW_tail) return HASTE_ERR_NULL;
+    HASTE_TRY(check_head(h, W_head, yh_rowptr, yh_col, scale_head, dW_head, dh, nullptr, loss, B, H, L_head));
+    if (!(scale_tail > 0.f)) return HASTE_ERR_DIM;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (B > kMaxLabelBatch) return HASTE_ERR_UNSUPPORTED;
+    if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(idx) || !aligned16(W_tail) || !aligned16(yt_rowptr) || !aligned16(yt_col) || !aligned16(dW_tail))
+        return HASTE_ERR_ALIGN;
+    HASTE_TRY(check_ws(workspace, workspace_bytes, haste_joint_workspace_size(B, H, K, G, F, L_head, dh_mode)));
+    // tail: writes dh and clears + accumulates the loss; head: adds to both
+    HASTE_TRY(haste_step(h, idx, W_tail, yt_rowptr, yt_col, scale_tail, dW_tail, dh, nullptr, loss, B, H, K, G, F,
+                         dh_mode, workspace, workspace_bytes, stream));
+    return head_pass(h, W_head, yh_rowptr, yh_col, scale_head, dW_head, dh, nullptr, loss, B, H, L_head, true, workspace,
+                     stream);
+}
+
 const char* haste_status_string(int status)
 {
     switch (status) {

@@ -1,0 +1,196 @@
+// Dense head of the head-tail split.
+//
+// HASTE "head-tail split" section: the most frequent labels go to a dense
+// head (every label sees all H features) and the rest to the group-shared
+// sparse tail; one BCE objective covers both.  The head's three products are
+// plain dense GEMMs (Z = h W^T, dW = dZ^T h, dh = dZ W) and run on rocBLAS
+// (bf16 in, fp32 accumulate and out); the BCE gradient between them is the
+// kernel below.  dZ goes to the GEMMs as two bf16 matrices, hi and the
+// rounding residual lo, so the two weight-side products carry about 16
+// significant bits of dZ, as the tail's fused kernels do.  The two parts are
+// stacked (hi rows 0..B-1, lo rows B..2B-1) so that each weight-side product
+// is one GEMM that reads W or writes dW once: dW = [hi; lo]^T [h; h] (a
+// 2B-deep contraction) and dh = [hi; lo] W (2B rows, whose halves are then
+// added).
+#include <rocblas/rocblas.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace haste {
+
+// dZ[b, l] = s (sigmoid(Z[b, l]) - Y[b, l]) as bf16 hi + lo, and optionally
+// loss += s sum [max(z, 0) + log(1 + e^-|z|) - y z].  One thread per eight
+// consecutive labels of one sample; Y comes from the sample's sorted CSR row.
+__global__ __launch_bounds__(256) void k_head_bce(const float* __restrict__ Z, const int32_t* __restrict__ rowptr,
+                                                  const int32_t* __restrict__ col, float scale,
+                                                  uint16_t* __restrict__ dz_hi, uint16_t* __restrict__ dz_lo,
+                                                  double* __restrict__ loss, int64_t B, int64_t L)
+{
+    const int64_t per_row = (L + 7) / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float lsum = 0.f;
+    if (t < B * per_row) {
+        const int64_t b = t / per_row;
+        const int64_t l0 = (t % per_row) * 8;
+        // positives of sample b among labels l0 .. l0 + 7
+        int lo = rowptr[b];
+        const int end = rowptr[b + 1];
+        int hi = end;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int64_t)col[mid] < l0) lo = mid + 1; else hi = mid;
+        }
+        uint32_t ymask = 0;
+        for (int p = lo; p < end && (int64_t)col[p] < l0 + 8; ++p)
+            ymask |= 1u << (int)((int64_t)col[p] - l0);
+
+        const float* zr = Z + b * L + l0;
+        float z[8];
+        const bool full = (l0 + 8 <= L) && (L % 4 == 0);
+        if (full) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(zr);
+            const f32x4_t c = *reinterpret_cast<const f32x4_t*>(zr + 4);
+            z[0] = a[0]; z[1] = a[1]; z[2] = a[2]; z[3] = a[3];
+            z[4] = c[0]; z[5] = c[1]; z[6] = c[2]; z[7] = c[3];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = (l0 + e < L) ? zr[e] : 0.f;
+        }
+        float dz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool y = (ymask >> e) & 1u;
+            // u = e^-|z|: sigmoid(|z|) = 1 / (1 + u), sigmoid(-|z|) = u / (1 + u)
+            const float u = __builtin_amdgcn_exp2f(-fabsf(z[e]) * kLog2e);
+            const float r = __builtin_amdgcn_rcpf(1.0f + u);
+            const float sg = z[e] >= 0.f ? r : u * r;         // sigmoid(z)
+            const float om = z[e] >= 0.f ? u * r : r;         // 1 - sigmoid(z)
+            dz[e] = y ? -scale * om : scale * sg;
+            if (loss && l0 + e < L)
+                lsum += fmaxf(z[e], 0.f) + __builtin_amdgcn_logf(1.0f + u) * kLn2 - (y ? z[e] : 0.f);
+        }
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x2_t p = split_pair(dz[2 * i], dz[2 * i + 1]);
+            ph[i] = p[0];
+            pl[i] = p[1];
+        }
+        uint16_t* oh = dz_hi + b * L + l0;
+        uint16_t* ol = dz_lo + b * L + l0;
+        if (l0 + 8 <= L && L % 8 == 0) {
+            *reinterpret_cast<u32x4_t*>(oh) = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+            *reinterpret_cast<u32x4_t*>(ol) = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (l0 + e < L) {
+                    oh[e] = (uint16_t)(ph[e / 2] >> (16 * (e % 2)));
+                    ol[e] = (uint16_t)(pl[e / 2] >> (16 * (e % 2)));
+                }
+            }
+        }
+    }
+    if (loss) {
+        // block sum, then one double atomic per block
+        __shared__ float red[4];
+        const float w = wave_sum(lsum);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+        __syncthreads();
+        if (threadIdx.x == 0) atomicAdd(loss, (double)((red[0] + red[1]) + (red[2] + red[3])) * (double)scale);
+    }
+}
+
+namespace {
+
+// One rocBLAS handle per host thread and device, created on first use and
+// kept for the process: its atomics are off (bitwise repeatable products)
+// and each call sets the stream and the caller's workspace.
+rocblas_handle blas_handle(hipStream_t stream, void* ws, size_t ws_bytes)
+{
+    thread_local rocblas_handle handles[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    rocblas_handle& h = handles[dev];
+    if (!h) {
+        if (rocblas_create_handle(&h) != rocblas_status_success) {
+            h = nullptr;
+            return nullptr;
+        }
+        (void)rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed);
+    }
+    if (rocblas_set_stream(h, stream) != rocblas_status_success) return nullptr;
+    if (rocblas_set_workspace(h, ws, ws_bytes) != rocblas_status_success) return nullptr;
+    return h;
+}
+
+// Row-major C (M x N, fp32) = alpha op(A) op(B) + beta C with bf16 A and B,
+// expressed as the column-major product C^T = op(B)^T op(A)^T.
+rocblas_status gemm_rm(rocblas_handle h, bool ta, bool tb, int64_t M, int64_t N, int64_t Kd, const uint16_t* A,
+                       int64_t lda, const uint16_t* Bm, int64_t ldb, float beta, float* C, int64_t ldc)
+{
+    const float alpha = 1.0f;
+    return rocblas_gemm_ex(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                           ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)N, (rocblas_int)M,
+                           (rocblas_int)Kd, &alpha, Bm, rocblas_datatype_bf16_r, (rocblas_int)ldb, A,
+                           rocblas_datatype_bf16_r, (rocblas_int)lda, &beta, C, rocblas_datatype_f32_r,
+                           (rocblas_int)ldc, C, rocblas_datatype_f32_r, (rocblas_int)ldc, rocblas_datatype_f32_r,
+                           rocblas_gemm_algo_standard, 0, 0);
+}
+
+}  // namespace
+
+// dh = base + top + bottom, with top and bottom the two B x H halves of the
+// stacked product (base = dh when accumulating, else 0).
+__global__ __launch_bounds__(256) void k_head_dh_sum(const float* __restrict__ part, float* __restrict__ dh, int64_t n,
+                                                     bool accumulate)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    if (i + 4 <= n && n % 4 == 0) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(part + i);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(part + n + i);
+        f32x4_t r = a + b;
+        if (accumulate) r = *reinterpret_cast<const f32x4_t*>(dh + i) + r;
+        *reinterpret_cast<f32x4_t*>(dh + i) = r;
+    } else {
+        for (int64_t e = i; e < i + 4 && e < n; ++e) {
+            const float r = part[e] + part[n + e];
+            dh[e] = accumulate ? dh[e] + r : r;
+        }
+    }
+}
+
+// The head pass on `stream`: Z (B x L fp32, in zbuf), the BCE gradient as a
+// stacked bf16 hi / lo matrix dzcat (2B x L), hcat = [h; h] (2B x H bf16),
+// dW = dzcat^T hcat (L x H fp32), the stacked dh product in dhcat (2B x H
+// fp32) and dh (B x H fp32, added to when accumulate_dh).  Returns false if a
+// rocBLAS call or a copy fails.
+bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
+              float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
+              uint16_t* dzcat, uint16_t* hcat, float* dhcat, void* blas_ws, size_t blas_ws_bytes,
+              hipStream_t stream)
+{
+    rocblas_handle bh = blas_handle(stream, blas_ws, blas_ws_bytes);
+    if (!bh) return false;
+    const size_t hbytes = (size_t)B * (size_t)H * 2;
+    if (hipMemcpyAsync(hcat, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
+    if (hipMemcpyAsync(hcat + B * H, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
+    // Z = h W^T (B x L)
+    if (gemm_rm(bh, false, true, B, L, H, h, H, W, H, 0.f, zbuf, L) != rocblas_status_success) return false;
+    const int64_t n = B * ((L + 7) / 8);
+    hipLaunchKernelGGL(k_head_bce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zbuf, rowptr, col, scale,
+                       dzcat, dzcat + B * L, loss, B, L);
+    // dW = [hi; lo]^T [h; h] (L x H)
+    if (gemm_rm(bh, true, false, L, H, 2 * B, dzcat, L, hcat, H, 0.f, dW, H) != rocblas_status_success) return false;
+    // [dh_hi; dh_lo] = [hi; lo] W (2B x H), then dh (+)= dh_hi + dh_lo
+    if (gemm_rm(bh, false, false, 2 * B, H, L, dzcat, L, W, H, 0.f, dhcat, H) != rocblas_status_success)
+        return false;
+    const int64_t m = B * H;
+    hipLaunchKernelGGL(k_head_dh_sum, dim3((unsigned)(((m + 3) / 4 + 255) / 256)), dim3(256), 0, stream, dhcat, dh, m,
+                       accumulate_dh);
+    return true;
+}
+
+}  // namespace haste

@@ -161,6 +161,48 @@ int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf1
                       int64_t B, int64_t H, int64_t L, int64_t F, int dh_mode,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Dense head of the head-tail split ("head-tail split" section: the most
+ * frequent labels get a dense head, every label seeing all H features, next
+ * to the group-shared sparse tail; one BCE objective over both).  One
+ * training pass of the head: Z = h W_head^T, dZ = scale * (sigmoid(Z) - Y)
+ * (Y: B x L_head 0/1 labels as CSR with sorted, unique, head-local ids),
+ * dW_head = dZ^T h and dh = dZ W_head.  W_head is L_head x H bf16
+ * row-major, dW_head L_head x H fp32 and dh B x H fp32 (both overwritten),
+ * Z_head (nullable) B x L_head fp32, loss (nullable) 1 double, set to
+ * scale * sum [max(z,0) + log(1 + e^-|z|) - y z].  The three products run on
+ * rocBLAS (bf16 in, fp32 accumulate and out, atomics off: Z, dW_head and dh
+ * are bitwise repeatable; the loss is summed with atomics).  dZ reaches the
+ * two weight-side products as stacked bf16 hi + lo parts (about 16
+ * significant bits).  The BCE gradient is a libhaste kernel.  The rocBLAS
+ * handle is created on the first call of a host thread on a device and kept
+ * for the process; each call hands it part of `workspace`.  Limits: B <=
+ * 2^24, H <= 2^20, L_head < 2^31 - 64.  Errors as haste_step.  Workspace:
+ * haste_head_workspace_size(B, H, L_head) bytes, 256-byte aligned. */
+size_t haste_head_workspace_size(int64_t B, int64_t H, int64_t L_head);
+int haste_head_step(const haste_bf16* h, const haste_bf16* W_head, const int32_t* y_rowptr, const int32_t* y_col,
+                    float scale, float* dW_head, float* dh, float* Z_head, double* loss, int64_t B, int64_t H,
+                    int64_t L_head, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Joint head + tail training pass of the head-tail split: haste_step on the
+ * group-shared tail (idx, W_tail, tail-local labels yt_*, scale_tail) and the
+ * dense head pass (W_head, head-local labels yh_*, scale_head) on the same
+ * features h.  With the objective averaged over samples both scales are
+ * 1/B; they are separate so that a caller can weight the branches.  dh
+ * receives the sum of both branches' feature gradients (tail first, then the
+ * head's product added on top, in a fixed order: deterministic when dh_mode
+ * is), loss (nullable) the sum of both branches' losses.  Tail shapes and
+ * limits as haste_step, head as haste_head_step.  Workspace:
+ * haste_joint_workspace_size(...) bytes (the branches run one after the
+ * other on `stream` and share it). */
+size_t haste_joint_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head,
+                                  int dh_mode);
+int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W_tail, const int32_t* yt_rowptr,
+                     const int32_t* yt_col, const haste_bf16* W_head, const int32_t* yh_rowptr,
+                     const int32_t* yh_col, float scale_tail, float scale_head, float* dW_tail, float* dW_head,
+                     float* dh, double* loss,
+                     int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head, int dh_mode,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Count (into *bad, a device int32 the call zeroes first) the index rows
  * that have an entry outside [0, H) or are not strictly increasing. */
 int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad,

@@ -1,8 +1,11 @@
-"""ctypes wrapper of liboracle.so (built from haste_oracle.c with gcc).
+"""ctypes wrapper of liboracle.so (built from haste_oracle.c with gcc), and
+the dense head of the head-tail split in numpy fp64.
 
-Test infrastructure only.  Every function takes numpy arrays: bf16 tensors as
-uint16 bit patterns, index sets and labels as int32, and returns fp64 numpy
-arrays.  Shapes are checked here; the C code assumes them.
+Test infrastructure only: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg use it, never the product path.  Every function
+takes numpy arrays: bf16 tensors as uint16 bit patterns, index sets and
+labels as int32, and returns fp64 numpy arrays.  Shapes are checked here; the
+C code assumes them.
 """
 
 from __future__ import annotations
@@ -150,3 +153,36 @@ def oracle_step(h, idx, W, y_rowptr, y_col, scale, G, want_dW=True, want_dh=True
     lib.oracle_step(_p(h), _p(idx), _p(W), _p(y_rowptr), _p(y_col), float(scale),
                     _p(Z), _p(dZ), _p(dW), _p(dh), _p(loss), B, H, K, G, F)
     return {"Z": Z, "dZ": dZ, "dW": dW, "dh": dh, "loss": float(loss[0])}
+
+
+def _bf16_f64(bits):
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def oracle_head_step(h, W_head, y_rowptr, y_col, scale, lib=None):
+    """Dense head of the head-tail split (HASTE notes, "Head-tail split":
+    every head label sees all H features; the BCE objective covers head and
+    tail labels alike).  Z = h W_head^T, dZ and the loss from oracle_bce,
+    dW = dZ^T h, dh = dZ W_head; numpy fp64 products.  Returns dict with Z,
+    dZ, dW (L_head x H), dh (B x H), loss."""
+    B, H = h.shape
+    L = W_head.shape[0]
+    _check("h", h, np.uint16, (B, H)); _check("W_head", W_head, np.uint16, (L, H))
+    hf, Wf = _bf16_f64(h), _bf16_f64(W_head)
+    Z = np.ascontiguousarray(hf @ Wf.T)
+    dZ, loss = oracle_bce(Z, y_rowptr, y_col, scale, lib=lib)
+    return {"Z": Z, "dZ": dZ, "dW": dZ.T @ hf, "dh": dZ @ Wf, "loss": loss}
+
+
+def oracle_joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_col, scale_tail, scale_head, G,
+                      lib=None):
+    """Head + tail training pass on shared features h (HASTE notes,
+    "Head-tail split"): the tail's oracle_step and the head's
+    oracle_head_step; the feature gradient and the loss of the joint
+    objective are the sums of the two branches'.  Returns dict with dW_tail,
+    dW_head, dh, loss and the per-branch results under "tail" and "head"."""
+    t = oracle_step(h, idx, W_tail, yt_rowptr, yt_col, scale_tail, G, lib=lib)
+    hd = oracle_head_step(h, W_head, yh_rowptr, yh_col, scale_head, lib=lib)
+    return {"dW_tail": t["dW"], "dW_head": hd["dW"], "dh": t["dh"] + hd["dh"], "loss": t["loss"] + hd["loss"],
+            "tail": t, "head": hd}

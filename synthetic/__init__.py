@@ -10,6 +10,7 @@ from .configs import WORKLOADS, Workload, get_workload  # noqa: F401
 from .gen import (  # noqa: F401
     bf16_bits,
     bf16_value,
+    head_tail_labels,
     make_inputs,
     normal_bf16,
     sorted_subsets,

@@ -23,6 +23,7 @@ class Workload:
     B: int          # batch
     m: int          # positive labels per sample (0/1 label matrix row weight)
     zipf_s: float = 1.1
+    head_labels: int = 0   # > 0: this is the tail of a head-tail split with this many head labels
 
     @property
     def K(self) -> int:
@@ -44,8 +45,13 @@ WORKLOADS = {
     "lfpaper8600k_shaped": Workload("lfpaper8600k_shaped", 4, L=8_601_600, G=64, H=768, F=64, B=64, m=5),
     # Sparse tail of a 3M label space after moving the 3 % most frequent
     # labels (89,088) to a dense head: 2,910,848 tail labels, divisible by
-    # 16, 32 and 64.  G here is the default of the G sweep.
-    "ht3m_tail_shaped": Workload("ht3m_tail_shaped", 5, L=2_910_848, G=32, H=768, F=64, B=128, m=36),
+    # 16, 32 and 64.  G here is the default of the G sweep.  The ~36
+    # positives per sample are drawn over all 2,999,936 labels and split.
+    "ht3m_tail_shaped": Workload("ht3m_tail_shaped", 5, L=2_910_848, G=32, H=768, F=64, B=128, m=36,
+                                 head_labels=89_088),
+    # Small head-tail split for parity tests: 1,504 tail labels (G = 16,
+    # F = 32) and a 73-label dense head over H = 96 features.
+    "ht_small": Workload("ht_small", 6, L=1_504, G=16, H=96, F=32, B=37, m=9, head_labels=73),
 }
 
 HT3M_FULL_LABELS = 2_999_936

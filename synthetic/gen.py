@@ -4,7 +4,7 @@ Every tensor is drawn from ``np.random.SeedSequence([seed_no, tensor_no,
 chunk])`` so the result does not depend on the number of worker threads.
 Tensor numbers: 0 group index sets, 1 features h, 2 weights W, 3 upstream
 gradient dZ, 4 label-rank permutation, 5 positive labels, 6 per-label index
-sets of the G=1 fixed fan-in baseline.
+sets of the G=1 fixed fan-in baseline, 7 dense-head weights.
 
 bf16 values are carried as their uint16 bit patterns, rounded from float32
 to nearest with ties to even.
@@ -17,7 +17,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-T_IDX, T_H, T_W, T_DZ, T_PERM, T_POS, T_IDX1 = range(7)
+T_IDX, T_H, T_W, T_DZ, T_PERM, T_POS, T_IDX1, T_WHEAD = range(8)
 
 _CHUNK = 1 << 22  # elements per independently seeded chunk
 
@@ -94,15 +94,9 @@ def sorted_subsets(rows: int, F: int, H: int, seed_no: int, tensor_no: int = T_I
     return out
 
 
-def zipf_labels(B: int, L: int, m: int, seed_no: int, s: float = 1.1):
-    """0/1 label matrix B x L as CSR (rowptr int32 [B+1], col int32 [B*m]).
-
-    Every sample gets exactly m distinct labels.  A label is drawn by rank r
-    from a Zipf(s) law truncated at L (p(r) proportional to r^-s, inverse-CDF
-    sampling), duplicates are redrawn, and rank r maps to label id perm[r-1]
-    for a seeded permutation perm of [0, L).  Column ids are sorted within a
-    row.
-    """
+def _zipf_draws(B: int, L: int, m: int, seed_no: int, s: float):
+    """Per sample, m distinct Zipf(s) ranks in [0, L) (0 = most frequent),
+    and the seeded permutation that maps rank r to label id perm[r]."""
     if m > L:
         raise ValueError("m > L")
     ranks = np.arange(1, L + 1, dtype=np.float64)
@@ -110,8 +104,7 @@ def zipf_labels(B: int, L: int, m: int, seed_no: int, s: float = 1.1):
     cdf /= cdf[-1]
     perm = _rng(seed_no, T_PERM).permutation(L).astype(np.int64)
     rng = _rng(seed_no, T_POS)
-    rowptr = np.arange(B + 1, dtype=np.int64) * m
-    col = np.empty(B * m, dtype=np.int32)
+    draws = np.empty((B, m), dtype=np.int64)
     for b in range(B):
         chosen: list[int] = []
         seen: set[int] = set()
@@ -124,17 +117,62 @@ def zipf_labels(B: int, L: int, m: int, seed_no: int, s: float = 1.1):
                     chosen.append(x)
                     if len(chosen) == m:
                         break
-        col[b * m:(b + 1) * m] = np.sort(perm[np.asarray(chosen)])
+        draws[b] = chosen
+    return draws, perm
+
+
+def _csr(rows: list) -> tuple:
+    rowptr = np.zeros(len(rows) + 1, dtype=np.int64)
+    rowptr[1:] = np.cumsum([r.size for r in rows])
+    col = np.concatenate(rows).astype(np.int32) if rows and rowptr[-1] else np.zeros(0, np.int32)
     return rowptr.astype(np.int32), col
 
 
-def make_inputs(w, *, dZ: bool = True, labels: bool = True, idx1: bool = False) -> dict:
+def zipf_labels(B: int, L: int, m: int, seed_no: int, s: float = 1.1):
+    """0/1 label matrix B x L as CSR (rowptr int32 [B+1], col int32 [B*m]).
+
+    Every sample gets exactly m distinct labels.  A label is drawn by rank r
+    from a Zipf(s) law truncated at L (p(r) proportional to r^-s, inverse-CDF
+    sampling), duplicates are redrawn, and rank r maps to label id perm[r-1]
+    for a seeded permutation perm of [0, L).  Column ids are sorted within a
+    row.
+    """
+    draws, perm = _zipf_draws(B, L, m, seed_no, s)
+    return _csr([np.sort(perm[d]) for d in draws])
+
+
+def head_tail_labels(B: int, L: int, L_head: int, m: int, seed_no: int, s: float = 1.1):
+    """The labels of zipf_labels(B, L, m, seed_no, s) split into a head (the
+    L_head most frequent ranks, label ids perm[0 .. L_head-1]) and a tail
+    (the other L - L_head ids).  Each part is renumbered in increasing order
+    of the original id.  Returns (head_rowptr, head_col, tail_rowptr,
+    tail_col), CSR with sorted ids per row."""
+    if not 0 < L_head < L:
+        raise ValueError("need 0 < L_head < L")
+    draws, perm = _zipf_draws(B, L, m, seed_no, s)
+    is_head = np.zeros(L, dtype=bool)
+    is_head[perm[:L_head]] = True
+    head_id = np.cumsum(is_head) - 1
+    tail_id = np.cumsum(~is_head) - 1
+    hrows, trows = [], []
+    for d in draws:
+        ids = np.sort(perm[d])
+        hd = is_head[ids]
+        hrows.append(head_id[ids[hd]])
+        trows.append(tail_id[ids[~hd]])
+    return (*_csr(hrows), *_csr(trows))
+
+
+def make_inputs(w, *, dZ: bool = True, labels: bool = True, idx1: bool = False, w_head: bool = False) -> dict:
     """All inputs of one workload `w` (a synthetic.configs.Workload).
 
     Returns a dict of numpy arrays: idx (K x F int32), h (B x H bf16 bits),
     W (L x F bf16 bits), optionally dZ (B x L bf16 bits), y_rowptr / y_col
     (CSR 0/1 labels) and idx1 (L x F int32 per-label index sets for the G=1
-    baseline).
+    baseline).  For the tail workload of a head-tail split (w.head_labels >
+    0) the labels are drawn over the full label space and split: y_* are the
+    tail's, yh_* the head's; w_head adds the head's weights W_head
+    (head_labels x H bf16 bits, N(0, 1/H)).
     """
     out = {
         "idx": sorted_subsets(w.K, w.F, w.H, w.seed_no, T_IDX),
@@ -143,8 +181,18 @@ def make_inputs(w, *, dZ: bool = True, labels: bool = True, idx1: bool = False) 
     }
     if dZ:
         out["dZ"] = normal_bf16(w.B * w.L, 1.0, w.seed_no, T_DZ).reshape(w.B, w.L)
-    if labels:
+    if labels and w.head_labels:
+        # tail workload of a head-tail split: labels drawn over the full
+        # label space, the tail's part as y_*, the head's as yh_*
+        out["yh_rowptr"], out["yh_col"], out["y_rowptr"], out["y_col"] = head_tail_labels(
+            w.B, w.L + w.head_labels, w.head_labels, w.m, w.seed_no, w.zipf_s)
+    elif labels:
         out["y_rowptr"], out["y_col"] = zipf_labels(w.B, w.L, w.m, w.seed_no, w.zipf_s)
+    if w_head:
+        if not w.head_labels:
+            raise ValueError(f"{w.name} has no dense head")
+        out["W_head"] = normal_bf16(w.head_labels * w.H, float(1.0 / np.sqrt(w.H)), w.seed_no,
+                                    T_WHEAD).reshape(w.head_labels, w.H)
     if idx1:
         out["idx1"] = sorted_subsets(w.L, w.F, w.H, w.seed_no, T_IDX1)
     return out

@@ -17,6 +17,10 @@ What pins what:
   torch autograd                dZ, dW, dh, loss == autograd of forward+BCE
   BCE closed form (W = 0)       dZ = s(1/2 - Y), loss = s*B*L*ln 2
   G=1 special case              per-label fixed fan-in dot products
+  head == tail oracle at F = H  dense head (numpy) == group-shared oracle (C) with I_k = [0, H)
+  head BCE closed form (W = 0)  head dZ, dW, dh = 0, loss
+  joint torch autograd          joint head + tail dW_tail, dW_head, dh, loss == autograd
+                                of both branches' BCE with separate scales
 """
 
 from __future__ import annotations
@@ -291,6 +295,85 @@ def pin_g1_per_label(lib):
     _close(O.oracle_bwd_h(dZ, idx1, W, 1, H, lib=lib), dh_ref, what="G1 dh")
 
 
+def _labels_dense(rowptr, col, B, L):
+    Y = np.zeros((B, L))
+    for b in range(B):
+        Y[b, col[rowptr[b]:rowptr[b + 1]]] = 1
+    return Y
+
+
+def pin_head_dense_equals_tail_oracle(lib):
+    """The dense head is the group-shared layer with F = H and every I_k =
+    [0, H): the numpy head oracle equals the C oracle on that layer."""
+    B, H, K, G = 6, 10, 3, 4
+    L = K * G
+    h = normal_bf16(B * H, 1.0, 21, 1).reshape(B, H)
+    W = normal_bf16(L * H, 0.5, 21, 2).reshape(L, H)
+    rowptr = np.array([0, 2, 3, 3, 6, 8, 9], np.int32)
+    col = np.array([0, 11, 4, 1, 2, 7, 5, 9, 3], np.int32)
+    s = 1.0 / B
+    idx = np.tile(np.arange(H, dtype=np.int32), (K, 1))
+    t = O.oracle_step(h, idx, W, rowptr, col, s, G, lib=lib)
+    hd = O.oracle_head_step(h, W, rowptr, col, s, lib=lib)
+    for k in ("Z", "dZ", "dW", "dh"):
+        _close(hd[k], t[k], what=f"head vs tail oracle {k}")
+    assert abs(hd["loss"] - t["loss"]) <= 1e-12 * abs(t["loss"]), "head vs tail oracle loss"
+
+
+def pin_head_zero_weights(lib):
+    """W_head = 0: Z = 0, dZ = s(1/2 - Y), dW = dZ^T h, dh = 0, loss = s*B*L*ln 2."""
+    B, H, L = 5, 7, 9
+    h = normal_bf16(B * H, 1.0, 22, 1).reshape(B, H)
+    W = np.zeros((L, H), np.uint16)
+    rowptr = np.array([0, 1, 4, 4, 5, 7], np.int32)
+    col = np.array([8, 0, 3, 5, 2, 1, 8], np.int32)
+    s = 0.25
+    r = O.oracle_head_step(h, W, rowptr, col, s, lib=lib)
+    Y = _labels_dense(rowptr, col, B, L)
+    dZ = s * (0.5 - Y)
+    _close(r["Z"], np.zeros((B, L)), 0, EXACT, "head0 Z")
+    _close(r["dZ"], dZ, 0, EXACT, "head0 dZ")
+    _close(r["dh"], np.zeros((B, H)), 0, EXACT, "head0 dh")
+    hf = _f(h)
+    dW = np.array([[sum(dZ[b, l] * hf[b, j] for b in range(B)) for j in range(H)] for l in range(L)])
+    _close(r["dW"], dW, 1e-14, 1e-15, "head0 dW")
+    assert abs(r["loss"] - s * B * L * math.log(2.0)) < 1e-12, "head0 loss"
+
+
+def pin_joint_torch_autograd(lib):
+    """Joint head + tail pass == torch autograd (fp64, CPU) of
+    s_t BCE(tail logits, Y_t) + s_h BCE(h W_head^T, Y_h), with the tail as a
+    masked dense L x H matrix (distinct scales pin which branch gets which)."""
+    import torch
+
+    B, H, K, G, F, Lh = 5, 20, 4, 3, 6, 7
+    Lt = K * G
+    h, idx, Wt, _ = _rand_case(B, H, K, G, F, 23)
+    Wh = normal_bf16(Lh * H, 0.5, 23, 7).reshape(Lh, H)
+    yt_rp = np.array([0, 2, 2, 3, 5, 6], np.int32)
+    yt_col = np.array([1, 10, 4, 0, 11, 6], np.int32)
+    yh_rp = np.array([0, 1, 3, 3, 4, 6], np.int32)
+    yh_col = np.array([6, 0, 2, 5, 1, 3], np.int32)
+    st, sh = 0.2, 0.35
+    r = O.oracle_joint_step(h, idx, Wt, yt_rp, yt_col, Wh, yh_rp, yh_col, st, sh, G, lib=lib)
+    ht = torch.tensor(_f(h), requires_grad=True)
+    Wd = torch.zeros(Lt, H, dtype=torch.float64)
+    for l in range(Lt):
+        Wd[l, torch.tensor(idx[l // G].astype(np.int64))] = torch.tensor(_f(Wt)[l])
+    Wd.requires_grad_(True)
+    Wht = torch.tensor(_f(Wh), requires_grad=True)
+    Yt = torch.tensor(_labels_dense(yt_rp, yt_col, B, Lt))
+    Yh = torch.tensor(_labels_dense(yh_rp, yh_col, B, Lh))
+    bce = torch.nn.functional.binary_cross_entropy_with_logits
+    loss = st * bce(ht @ Wd.T, Yt, reduction="sum") + sh * bce(ht @ Wht.T, Yh, reduction="sum")
+    loss.backward()
+    dWt_ref = np.stack([Wd.grad.numpy()[l, idx[l // G]] for l in range(Lt)])
+    _close(r["dW_tail"], dWt_ref, 1e-10, 1e-13, "joint dW_tail")
+    _close(r["dW_head"], Wht.grad.numpy(), 1e-10, 1e-13, "joint dW_head")
+    _close(r["dh"], ht.grad.numpy(), 1e-10, 1e-13, "joint dh")
+    assert abs(r["loss"] - loss.item()) < 1e-10 * abs(loss.item()), "joint loss"
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -303,4 +386,7 @@ ALL_PINS = [
     pin_bce_zero_weights,
     pin_torch_autograd,
     pin_g1_per_label,
+    pin_head_dense_equals_tail_oracle,
+    pin_head_zero_weights,
+    pin_joint_torch_autograd,
 ]

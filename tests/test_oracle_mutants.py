@@ -70,3 +70,38 @@ def test_mutant_is_caught(name):
 
 def test_pristine_oracle_passes_all_pins():
     assert _pins_fail(O.load()) == []
+
+
+# The dense head and the joint pass live in oracle.py (numpy): the same
+# check, on mutated copies of that module.
+PY_SRC = os.path.join(os.path.dirname(O.__file__), "oracle.py")
+PY_MUTANTS = {
+    "head_dw_from_logits": ('"dW": dZ.T @ hf', '"dW": Z.T @ hf'),
+    "head_scale_twice": ("oracle_bce(Z, y_rowptr, y_col, scale, lib=lib)",
+                         "oracle_bce(Z, y_rowptr, y_col, scale * scale, lib=lib)"),
+    "head_dh_negated": ('"dh": dZ @ Wf', '"dh": -(dZ @ Wf)'),
+    "joint_dh_tail_only": ('"dh": t["dh"] + hd["dh"]', '"dh": t["dh"]'),
+    "joint_loss_head_only": ('"loss": t["loss"] + hd["loss"]', '"loss": hd["loss"]'),
+    "joint_scales_swapped": ("yt_col, scale_tail, G, lib=lib)", "yt_col, scale_head, G, lib=lib)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_head_mutant_is_caught(name, monkeypatch):
+    import importlib.util
+
+    old, new = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "oracle_mutant.py")
+        with open(path, "w") as fh:
+            fh.write(src.replace(old, new))
+        spec = importlib.util.spec_from_file_location("oracle_mutant", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        lib = O.load()
+        monkeypatch.setattr(O, "oracle_head_step", mod.oracle_head_step)
+        monkeypatch.setattr(O, "oracle_joint_step", mod.oracle_joint_step)
+        failed = _pins_fail(lib)
+    assert failed, f"mutant {name} passes every pin"
