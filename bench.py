@@ -282,6 +282,103 @@ def sweep_g(args):
             fh.write(line + "\n")
 
 
+def joint_bench(args):
+    """The joint head + tail step of the head-tail split at 3M (haste_joint_step):
+    89,088 dense-head labels and 2,910,848 tail labels (G = 32, F = 64),
+    H = 768, B = 128, ~36 positives per sample drawn over the full label
+    space and split.  One JSON line: joint samples/s, the two branches timed
+    alone, the head pass against HBM bandwidth, and the oracle on the CPU."""
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import get_workload, make_inputs
+
+    w = get_workload("ht3m_tail_shaped")
+    B, H, K, G, F, L, Lh = w.B, w.H, w.K, w.G, w.F, w.L, w.head_labels
+    dev = torch.device("cuda:0")
+    log(f"[joint] generating {w.name}: tail L={L} G={G} F={F}, head {Lh} x {H}, B={B}")
+    d = make_inputs(w, dZ=False, w_head=True)
+    h, idx, Wt, Wh = (bf16_dev(d["h"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev),
+                      bf16_dev(d["W_head"], dev))
+    yt = (i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev))
+    yh = (i32_dev(d["yh_rowptr"], dev), i32_dev(d["yh_col"], dev))
+    s = 1.0 / B
+    out = {"dW_tail": torch.empty(L, F, dtype=torch.float32, device=dev),
+           "dW_head": torch.empty(Lh, H, dtype=torch.float32, device=dev),
+           "dh": torch.empty(B, H, dtype=torch.float32, device=dev), "loss": None}
+    ws = torch.empty(hs.joint_workspace_size(B, H, K, G, F, Lh, args.mode), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ev = HipEvents(4)
+
+    def run():
+        hs.joint_step(h, idx, Wt, *yt, Wh, *yh, s, s, G, mode=args.mode, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    o_t = {"dW": out["dW_tail"], "dh": out["dh"], "Z": None, "loss": None}
+    o_h = {"dW": out["dW_head"], "dh": out["dh"], "Z": None, "loss": None}
+    reps = max(10, args.steps // 2)
+    tail_us = 1e3 * time_call(lambda: hs.step(h, idx, Wt, *yt, s, G, mode=args.mode, out=o_t, workspace=ws),
+                              reps, sh, ev)
+    head_us = 1e3 * time_call(lambda: hs.head_step(h, Wh, *yh, s, out=o_h, workspace=ws), reps, sh, ev)
+    log(f"[joint] step {ms_step:.3f} ms; tail alone {tail_us:.1f} us, head alone {head_us:.1f} us")
+    nnz_h = int(d["yh_rowptr"][-1])
+    # head pass, every compulsory tensor once: W_head, h, head labels in; dW_head, dh out
+    head_bytes = Lh * H * 2 + B * H * 2 + (B + 1) * 4 + nnz_h * 4 + Lh * H * 4 + B * H * 4
+    head_flops = 3 * 2 * B * Lh * H
+    tail_flops = 6 * B * L * F
+    ach = head_bytes / (head_us * 1e-6) / 1e9
+    res = {
+        "metric": "joint head+tail step samples/s (head-tail split, 3M labels)",
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ht3m_joint_shaped", "L_head": Lh, "L_tail": L, "G": G, "K": K, "F": F, "H": H,
+                   "B": B, "positives_per_sample": w.m, "dh_mode": args.mode,
+                   "step": "haste_joint_step: tail haste_step, then the dense head (rocBLAS products + BCE kernel)"},
+        "useful_tflops": round((head_flops + tail_flops) / (ms_step * 1e-3) / 1e12, 2),
+        "branches_us": {"tail_step": round(tail_us, 2), "head_step": round(head_us, 2)},
+        "roofline_head": {"kernel": "head pass (3 rocBLAS GEMMs + BCE + dh sum)", "bound": "hbm",
+                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": head_bytes,
+                          "avg_us": round(head_us, 2), "head_tflops": round(head_flops / (head_us * 1e-6) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        log("[joint] timing the CPU oracle")
+        cb = cpu_baseline(w, d, args.cpu_seconds)
+        t0 = time.perf_counter()
+        O.oracle_head_step(d["h"], d["W_head"], d["yh_rowptr"], d["yh_col"], s)
+        t_head = time.perf_counter() - t0
+        t_all = cb["seconds_per_step"] + t_head
+        res["cpu_baseline"] = {"value": round(B / t_all, 3), "unit": "samples/s", "cores": cb["cores"],
+                               "kind": "oracle",
+                               "sample": cb["sample"] + f"; plus the whole fp64 head pass ({t_head:.2f} s)",
+                               "seconds_per_step": round(t_all, 3)}
+    ev.close()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,19 +400,23 @@ def main():
     ap.add_argument("--sweep-g", action="store_true",
                     help="tail of the head-tail split at 3M (2,910,848 labels): per-G timings for G in "
                          "{16, 32, 64} and the G = 1 baseline, one JSON line")
+    ap.add_argument("--joint", action="store_true",
+                    help="joint head + tail step of the 3M head-tail split (haste_joint_step), one JSON line")
     args = ap.parse_args()
 
     if args.ingest:
         ingest_counters(args.ingest[0], args.ingest[1], args.workload, args.commands)
         return
 
-    if args.sweep_g:
-        return sweep_g(args)
-
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and measured on a single MI355X; "
               "multi-GPU runs are not supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep_g:
+        return sweep_g(args)
+    if args.joint:
+        return joint_bench(args)
 
     import numpy as np
     import torch

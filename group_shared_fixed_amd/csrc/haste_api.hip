@@ -302,7 +302,8 @@ int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t
 namespace {
 
 // Head workspace: Z (B x L fp32), stacked dZ hi / lo (2B x L bf16), [h; h]
-// (2B x H bf16), the stacked dh product (2B x H fp32), rocBLAS's workspace.
+// (2B x H bf16), the stacked dh products of the label chunks (2B x H fp32
+// each), rocBLAS's workspace.
 struct HeadLayout {
     size_t z, dz, hcat, dhcat, blas, total;
     HeadLayout(int64_t B, int64_t H, int64_t L)
@@ -312,7 +313,7 @@ struct HeadLayout {
         dz = z + align256(bl * 4);
         hcat = dz + align256(bl * 4);
         dhcat = hcat + align256(bh * 4);
-        blas = dhcat + align256(bh * 8);
+        blas = dhcat + align256(bh * 8 * (size_t)head_dh_chunks(L));
         total = blas + kHeadBlasWorkspace;
     }
 };

@@ -141,32 +141,28 @@ rocblas_status gemm_rm(rocblas_handle h, bool ta, bool tb, int64_t M, int64_t N,
 
 }  // namespace
 
-// dh = base + top + bottom, with top and bottom the two B x H halves of the
-// stacked product (base = dh when accumulating, else 0).
+// dh = base + sum over the S label chunks of (top + bottom), with top and
+// bottom the two B x H halves of each chunk's stacked product (base = dh
+// when accumulating, else 0), in a fixed order.
 __global__ __launch_bounds__(256) void k_head_dh_sum(const float* __restrict__ part, float* __restrict__ dh, int64_t n,
-                                                     bool accumulate)
+                                                     int S, bool accumulate)
 {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    if (i + 4 <= n && n % 4 == 0) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(part + i);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(part + n + i);
-        f32x4_t r = a + b;
-        if (accumulate) r = *reinterpret_cast<const f32x4_t*>(dh + i) + r;
-        *reinterpret_cast<f32x4_t*>(dh + i) = r;
-    } else {
-        for (int64_t e = i; e < i + 4 && e < n; ++e) {
-            const float r = part[e] + part[n + e];
-            dh[e] = accumulate ? dh[e] + r : r;
-        }
-    }
+    float r = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) r += part[(int64_t)s * 2 * n + i] + part[(int64_t)s * 2 * n + n + i];
+    dh[i] = accumulate ? dh[i] + r : r;
 }
 
 // The head pass on `stream`: Z (B x L fp32, in zbuf), the BCE gradient as a
 // stacked bf16 hi / lo matrix dzcat (2B x L), hcat = [h; h] (2B x H bf16),
-// dW = dzcat^T hcat (L x H fp32), the stacked dh product in dhcat (2B x H
-// fp32) and dh (B x H fp32, added to when accumulate_dh).  Returns false if a
-// rocBLAS call or a copy fails.
+// dW = dzcat^T hcat (L x H fp32), the stacked dh products of the
+// head_dh_chunks(L) label chunks in dhcat (that many 2B x H fp32 blocks) and
+// dh (B x H fp32, added to when accumulate_dh).  The feature-gradient
+// product has a B x H output and an L-deep contraction; splitting the
+// contraction into label chunks (a strided batch of GEMMs) is what spreads
+// it over the chip.  Returns false if a rocBLAS call or a copy fails.
 bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
               float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
               uint16_t* dzcat, uint16_t* hcat, float* dhcat, void* blas_ws, size_t blas_ws_bytes,
@@ -184,12 +180,24 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
                        dzcat, dzcat + B * L, loss, B, L);
     // dW = [hi; lo]^T [h; h] (L x H)
     if (gemm_rm(bh, true, false, L, H, 2 * B, dzcat, L, hcat, H, 0.f, dW, H) != rocblas_status_success) return false;
-    // [dh_hi; dh_lo] = [hi; lo] W (2B x H), then dh (+)= dh_hi + dh_lo
-    if (gemm_rm(bh, false, false, 2 * B, H, L, dzcat, L, W, H, 0.f, dhcat, H) != rocblas_status_success)
+    // per label chunk c: [dh_hi; dh_lo]_c = [hi; lo][:, chunk c] W[chunk c, :] (2B x H)
+    const int64_t Lc = kHeadDhChunk, full = L / Lc, rem = L % Lc;
+    const float one = 1.0f, zero = 0.0f;
+    if (full > 0 &&
+        rocblas_gemm_strided_batched_ex(bh, rocblas_operation_none, rocblas_operation_none, (rocblas_int)H,
+                                        (rocblas_int)(2 * B), (rocblas_int)Lc, &one, W, rocblas_datatype_bf16_r,
+                                        (rocblas_int)H, Lc * H, dzcat, rocblas_datatype_bf16_r, (rocblas_int)L, Lc,
+                                        &zero, dhcat, rocblas_datatype_f32_r, (rocblas_int)H, 2 * B * H, dhcat,
+                                        rocblas_datatype_f32_r, (rocblas_int)H, 2 * B * H, (rocblas_int)full,
+                                        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                                        0) != rocblas_status_success)
+        return false;
+    if (rem > 0 && gemm_rm(bh, false, false, 2 * B, H, rem, dzcat + full * Lc, L, W + full * Lc * H, H, 0.f,
+                           dhcat + full * 2 * B * H, H) != rocblas_status_success)
         return false;
     const int64_t m = B * H;
-    hipLaunchKernelGGL(k_head_dh_sum, dim3((unsigned)(((m + 3) / 4 + 255) / 256)), dim3(256), 0, stream, dhcat, dh, m,
-                       accumulate_dh);
+    hipLaunchKernelGGL(k_head_dh_sum, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, dhcat, dh, m,
+                       (int)head_dh_chunks(L), accumulate_dh);
     return true;
 }
 

@@ -94,5 +94,9 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
               hipStream_t stream);
 // Bytes of caller workspace the head pass hands to rocBLAS.
 constexpr size_t kHeadBlasWorkspace = 64ull << 20;
+// Labels per chunk of the head's split feature-gradient product, and the
+// number of chunks (each leaves a 2B x H fp32 partial in the workspace).
+constexpr int64_t kHeadDhChunk = 1024;
+constexpr int64_t head_dh_chunks(int64_t L) { return (L + kHeadDhChunk - 1) / kHeadDhChunk; }
 
 }  // namespace haste
