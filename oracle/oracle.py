@@ -186,3 +186,67 @@ def oracle_joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_c
     hd = oracle_head_step(h, W_head, yh_rowptr, yh_col, scale_head, lib=lib)
     return {"dW_tail": t["dW"], "dW_head": hd["dW"], "dh": t["dh"] + hd["dh"], "loss": t["loss"] + hd["loss"],
             "tail": t, "head": hd}
+
+
+def oracle_rewire_scores(h, dZ, idx, W, G):
+    """Scores of the group-level rewiring step (HASTE notes, "loss /
+    training strategy": RigL-style dynamic sparse training periodically
+    reselects each group's index set I_k, keeping |I_k| = F; the algorithm
+    itself is not printed, so this follows RigL with the group as the unit).
+      grow[k, j]  = sum_g | sum_b dZ[b, kG+g] h[b, j] |   (K x H): the size of
+                    the dense loss gradient the group's labels would have on
+                    feature column j (RigL's growth criterion, summed over G)
+      prune[k, f] = sum_g | W[kG+g, f] |                  (K x F): the weight
+                    magnitude of slot f (RigL's drop criterion, summed over G)
+    dZ is bf16 bits (B x L); fp64 results."""
+    B, H = h.shape
+    K, F = idx.shape
+    L = K * G
+    _check("h", h, np.uint16, (B, H)); _check("dZ", dZ, np.uint16, (B, L))
+    _check("idx", idx, np.int32, (K, F)); _check("W", W, np.uint16, (L, F))
+    hf, dzf, wf = _bf16_f64(h), _bf16_f64(dZ), _bf16_f64(W)
+    grow = np.empty((K, H))
+    for k in range(K):
+        dense_grad = dzf[:, k * G:(k + 1) * G].T @ hf          # G x H
+        grow[k] = np.abs(dense_grad).sum(axis=0)
+    prune = np.abs(wf).reshape(K, G, F).sum(axis=1)
+    return grow, prune
+
+
+def oracle_rewire_select(idx, W, grow, prune, n_swap, G):
+    """The discrete rewiring phase for every group k, given its scores:
+      1. drop the n_swap slots with the smallest prune score (equal scores:
+         the lower column id is dropped first);
+      2. grow the n_swap columns with the largest grow score among the
+         columns not kept (a dropped column may come back; equal scores:
+         the lower column id first);
+      3. the new I_k is the kept and grown columns in increasing order; a
+         kept column keeps its weights (its W column moves with it), a grown
+         column starts at weight zero.
+    Returns (idx_new K x F int32, W_new L x F bf16 bits)."""
+    K, F = idx.shape
+    H = grow.shape[1]
+    if not 0 <= n_swap <= F:
+        raise ValueError("need 0 <= n_swap <= F")
+    idx_new = np.empty_like(idx)
+    W_new = np.zeros_like(W)
+    for k in range(K):
+        cols = [int(c) for c in idx[k]]
+        by_weight = sorted(range(F), key=lambda f: (prune[k, f], cols[f]))
+        dropped = set(by_weight[:n_swap])
+        kept = {cols[f]: f for f in range(F) if f not in dropped}
+        candidates = [j for j in range(H) if j not in kept]
+        grown = sorted(candidates, key=lambda j: (-grow[k, j], j))[:n_swap]
+        new_cols = sorted(list(kept) + grown)
+        idx_new[k] = new_cols
+        for f_new, c in enumerate(new_cols):
+            if c in kept:
+                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]
+    return idx_new, W_new
+
+
+def oracle_rewire(h, dZ, idx, W, n_swap, G):
+    """Scores, then the selection: (idx_new, W_new, grow, prune)."""
+    grow, prune = oracle_rewire_scores(h, dZ, idx, W, G)
+    idx_new, W_new = oracle_rewire_select(idx, W, grow, prune, n_swap, G)
+    return idx_new, W_new, grow, prune

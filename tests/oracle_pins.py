@@ -21,6 +21,10 @@ What pins what:
   head BCE closed form (W = 0)  head dZ, dW, dh = 0, loss
   joint torch autograd          joint head + tail dW_tail, dW_head, dh, loss == autograd
                                 of both branches' BCE with separate scales
+  rewire scores via autograd    grow score == |dense gradient| (torch autograd) summed per group,
+                                prune score == |W| summed per group (plain loops)
+  rewire brute force            drop / grow sets == the best n-subsets found by enumeration
+  rewire special cases          n = 0 identity, all-slots swap, ties, a planted strongest column
 """
 
 from __future__ import annotations
@@ -374,6 +378,97 @@ def pin_joint_torch_autograd(lib):
     assert abs(r["loss"] - loss.item()) < 1e-10 * abs(loss.item()), "joint loss"
 
 
+def pin_rewire_scores_autograd(lib):
+    """grow[k, j] = sum over the group's labels of |d<dZ, h W_dense^T>/dW_dense[l, j]|
+    with the gradient from torch autograd on a dense L x H weight matrix;
+    prune[k, f] = sum over the group's labels of |W[l, f]| by plain loops."""
+    import torch
+
+    B, H, K, G, F = 6, 14, 3, 4, 5
+    h, idx, W, dZ = _rand_case(B, H, K, G, F, 24)
+    grow, prune = O.oracle_rewire_scores(h, dZ, idx, W, G)
+    Wd = torch.zeros(K * G, H, dtype=torch.float64, requires_grad=True)
+    S = (torch.tensor(_f(dZ)) * (torch.tensor(_f(h)) @ Wd.T)).sum()
+    S.backward()
+    g = Wd.grad.numpy()
+    want = np.array([[sum(abs(g[k * G + i, j]) for i in range(G)) for j in range(H)] for k in range(K)])
+    _close(grow, want, 1e-12, 1e-13, "rewire grow score")
+    wf = _f(W)
+    want_p = np.array([[sum(abs(wf[k * G + i, f]) for i in range(G)) for f in range(F)] for k in range(K)])
+    _close(prune, want_p, 0, EXACT, "rewire prune score")
+
+
+def pin_rewire_brute_force(lib):
+    """With distinct scores the dropped slots are the n-subset of I_k with
+    the smallest total prune score and the grown columns the n-subset of the
+    non-kept columns with the largest total grow score (enumerated)."""
+    import itertools
+
+    rng = np.random.default_rng(25)
+    K, G, F, H = 6, 2, 4, 9
+    for n in (1, 2, 3, 4):
+        idx = np.stack([np.sort(rng.choice(H, F, replace=False)) for _ in range(K)]).astype(np.int32)
+        W = bf16_bits(rng.normal(size=(K * G, F)).astype(np.float32))
+        prune = rng.permutation(K * F).reshape(K, F).astype(np.float64)
+        grow = rng.permutation(K * H).reshape(K, H).astype(np.float64)
+        # make a dropped column the strongest grower in group 0: it must come back
+        f_low = int(np.argmin(prune[0]))
+        grow[0, idx[0, f_low]] = 10.0 * K * H
+        idx_new, W_new = O.oracle_rewire_select(idx, W, grow, prune, n, G)
+        for k in range(K):
+            cols = list(idx[k])
+            drop = min(itertools.combinations(range(F), n), key=lambda c: sum(prune[k, f] for f in c))
+            kept = [cols[f] for f in range(F) if f not in drop]
+            cand = [j for j in range(H) if j not in kept]
+            add = max(itertools.combinations(cand, n), key=lambda c: sum(grow[k, j] for j in c))
+            want = sorted(kept + list(add))
+            assert list(idx_new[k]) == want, f"rewire brute force n={n} k={k}: {list(idx_new[k])} vs {want}"
+            for f_new, c in enumerate(want):
+                src = W[k * G:(k + 1) * G, cols.index(c)] if c in kept else np.zeros(G, np.uint16)
+                assert (W_new[k * G:(k + 1) * G, f_new] == src).all(), f"rewire weights n={n} k={k} col {c}"
+        assert idx[0, f_low] in idx_new[0], "a dropped column with the top grow score must be regrown"
+
+
+def pin_rewire_special_cases(lib):
+    """n = 0 changes nothing; n = F with H = F regrows every column at zero
+    weight; equal scores drop and grow the lowest column ids; a planted
+    feature/gradient pair makes one column the strongest grower."""
+    B, H, K, G, F = 5, 12, 3, 4, 4
+    h, idx, W, dZ = _rand_case(B, H, K, G, F, 26)
+    i0, w0, _, _ = O.oracle_rewire(h, dZ, idx, W, 0, G)
+    assert (i0 == idx).all() and (w0 == W).all(), "n = 0 must be the identity"
+    # H = F: the only candidates are the dropped columns themselves
+    idx_d = np.tile(np.arange(F, dtype=np.int32), (K, 1))
+    hd = h[:, :F].copy()
+    i1, w1, _, _ = O.oracle_rewire(hd, dZ, idx_d, W, F, G)
+    assert (i1 == idx_d).all() and (w1 == 0).all(), "full swap at H = F"
+    # ties: equal prune and grow scores everywhere
+    prune = np.ones((K, F))
+    grow = np.ones((K, H))
+    i2, w2 = O.oracle_rewire_select(idx, W, grow, prune, 2, G)
+    for k in range(K):
+        kept = sorted(idx[k])[2:]
+        add = [j for j in range(H) if j not in kept][:2]
+        assert list(i2[k]) == sorted(kept + add), f"tie-break, group {k}"
+    # planted case: only label 1 of group 1 has a gradient, and only through
+    # feature column j*, which group 1 does not use; slot 2 of group 1 has
+    # the smallest weights
+    jstar = [j for j in range(H) if j not in idx[1]][0]
+    hp = np.zeros((B, H), np.uint16)
+    hp[:, jstar] = bf16_bits(np.full(B, 2.0, np.float32))
+    hp[:, (jstar + 1) % H] = bf16_bits(np.full(B, 0.5, np.float32))
+    dZp = np.zeros_like(dZ)
+    dZp[:, 1 * G + 1] = bf16_bits(np.linspace(0.5, 1.5, B).astype(np.float32))
+    Wp = bf16_bits(np.full((K * G, F), 1.0, np.float32))
+    Wp[1 * G:2 * G, 2] = bf16_bits(np.full(G, 0.125, np.float32))
+    i3, w3, grow3, _ = O.oracle_rewire(hp, dZp, idx, Wp, 1, G)
+    assert abs(grow3[1, jstar] - 2.0 * np.linspace(0.5, 1.5, B).astype(np.float32).astype(np.float64).sum()) < 1e-9
+    want = sorted([c for f, c in enumerate(idx[1]) if f != 2] + [jstar])
+    assert list(i3[1]) == want, "planted strongest column must replace the weakest slot"
+    f_new = want.index(jstar)
+    assert (w3[G:2 * G, f_new] == 0).all() and (w3[G:2 * G] != 0).sum() == G * (F - 1)
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -389,4 +484,7 @@ ALL_PINS = [
     pin_head_dense_equals_tail_oracle,
     pin_head_zero_weights,
     pin_joint_torch_autograd,
+    pin_rewire_scores_autograd,
+    pin_rewire_brute_force,
+    pin_rewire_special_cases,
 ]

@@ -49,7 +49,7 @@ def _pins_fail(lib):
     for pin in ALL_PINS:
         try:
             pin(lib)
-        except AssertionError:
+        except Exception:  # a wrong value, or an error a mutant's output triggers
             failed.append(pin.__name__)
     return failed
 
@@ -83,6 +83,19 @@ PY_MUTANTS = {
     "joint_dh_tail_only": ('"dh": t["dh"] + hd["dh"]', '"dh": t["dh"]'),
     "joint_loss_head_only": ('"loss": t["loss"] + hd["loss"]', '"loss": hd["loss"]'),
     "joint_scales_swapped": ("yt_col, scale_tail, G, lib=lib)", "yt_col, scale_head, G, lib=lib)"),
+    "rewire_grow_signed": ("grow[k] = np.abs(dense_grad).sum(axis=0)", "grow[k] = dense_grad.sum(axis=0)"),
+    "rewire_grow_abs_after_sum": ("grow[k] = np.abs(dense_grad).sum(axis=0)",
+                                  "grow[k] = np.abs(dense_grad.sum(axis=0))"),
+    "rewire_prune_signed": ("prune = np.abs(wf).reshape(K, G, F).sum(axis=1)", "prune = wf.reshape(K, G, F).sum(axis=1)"),
+    "rewire_drop_strongest": ("dropped = set(by_weight[:n_swap])", "dropped = set(by_weight[F - n_swap:])"),
+    "rewire_grow_weakest": ("key=lambda j: (-grow[k, j], j))[:n_swap]", "key=lambda j: (grow[k, j], j))[:n_swap]"),
+    "rewire_tie_high_id": ("key=lambda j: (-grow[k, j], j))[:n_swap]", "key=lambda j: (-grow[k, j], -j))[:n_swap]"),
+    "rewire_no_regrow_of_dropped": ("candidates = [j for j in range(H) if j not in kept]",
+                                    "candidates = [j for j in range(H) if j not in cols]"),
+    "rewire_weights_stay_in_slot": ("W[k * G:(k + 1) * G, kept[c]]", "W[k * G:(k + 1) * G, f_new]"),
+    "rewire_grown_keep_old_weight": (
+        "            if c in kept:\n                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]",
+        "            W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept.get(c, f_new)]"),
 }
 
 
@@ -103,5 +116,7 @@ def test_head_mutant_is_caught(name, monkeypatch):
         lib = O.load()
         monkeypatch.setattr(O, "oracle_head_step", mod.oracle_head_step)
         monkeypatch.setattr(O, "oracle_joint_step", mod.oracle_joint_step)
+        for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire"):
+            monkeypatch.setattr(O, fn, getattr(mod, fn))
         failed = _pins_fail(lib)
     assert failed, f"mutant {name} passes every pin"
