@@ -379,6 +379,100 @@ def joint_bench(args):
             fh.write(line + "\n")
 
 
+def rewire_bench(args):
+    """Group-level rewiring (haste_rewire) on the Amazon-3M shape: K =
+    93,748 groups of G = 32, F = 64, H = 768, B = 128, dZ ~ N(0, 1) bf16,
+    --n-swap slots per group (default 16).  One JSON line: calls/s, the
+    score kernel against the bf16 matrix-core peak and the selection kernel
+    against HBM bandwidth (HIP events on the launch stream), and the oracle
+    on the CPU."""
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import get_workload, make_inputs
+
+    w = get_workload("amazon3m_shaped")
+    B, H, K, G, F, L = w.B, w.H, w.K, w.G, w.F, w.L
+    n = args.n_swap
+    dev = torch.device("cuda:0")
+    log(f"[rewire] generating {w.name}: L={L} G={G} K={K} F={F} H={H} B={B}, n_swap={n}")
+    d = make_inputs(w, dZ=True, labels=False)
+    h, dZ, idx, W = bf16_dev(d["h"], dev), bf16_dev(d["dZ"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev)
+    idx_o, W_o = torch.empty_like(idx), torch.empty_like(W)
+    ws = torch.empty(hs.rewire_workspace_size(B, H, K, G, F), dtype=torch.uint8, device=dev)
+    ev = HipEvents(4 * args.steps + 2)
+
+    def run(i=None):
+        hs.rewire(h, dZ, idx, W, G, n, idx_out=idx_o, W_out=W_o, workspace=ws,
+                  events=None if i is None else ev.block(4 * i, 4))
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+
+    def avg(a, b):
+        return sum(ev.ms(4 * i + a, 4 * i + b) for i in range(args.steps)) / args.steps
+
+    score_us, select_us = 1e3 * avg(1, 2), 1e3 * avg(2, 3)
+    flops = 2 * B * L * H                       # the dense gradient dZ^T h
+    score_bytes = B * L * 2 + B * H * 2 + K * H * 4
+    select_bytes = K * H * 4 + 2 * (L * F * 2 + K * F * 4)
+    tf = flops / (score_us * 1e-6) / 1e12
+    sel_gbs = select_bytes / (select_us * 1e-6) / 1e9
+    log(f"[rewire] {ms:.3f} ms per call; score {score_us:.1f} us ({tf:.0f} TFLOP/s), select {select_us:.1f} us")
+    res = {
+        "metric": "group-level rewiring calls/s (haste_rewire, Amazon-3M shape)",
+        "value": round(1e3 / ms, 2), "unit": "calls/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "L": L, "G": G, "K": K, "F": F, "H": H, "B": B, "n_swap": n,
+                   "step": "haste_rewire: grow scores (dense dZ^T h on matrix cores) + per-group selection"},
+        "kernels_us": {"prep_us": round(1e3 * avg(0, 1), 2), "score_us": round(score_us, 2),
+                       "select_us": round(select_us, 2)},
+        "roofline": {"kernel": "k_rewire_score (dense gradient, |.| summed per group)", "bound": "mfma",
+                     "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "algorithmic_flops": flops,
+                     "algorithmic_bytes": score_bytes, "avg_us": round(score_us, 2)},
+        "roofline_other": {"kernel": "k_rewire_select", "bound": "hbm", "achieved": round(sel_gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": None, "algorithmic_bytes": select_bytes, "avg_us": round(select_us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        log("[rewire] timing the CPU oracle")
+        per, done = 256, 0
+        t0 = time.perf_counter()
+        while done < K and time.perf_counter() - t0 < args.cpu_seconds:
+            k0, k1 = done, min(K, done + per)
+            idx_s = np.ascontiguousarray(d["idx"][k0:k1])
+            W_s = np.ascontiguousarray(d["W"][k0 * G:k1 * G])
+            dZ_s = np.ascontiguousarray(d["dZ"][:, k0 * G:k1 * G])
+            O.oracle_rewire(d["h"], dZ_s, idx_s, W_s, n, G)
+            done = k1
+        el = time.perf_counter() - t0
+        t_full = el * K / done
+        res["cpu_baseline"] = {"value": round(1.0 / t_full, 5), "unit": "calls/s", "cores": O.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"oracle rewiring (numpy fp64 scores, Python selection) on groups "
+                                         f"[0, {done}) of {K}; {el:.1f} s wall, extrapolated x{K / done:.1f}",
+                               "seconds_per_call": round(t_full, 2)}
+    ev.close()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +496,9 @@ def main():
                          "{16, 32, 64} and the G = 1 baseline, one JSON line")
     ap.add_argument("--joint", action="store_true",
                     help="joint head + tail step of the 3M head-tail split (haste_joint_step), one JSON line")
+    ap.add_argument("--rewire", action="store_true",
+                    help="group-level rewiring (haste_rewire) on the Amazon-3M shape, one JSON line")
+    ap.add_argument("--n-swap", type=int, default=16, help="with --rewire: slots replaced per group")
     args = ap.parse_args()
 
     if args.ingest:
@@ -417,6 +514,8 @@ def main():
         return sweep_g(args)
     if args.joint:
         return joint_bench(args)
+    if args.rewire:
+        return rewire_bench(args)
 
     import numpy as np
     import torch

@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     head_workspace_size,
     joint_step,
     joint_workspace_size,
+    rewire,
+    rewire_workspace_size,
     step,
     validate_idx,
     validate_labels,

@@ -41,6 +41,9 @@ SIGNATURES = {
     "haste_joint_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _M]),
     "haste_joint_step": (_M, [_P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _M,
                               _P, _S, _P]),
+    "haste_rewire_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "haste_rewire": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
     "haste_validate_idx": (_M, [_P, _I, _I, _I, _P, _P]),
     "haste_validate_labels": (_M, [_P, _P, _I, _I, _P, _P]),
     "haste_status_string": (ctypes.c_char_p, [_M]),
@@ -316,6 +319,36 @@ def joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_col, sca
         _ptr(yh_col), float(scale_tail), float(scale_head), _ptr(out["dW_tail"]), _ptr(out["dW_head"]),
         _ptr(out["dh"]), _ptr(out.get("loss")), B, H, K, G, F, L, m, _ptr(ws), ws.numel(), _stream(h, stream)))
     return out
+
+
+def rewire_workspace_size(B, H, K, G, F) -> int:
+    return int(lib().haste_rewire_workspace_size(B, H, K, G, F))
+
+
+def rewire(h, dZ, idx, W, G, n_swap, idx_out=None, W_out=None, want_scores=False, workspace=None, stream=None,
+           events=None):
+    """Group-level rewiring.  Returns dict(idx, W, grow, prune); idx_out /
+    W_out may be idx / W (in place).  events: optional ctypes array of 4
+    hipEvent_t handles (haste_rewire_timed)."""
+    torch = _torch()
+    _bits(h); _bits(dZ); _bits(W); _i32(idx)
+    B, H = h.shape
+    K, F = idx.shape
+    if idx_out is None:
+        idx_out = torch.empty_like(idx)
+    if W_out is None:
+        W_out = torch.empty_like(W)
+    grow = torch.empty(K, H, dtype=torch.float32, device=h.device) if want_scores else None
+    prune = torch.empty(K, F, dtype=torch.float32, device=h.device) if want_scores else None
+    n = rewire_workspace_size(B, H, K, G, F)
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=h.device)
+    args = (_ptr(h), _ptr(dZ), _ptr(idx), _ptr(W), int(n_swap), _ptr(idx_out), _ptr(W_out), _ptr(grow), _ptr(prune),
+            B, H, K, G, F, _ptr(ws), ws.numel(), _stream(h, stream))
+    if events is None:
+        _check("haste_rewire", lib().haste_rewire(*args))
+    else:
+        _check("haste_rewire_timed", lib().haste_rewire_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+    return {"idx": idx_out, "W": W_out, "grow": grow, "prune": prune}
 
 
 def validate_idx(idx, H, stream=None) -> int:

@@ -401,6 +401,65 @@ int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
                      stream);
 }
 
+size_t haste_rewire_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F)
+{
+    (void)G;
+    (void)F;
+    if (B < 1 || H < 1 || K < 1) return 0;
+    return align256((size_t)H * (size_t)round_up(B, 32) * 2) + align256((size_t)K * (size_t)H * 4);
+}
+
+namespace {
+
+// true when [a, a + na) and [b, b + nb) are the same range or disjoint
+bool same_or_disjoint(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return (x == y && na == nb) || x + na <= y || y + nb <= x;
+}
+
+}  // namespace
+
+int haste_rewire_timed(const haste_bf16* h, const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W,
+                       int64_t n_swap, int32_t* idx_out, haste_bf16* W_out, float* grow_score, float* prune_score,
+                       int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    if (!h || !dZ || !idx || !W || !idx_out || !W_out) return HASTE_ERR_NULL;
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (n_swap < 0 || n_swap > F) return HASTE_ERR_DIM;
+    if (B > 256) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(dZ) || !aligned16(idx) || !aligned16(W) || !aligned16(idx_out) ||
+        !aligned16(W_out) || (grow_score && !aligned16(grow_score)) || (prune_score && !aligned16(prune_score)))
+        return HASTE_ERR_ALIGN;
+    const size_t nidx = (size_t)K * (size_t)F * 4, nw = (size_t)K * (size_t)G * (size_t)F * 2;
+    if (!same_or_disjoint(idx, nidx, idx_out, nidx) || !same_or_disjoint(W, nw, W_out, nw)) return HASTE_ERR_DIM;
+    HASTE_TRY(check_ws(workspace, workspace_bytes, haste_rewire_workspace_size(B, H, K, G, F)));
+    const int64_t Bp = round_up(B, 32);
+    uint16_t* hT = (uint16_t*)workspace;
+    float* grow = grow_score ? grow_score : (float*)((char*)workspace + align256((size_t)H * (size_t)Bp * 2));
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord(events[i], stream);
+    };
+    mark(0);
+    launch_transpose_h(h, hT, B, H, Bp, stream);
+    mark(1);
+    if (!launch_rewire_score(hT, Bp, B, H, dZ, K * G, (int)G, grow, stream)) return HASTE_ERR_UNSUPPORTED;
+    mark(2);
+    if (!launch_rewire_select((int)G, (int)F, idx, W, grow, K, H, (int)n_swap, idx_out, W_out, prune_score, stream))
+        return HASTE_ERR_UNSUPPORTED;
+    mark(3);
+    return hip_status();
+}
+
+int haste_rewire(const haste_bf16* h, const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, int64_t n_swap,
+                 int32_t* idx_out, haste_bf16* W_out, float* grow_score, float* prune_score, int64_t B, int64_t H,
+                 int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return haste_rewire_timed(h, dZ, idx, W, n_swap, idx_out, W_out, grow_score, prune_score, B, H, K, G, F,
+                              workspace, workspace_bytes, stream, nullptr);
+}
+
 const char* haste_status_string(int status)
 {
     switch (status) {

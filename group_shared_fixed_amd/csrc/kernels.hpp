@@ -99,4 +99,12 @@ constexpr size_t kHeadBlasWorkspace = 64ull << 20;
 constexpr int64_t kHeadDhChunk = 1024;
 constexpr int64_t head_dh_chunks(int64_t L) { return (L + kHeadDhChunk - 1) / kHeadDhChunk; }
 
+// Rewiring (dynamic sparse training): grow[k, j] = sum over group k's labels
+// of |(dZ^T h)[l, j]| from hT (H x Bp, Bp = 32 * (1..8)) and bf16 dZ; then
+// the per-group selection (idx_out / W_out may alias idx / W).
+bool launch_rewire_score(const uint16_t* hT, int64_t Bp, int64_t B, int64_t H, const uint16_t* dZ, int64_t L, int G,
+                         float* grow, hipStream_t s);
+bool launch_rewire_select(int G, int F, const int32_t* idx, const uint16_t* W, const float* grow, int64_t K,
+                          int64_t H, int n_swap, int32_t* idx_out, uint16_t* W_out, float* prune_out, hipStream_t s);
+
 }  // namespace haste

@@ -203,6 +203,39 @@ int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
                      int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head, int dh_mode,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Group-level rewiring of the index sets: the discrete phase of the dynamic
+ * sparse training ("loss / training strategy" section: every so many steps
+ * the group-level I_k are reselected RigL-style with |I_k| = F kept; the
+ * algorithm is not printed, so RigL's steps are taken per group):
+ *   grow[k, j]  = sum_g | sum_b dZ[b, kG+g] h[b, j] |   (K x H fp32): the
+ *                 dense loss gradient's size on feature column j;
+ *   prune[k, f] = sum_g | W[kG+g, f] |                 (K x F fp32);
+ *   drop the n_swap slots with the smallest prune score, grow the n_swap
+ *   columns with the largest grow score among those not kept (a dropped
+ *   column may return), equal scores going to the lower column id; the new
+ *   row of idx_out is sorted ascending, a kept column's weights move with it
+ *   in W_out and a grown column's weights are zero.
+ * h: B x H bf16; dZ: B x L bf16 (e.g. from haste_fwd_bce); idx / W as in
+ * haste_fwd; 0 <= n_swap <= F.  idx_out (K x F int32) and W_out (L x F bf16)
+ * may be idx and W themselves (in place) or must not overlap them.
+ * grow_score (K x H) and prune_score (K x F) are optional fp32 outputs.
+ * Scores are fp32 (matrix-core products, fixed summation order), so the
+ * result is bitwise repeatable; the selection is exact given the scores.
+ * Limits: G in {16, 32, 64}, F in {32, 64, 128}, F <= H <= 1024, B <= 256.
+ * Workspace: haste_rewire_workspace_size(B, H, K, G, F) bytes (hT and the
+ * K x H grow scores). */
+size_t haste_rewire_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F);
+int haste_rewire(const haste_bf16* h, const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, int64_t n_swap,
+                 int32_t* idx_out, haste_bf16* W_out, float* grow_score, float* prune_score, int64_t B, int64_t H,
+                 int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* haste_rewire with timing events (events NULL: no events).  events[0..3]
+ * are recorded on `stream` before the feature-major copy of h, before the
+ * score kernel, before the selection kernel and after it. */
+int haste_rewire_timed(const haste_bf16* h, const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W,
+                       int64_t n_swap, int32_t* idx_out, haste_bf16* W_out, float* grow_score, float* prune_score,
+                       int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* Count (into *bad, a device int32 the call zeroes first) the index rows
  * that have an entry outside [0, H) or are not strictly increasing. */
 int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad,
