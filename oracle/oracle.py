@@ -250,3 +250,81 @@ def oracle_rewire(h, dZ, idx, W, n_swap, G):
     grow, prune = oracle_rewire_scores(h, dZ, idx, W, G)
     idx_new, W_new = oracle_rewire_select(idx, W, grow, prune, n_swap, G)
     return idx_new, W_new, grow, prune
+
+
+# ---------------------------------------------------------------- FP8 weights
+#
+# HASTE notes, "limitations": combining the layer with FP8 quantisation is
+# the named next step.  The reading here: W is stored as OCP FP8 E4M3 codes
+# (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities, the
+# all-ones magnitude is NaN, largest finite 448) with one power-of-two scale
+# 2^e_k per label group; the layer then computes exactly what the bf16 layer
+# computes on the dequantized weights.
+
+def e4m3_decode(codes):
+    """E4M3 codes (uint8) -> fp64 values, from the format's definition."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.ldexp(1.0, e - 10))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x):
+    """fp64 values with |x| <= 448 -> E4M3 codes (uint8), rounded to nearest
+    with ties to the even code.  Normal range (|x| >= 2^-6): 3 fraction bits
+    of |x| = q 2^(E-3), q in [8, 16], code = 8 (E + 6) + q (q = 16 carries into
+    the next binade); below it, n = |x| 2^9 rounded, code = n."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 448.0) or np.any(np.isnan(a)):
+        raise ValueError("value outside the E4M3 range")
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f 2^ex, f in [0.5, 1)
+    E = ex - 1                                           # a = 1.xxx 2^E
+    normal = a >= 2.0 ** -6
+    q = np.rint(np.ldexp(a, 3 - E))                      # exact scaling, rint = ties to even
+    code_n = 8 * (E + 6) + q
+    code_s = np.rint(np.ldexp(a, 9))
+    code = np.where(normal, code_n, code_s).astype(np.int64)
+    code |= np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def w8_group_exponent(W, G):
+    """Per group k, the smallest integer e_k with max |W_k| 2^-e_k <= 448
+    (0 for an all-zero group), clamped to [-120, 120]."""
+    K = W.shape[0] // G
+    mx = np.abs(_bf16_f64(W)).reshape(K, -1).max(axis=1)
+    e = np.zeros(K, dtype=np.int64)
+    nz = mx > 0
+    e[nz] = np.ceil(np.log2(mx[nz] / 448.0)).astype(np.int64)
+    # log2 of an exact ratio: confirm the integer against the condition itself
+    for k in np.nonzero(nz)[0]:
+        while np.ldexp(mx[k], -int(e[k])) > 448.0:
+            e[k] += 1
+        while np.ldexp(mx[k], -(int(e[k]) - 1)) <= 448.0:
+            e[k] -= 1
+    return np.clip(e, -120, 120).astype(np.int32)
+
+
+def oracle_quantize_w8(W, G):
+    """bf16 W (L x F bits) -> (W8 L x F uint8 E4M3 codes, wexp K int32):
+    code = encode(W 2^-e_k) for the labels of group k."""
+    L, F = W.shape
+    _check("W", W, np.uint16, (L, F))
+    wexp = w8_group_exponent(W, G)
+    scaled = _bf16_f64(W) * np.ldexp(1.0, -np.repeat(wexp, G).astype(np.int64))[:, None]
+    return e4m3_encode(scaled), wexp
+
+
+def oracle_dequantize_w8(W8, wexp, G):
+    """(W8, wexp) -> bf16 bits of decode(code) 2^e_k (exact in bf16)."""
+    vals = e4m3_decode(W8) * np.ldexp(1.0, np.repeat(wexp, G).astype(np.int64))[:, None]
+    f32 = vals.astype(np.float32)
+    bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    back = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if not np.array_equal(back, vals):
+        raise ValueError("dequantized weight not exact in bf16")
+    return bits

@@ -25,6 +25,11 @@ What pins what:
                                 prune score == |W| summed per group (plain loops)
   rewire brute force            drop / grow sets == the best n-subsets found by enumeration
   rewire special cases          n = 0 identity, all-slots swap, ties, a planted strongest column
+  E4M3 codec vs torch           decode of all 256 codes and encode of random, midpoint and
+                                subnormal values == torch.float8_e4m3fn (a library routine)
+  E4M3 hand values              codes of 1, 448, 2^-9, -2, ties to even
+  FP8 group scales              e_k minimal, dequantized weights exact in bf16, within the
+                                format's rounding bound of W, and encoding back to their codes
 """
 
 from __future__ import annotations
@@ -469,6 +474,67 @@ def pin_rewire_special_cases(lib):
     assert (w3[G:2 * G, f_new] == 0).all() and (w3[G:2 * G] != 0).sum() == G * (F - 1)
 
 
+def pin_e4m3_codec_torch(lib):
+    """The E4M3 codec against torch's float8_e4m3fn conversion (CPU)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "E4M3 NaN codes"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]), "E4M3 decode"
+    rng = np.random.default_rng(27)
+    finite = np.sort(np.unique(got[fin & (got >= 0)]))
+    mids = (finite[1:] + finite[:-1]) / 2                      # exact ties
+    vals = np.concatenate([
+        rng.uniform(-448, 448, 4000), rng.normal(0, 1, 4000), rng.normal(0, 2.0 ** -7, 2000),
+        mids, -mids, finite, -finite, [0.0, -0.0, 448.0, -448.0],
+    ]).astype(np.float32).astype(np.float64)                   # fp32-exact inputs
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    enc = O.e4m3_encode(vals)
+    bad = np.nonzero(enc != want)[0]
+    assert bad.size == 0, f"E4M3 encode: {bad.size} differ, e.g. {vals[bad[:3]]} -> {enc[bad[:3]]} vs {want[bad[:3]]}"
+
+
+def pin_e4m3_hand_values(lib):
+    """1 = 0x38, 448 = 0x7E, 2^-9 = 0x01, 2^-6 = 0x08, -2 = 0xC0, 0 = 0x00;
+    1.0625 lies halfway between 1 (0x38) and 1.125 (0x39): the even code
+    0x38; 1.1875 halfway between 0x39 and 0x3A (1.25): 0x3A."""
+    vals = np.array([1.0, 448.0, 2.0 ** -9, 2.0 ** -6, -2.0, 0.0, 1.0625, 1.1875])
+    want = np.array([0x38, 0x7E, 0x01, 0x08, 0xC0, 0x00, 0x38, 0x3A], np.uint8)
+    assert np.array_equal(O.e4m3_encode(vals), want), "E4M3 hand values"
+    assert np.array_equal(O.e4m3_decode(want[:6]), vals[:6]), "E4M3 hand decode"
+
+
+def pin_w8_group_scales(lib):
+    """e_k is the smallest integer with max|W_k| 2^-e_k <= 448; the
+    dequantized weights are exact bf16 values within the E4M3 rounding bound
+    of W (relative 2^-4 in the normal range, 2^(e_k-10) absolute below)."""
+    K, G, F = 40, 16, 32
+    rng = np.random.default_rng(28)
+    mag = 2.0 ** rng.integers(-12, 12, size=K)
+    W = bf16_bits((rng.normal(size=(K * G, F)) * np.repeat(mag, G)[:, None]).astype(np.float32))
+    W[:G] = 0                                                  # an all-zero group
+    W8, e = O.oracle_quantize_w8(W, G)
+    wf = _f(W)
+    mx = np.abs(wf).reshape(K, -1).max(axis=1)
+    for k in range(K):
+        if mx[k] == 0:
+            assert e[k] == 0
+            continue
+        assert mx[k] * 2.0 ** -int(e[k]) <= 448.0 < mx[k] * 2.0 ** -(int(e[k]) - 1), f"group {k} exponent"
+    deq = _f(O.oracle_dequantize_w8(W8, e, G))
+    sc = np.repeat(2.0 ** e.astype(np.float64), G)[:, None]
+    normal = np.abs(wf) >= 2.0 ** -6 * sc
+    err = np.abs(deq - wf)
+    assert (err[normal] <= 2.0 ** -4 * np.abs(wf[normal])).all(), "normal-range rounding bound"
+    assert (err[~normal] <= (2.0 ** -10 * sc + 0 * wf)[~normal]).all(), "subnormal-range rounding bound"
+    # with the same exponents the dequantized weights encode back to the same codes
+    again = O.e4m3_encode(deq / sc)
+    assert (again == W8).all(), "codes do not round-trip"
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -487,4 +553,7 @@ ALL_PINS = [
     pin_rewire_scores_autograd,
     pin_rewire_brute_force,
     pin_rewire_special_cases,
+    pin_e4m3_codec_torch,
+    pin_e4m3_hand_values,
+    pin_w8_group_scales,
 ]

@@ -93,6 +93,14 @@ PY_MUTANTS = {
     "rewire_no_regrow_of_dropped": ("candidates = [j for j in range(H) if j not in kept]",
                                     "candidates = [j for j in range(H) if j not in cols]"),
     "rewire_weights_stay_in_slot": ("W[k * G:(k + 1) * G, kept[c]]", "W[k * G:(k + 1) * G, f_new]"),
+    "e4m3_ties_away": ("    q = np.rint(np.ldexp(a, 3 - E))", "    q = np.floor(np.ldexp(a, 3 - E) + 0.5)"),
+    "e4m3_bias": ("    code_n = 8 * (E + 6) + q", "    code_n = 8 * (E + 7) + q"),
+    "e4m3_subnormal_step": ("    code_s = np.rint(np.ldexp(a, 9))", "    code_s = np.rint(np.ldexp(a, 8))"),
+    "e4m3_decode_mantissa": ("np.where(e == 0, m * 2.0 ** -9, (8.0 + m)", "np.where(e == 0, m * 2.0 ** -9, (7.0 + m)"),
+    "w8_scale_inverted": ("scaled = _bf16_f64(W) * np.ldexp(1.0, -np.repeat(wexp, G)",
+                          "scaled = _bf16_f64(W) * np.ldexp(1.0, 0 * np.repeat(wexp, G)"),
+    "w8_exponent_one_high": ("    return np.clip(e, -120, 120).astype(np.int32)",
+                             "    return np.clip(e + 1, -120, 120).astype(np.int32)"),
     "rewire_grown_keep_old_weight": (
         "            if c in kept:\n                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]",
         "            W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept.get(c, f_new)]"),
@@ -116,7 +124,8 @@ def test_head_mutant_is_caught(name, monkeypatch):
         lib = O.load()
         monkeypatch.setattr(O, "oracle_head_step", mod.oracle_head_step)
         monkeypatch.setattr(O, "oracle_joint_step", mod.oracle_joint_step)
-        for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire"):
+        for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire", "e4m3_decode", "e4m3_encode",
+                   "w8_group_exponent", "oracle_quantize_w8", "oracle_dequantize_w8"):
             monkeypatch.setattr(O, fn, getattr(mod, fn))
         failed = _pins_fail(lib)
     assert failed, f"mutant {name} passes every pin"
