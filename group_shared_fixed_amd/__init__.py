@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     fixed_fwd,
     fwd,
     fwd_bce,
+    fwd_w8,
     head_step,
     head_workspace_size,
     joint_step,
@@ -21,6 +22,8 @@ from .binding import (  # noqa: F401
     rewire,
     rewire_workspace_size,
     step,
+    step_w8,
+    quantize_w8,
     validate_idx,
     validate_labels,
     workspace_size,

@@ -41,6 +41,11 @@ SIGNATURES = {
     "haste_joint_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _M]),
     "haste_joint_step": (_M, [_P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _M,
                               _P, _S, _P]),
+    "haste_quantize_w8": (_M, [_P, _P, _P, _I, _I, _I, _P]),
+    "haste_fwd_w8": (_M, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "haste_step_w8": (_M, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
+    "haste_step_w8_timed": (_M, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P,
+                                 _P]),
     "haste_rewire_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "haste_rewire": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
@@ -318,6 +323,67 @@ def joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_col, sca
         _ptr(h), _ptr(idx), _ptr(W_tail), _ptr(yt_rowptr), _ptr(yt_col), _ptr(W_head), _ptr(yh_rowptr),
         _ptr(yh_col), float(scale_tail), float(scale_head), _ptr(out["dW_tail"]), _ptr(out["dW_head"]),
         _ptr(out["dh"]), _ptr(out.get("loss")), B, H, K, G, F, L, m, _ptr(ws), ws.numel(), _stream(h, stream)))
+    return out
+
+
+def _u8(t):
+    torch = _torch()
+    if t.dtype != torch.uint8 or not t.is_contiguous():
+        raise TypeError("FP8 codes must be a contiguous uint8 tensor")
+    return t
+
+
+def quantize_w8(W, G, W8=None, wexp=None, stream=None):
+    """bf16 W (L x F) -> (W8 uint8 E4M3 codes L x F, wexp int32 K)."""
+    torch = _torch()
+    _bits(W)
+    L, F = W.shape
+    K = L // G
+    if W8 is None:
+        W8 = torch.empty(L, F, dtype=torch.uint8, device=W.device)
+    if wexp is None:
+        wexp = torch.empty(K, dtype=torch.int32, device=W.device)
+    _check("haste_quantize_w8", lib().haste_quantize_w8(_ptr(W), _ptr(W8), _ptr(wexp), K, G, F, _stream(W, stream)))
+    return W8, wexp
+
+
+def fwd_w8(h, idx, W8, wexp, G, Z=None, workspace=None, stream=None):
+    """Z (B x L fp32) from FP8 weights."""
+    torch = _torch()
+    _bits(h); _u8(W8); _i32(idx); _i32(wexp)
+    B, H = h.shape
+    K, F = idx.shape
+    if Z is None:
+        Z = torch.empty(B, K * G, dtype=torch.float32, device=h.device)
+    ws, n = _workspace("fwd", B, H, K, G, F, 0, h.device, workspace)
+    _check("haste_fwd_w8", lib().haste_fwd_w8(_ptr(h), _ptr(idx), _ptr(W8), _ptr(wexp), _ptr(Z), B, H, K, G, F,
+                                               _ptr(ws), ws.numel() if ws is not None else 0, _stream(h, stream)))
+    return Z
+
+
+def step_w8(h, idx, W8, wexp, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want_loss=False, out=None,
+            workspace=None, stream=None, events=None):
+    """Fused step from FP8 weights.  Returns dict(dW, dh, Z, loss)."""
+    torch = _torch()
+    _bits(h); _u8(W8); _i32(idx); _i32(wexp); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    K, F = idx.shape
+    if out is None:
+        out = {
+            "dW": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "Z": torch.empty(B, K * G, dtype=torch.float32, device=h.device) if want_Z else None,
+            "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
+        }
+    m = DH_MODE[mode]
+    ws, n = _workspace("step", B, H, K, G, F, m, h.device, workspace)
+    args = (_ptr(h), _ptr(idx), _ptr(W8), _ptr(wexp), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]),
+            _ptr(out["dh"]), _ptr(out.get("Z")), _ptr(out.get("loss")), B, H, K, G, F, m, _ptr(ws),
+            ws.numel() if ws is not None else 0, _stream(h, stream))
+    if events is None:
+        _check("haste_step_w8", lib().haste_step_w8(*args))
+    else:
+        _check("haste_step_w8_timed", lib().haste_step_w8_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
     return out
 
 

@@ -82,6 +82,37 @@ __device__ __forceinline__ u32x4_t cat(u32x2_t a, u32x2_t b) { return u32x4_t{a[
 __device__ __forceinline__ void settle(const u32x4_t& v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void settle(int v) { asm volatile("" ::"v"(v)); }
 
+__device__ __forceinline__ void settle(const u32x2_t& v) { asm volatile("" ::"v"(v)); }
+
+// Type selection without <type_traits>.
+template <bool C, class A, class B>
+struct pick {
+    using type = A;
+};
+template <class A, class B>
+struct pick<false, A, B> {
+    using type = B;
+};
+
+// Eight FP8 E4M3 weights (one 8-byte piece, weight i in byte i) times the
+// power-of-two scale sc, as eight bf16 values in one 16-byte piece (value i
+// in half i).  Exact: a code has four significant bits.
+__device__ __forceinline__ u32x4_t widen_w8(u32x2_t v, float sc)
+{
+    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true))};
+}
+// Identity for bf16 weight pieces (the same call site serves both formats).
+__device__ __forceinline__ u32x4_t widen_w8(u32x4_t v, float) { return v; }
+
+__device__ __forceinline__ u32x2_t ldg8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+__device__ __forceinline__ u32x2_t ldg8_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
 __device__ __forceinline__ u32x4_t ldg16(const void* p)
 {
     return *reinterpret_cast<const u32x4_t*>(p);

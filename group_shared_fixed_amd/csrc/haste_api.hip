@@ -102,19 +102,53 @@ size_t haste_workspace_size(int op, int64_t B, int64_t H, int64_t K, int64_t G, 
     return layout(op, B, H, G, F, dh_mode).total;
 }
 
-int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, float* Z, int64_t B, int64_t H,
-              int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+namespace {
+
+// Forward logits from bf16 weights (W) or FP8 codes and group exponents (W8, wexp).
+int fwd_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
+             float* Z, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace,
+             size_t workspace_bytes, hipStream_t stream)
 {
-    if (!h || !idx || !W || !Z) return HASTE_ERR_NULL;
+    const bool w8 = W8 != nullptr;
+    if (!h || !idx || !Z || (w8 ? !wexp : !W)) return HASTE_ERR_NULL;
     HASTE_TRY(check_shape(B, H, K, G, F, false));
-    if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(Z) || (w8 ? (!aligned16(W8) || !aligned16(wexp)) : !aligned16(W)))
+        return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_FWD, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     uint16_t* hT = (uint16_t*)workspace;
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FwdArgs a{};
-    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K; a.scale = 1.f; a.Z = Z;
-    if (!launch_fwd((int)G, (int)F, FWD_Z, false, a, fwd_grid(K), stream)) return HASTE_ERR_UNSUPPORTED;
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.W8 = W8; a.wexp = wexp; a.K = K; a.scale = 1.f;
+    a.Z = Z;
+    if (!launch_fwd((int)G, (int)F, FWD_Z, false, a, fwd_grid(K), stream, w8)) return HASTE_ERR_UNSUPPORTED;
+    return hip_status();
+}
+
+}  // namespace
+
+int haste_fwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, float* Z, int64_t B, int64_t H,
+              int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return fwd_impl(h, idx, W, nullptr, nullptr, Z, B, H, K, G, F, workspace, workspace_bytes, stream);
+}
+
+int haste_fwd_w8(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp, float* Z,
+                 int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream)
+{
+    if (!W8) return HASTE_ERR_NULL;
+    return fwd_impl(h, idx, nullptr, W8, wexp, Z, B, H, K, G, F, workspace, workspace_bytes, stream);
+}
+
+int haste_quantize_w8(const haste_bf16* W, uint8_t* W8, int32_t* wexp, int64_t K, int64_t G, int64_t F,
+                      hipStream_t stream)
+{
+    if (!W || !W8 || !wexp) return HASTE_ERR_NULL;
+    if (K < 1) return HASTE_ERR_DIM;
+    HASTE_TRY(check_shape(1, F, K, G, F, false));
+    if (!aligned16(W) || !aligned16(W8) || !aligned16(wexp)) return HASTE_ERR_ALIGN;
+    if (!launch_quantize_w8((int)G, (int)F, W, W8, wexp, K, stream)) return HASTE_ERR_UNSUPPORTED;
     return hip_status();
 }
 
@@ -178,18 +212,23 @@ int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, 
     return hip_status();
 }
 
-int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
-                     const int32_t* y_col, float scale, float* dW, float* dh, float* Z, double* loss, int64_t B,
-                     int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+namespace {
+
+// The fused step from bf16 weights (W) or FP8 codes and group exponents (W8, wexp).
+int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
+              const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+              double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
 {
-    if (!h || !idx || !W || !y_rowptr || !y_col || !dW || !dh) return HASTE_ERR_NULL;
+    const bool w8 = W8 != nullptr;
+    if (!h || !idx || !y_rowptr || !y_col || !dW || !dh || (w8 ? !wexp : !W)) return HASTE_ERR_NULL;
+    if (w8 ? (!aligned16(W8) || !aligned16(wexp)) : !aligned16(W)) return HASTE_ERR_ALIGN;
     HASTE_TRY(check_shape(B, H, K, G, F, false));
     if (B > kMaxLabelBatch) return HASTE_ERR_UNSUPPORTED;
     if (dh_mode != HASTE_DH_ATOMIC && dh_mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
     if (!(scale > 0.f)) return HASTE_ERR_DIM;
-    if (!aligned16(h) || !aligned16(idx) || !aligned16(W) || !aligned16(y_rowptr) || !aligned16(y_col) ||
-        !aligned16(dW) || !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
+    if (!aligned16(h) || !aligned16(idx) || !aligned16(y_rowptr) || !aligned16(y_col) || !aligned16(dW) ||
+        !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
         return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_STEP, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
@@ -203,20 +242,51 @@ int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
     launch_transpose_h(h, hT, B, H, l.Bp, stream, det ? nullptr : dh, B * H, loss);
     mark(1);
     FwdArgs a{};
-    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;
+    a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.W8 = W8; a.wexp = wexp; a.K = K;
     a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dW = dW; a.loss = loss;
-    if (!launch_fwd((int)G, (int)F, STEP_DW, loss != nullptr, a, fwd_grid(K), stream))
+    if (!launch_fwd((int)G, (int)F, STEP_DW, loss != nullptr, a, fwd_grid(K), stream, w8))
         return HASTE_ERR_UNSUPPORTED;
     mark(2);
     DhArgs d{};
-    d.hT = hT; d.Bp = l.Bp; d.B = B; d.H = H; d.idx = idx; d.W = W; d.K = K;
+    d.hT = hT; d.Bp = l.Bp; d.B = B; d.H = H; d.idx = idx; d.W = W; d.W8 = W8; d.wexp = wexp; d.K = K;
     d.y_rowptr = y_rowptr; d.y_col = y_col; d.scale = scale;
     d.nchunks = l.nchunks; d.ntiles = l.ntiles; d.dh = dh; d.part = part;
-    if (!launch_dh((int)G, (int)F, DH_FROM_LABELS, det, d, stream)) return HASTE_ERR_UNSUPPORTED;
+    if (!launch_dh((int)G, (int)F, DH_FROM_LABELS, det, d, stream, w8)) return HASTE_ERR_UNSUPPORTED;
     mark(3);
     if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
     mark(4);
     return hip_status();
+}
+
+}  // namespace
+
+int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                     const int32_t* y_col, float scale, float* dW, float* dh, float* Z, double* loss, int64_t B,
+                     int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    if (!W) return HASTE_ERR_NULL;
+    return step_impl(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
+                     workspace, workspace_bytes, stream, events);
+}
+
+int haste_step_w8_timed(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp,
+                        const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+                        double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    if (!W8) return HASTE_ERR_NULL;
+    return step_impl(h, idx, nullptr, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
+                     workspace, workspace_bytes, stream, events);
+}
+
+int haste_step_w8(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp,
+                  const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+                  double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream)
+{
+    return haste_step_w8_timed(h, idx, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
+                               workspace, workspace_bytes, stream, nullptr);
 }
 
 int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,

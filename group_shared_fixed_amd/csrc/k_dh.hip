@@ -77,7 +77,7 @@ constexpr bool dh16_turn_per_round(int G, int F, int src)
     return src == DH_FROM_DZ ? G * F > 4096 : (G * F > 2048 && F > 64);
 }
 
-template <int G, int F, int SRC, bool DET, int RPT>
+template <int G, int F, int SRC, bool DET, int RPT, bool WQ = false>
 __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 {
     constexpr int NT = F / 16;          // output slot tiles of P
@@ -131,17 +131,23 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     // Inputs of one round of a wave.
     struct Stage {
-        u32x4_t w[NWP];             // W_k (G x F, contiguous) as 16-byte pieces lane + 64 p
+        typename pick<WQ, u32x2_t, u32x4_t>::type w[NWP];   // W_k (G x F, contiguous), pieces lane + 64 p
+        int wex;                    // group exponent (FP8 weights)
         u32x4_t h[LAB ? NHP : 1];   // gathered tile pieces
         u32x4_t d[LAB ? 1 : NDP];   // dZ tile pieces
         int col[NT];                // accumulator columns I_k[16t + r16]
     };
     // W_k as contiguous 16-byte pieces (four consecutive lanes read 64
     // consecutive bytes, which keeps the address units' per-line work low)
-    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
+    auto load_w = [&](int64_t kk, auto& st) {
 #pragma unroll
-        for (int p = 0; p < NWP; ++p)
-            if (lane + 64 * p < G * F / 8) wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+        for (int p = 0; p < NWP; ++p) {
+            if (lane + 64 * p < G * F / 8) {
+                if constexpr (WQ) st.w[p] = ldg8(a.W8 + kk * G * F + 8 * (lane + 64 * p));
+                else st.w[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+            }
+        }
+        st.wex = WQ ? a.wexp[kk] : 0;
     };
     auto load_col = [&](int64_t kk, int (&cl)[NT]) {
 #pragma unroll
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             load_dz(kk, sa.d);
         }
         load_col(kk, sa.col);
-        load_w(kk, sa.w);
+        load_w(kk, sa);
     }
 
     __syncthreads();
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             load_dz(kn, n.d);
         }
         load_col(kn, n.col);
-        load_w(kn, n.w);
+        load_w(kn, n);
 
         if (active) {
             // W_k rows into LDS (the contraction over labels reads them transposed)
@@ -222,7 +228,8 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             for (int pp = 0; pp < NWP; ++pp) {
                 const int u = lane + 64 * pp;
                 if (u < G * F / 8)
-                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = c.w[pp];
+                    *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) =
+                        widen_w8(c.w[pp], WQ ? __builtin_amdgcn_ldexpf(1.0f, c.wex) : 1.0f);
             }
 
 #pragma unroll
@@ -440,7 +447,7 @@ __device__ __forceinline__ int acc32_off(int j, int r)
 // takes its turn on the accumulator once per RPT rounds (RPT groups per
 // turn): four when dZ is given (the turn hand-offs bound that kernel, and
 // its per-group registers are few), two when the logits are recomputed.
-template <int G, int F, int SRC, bool DET, int NWV, int RPT>
+template <int G, int F, int SRC, bool DET, int NWV, int RPT, bool WQ = false>
 __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 {
     constexpr int NT = F / 16;          // output slot tiles of P
@@ -496,16 +503,22 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 
     // Inputs of one round as loaded from global memory.
     struct In {
-        u32x4_t w[NWP];                  // W_k (G x F, contiguous) as 16-byte pieces lane + 64 p
+        typename pick<WQ, u32x2_t, u32x4_t>::type w[NWP];   // W_k (G x F, contiguous), pieces lane + 64 p
+        int wex;                         // group exponent (FP8 weights)
         u32x4_t h[LAB ? 2 : 1][NHH];     // gathered pieces, per 16-row half
         u32x4_t d[LAB ? 1 : 2][NDH];     // dZ tile pieces, per 16-row half
         int col[NT];                     // accumulator columns I_k[16t + r16]
     };
     // W_k as contiguous 16-byte pieces (four consecutive lanes read 64 bytes)
-    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
+    auto load_w = [&](int64_t kk, auto& st) {
 #pragma unroll
-        for (int p = 0; p < NWP; ++p)
-            if (lane + 64 * p < G * F / 8) wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+        for (int p = 0; p < NWP; ++p) {
+            if (lane + 64 * p < G * F / 8) {
+                if constexpr (WQ) st.w[p] = ldg8(a.W8 + kk * G * F + 8 * (lane + 64 * p));
+                else st.w[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
+            }
+        }
+        st.wex = WQ ? a.wexp[kk] : 0;
     };
     auto load_col = [&](int64_t kk, int (&cl)[NT]) {
 #pragma unroll
@@ -563,7 +576,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             load_dz(kk, sa.d);
         }
         load_col(kk, sa.col);
-        load_w(kk, sa.w);
+        load_w(kk, sa);
     }
 
     __syncthreads();
@@ -580,7 +593,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             load_dz(kn, n.d);
         }
         load_col(kn, n.col);
-        load_w(kn, n.w);
+        load_w(kn, n);
         if (!active) {
             // the inputs of an idle round still count as consumed (see settle)
 #pragma unroll
@@ -601,7 +614,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         for (int pp = 0; pp < NWP; ++pp) {
             const int u = lane + 64 * pp;
             if (u < G * F / 8)
-                *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) = c.w[pp];
+                *reinterpret_cast<u32x4_t*>(wt + wt_off<F>(u / (F / 8), 8 * (u % (F / 8)))) =
+                    widen_w8(c.w[pp], WQ ? __builtin_amdgcn_ldexpf(1.0f, c.wex) : 1.0f);
         }
         u32x4_t ahi[2][KSG], alo[2][KSG];
         if constexpr (!LAB) {
@@ -838,20 +852,45 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
     }
 }
 
+// Launch with the kernel's dynamic-LDS limit raised to what this launch
+// needs (per kernel, only when it grows).  A refused raise is not left
+// behind as the thread's last error: the launch reports its own failure.
+template <void (*Kern)(DhArgs)>
+static void launch_kern(dim3 grid, dim3 blk, size_t lds, hipStream_t s, const DhArgs& a)
+{
+    static size_t raised = 64 * 1024;
+    if (lds > raised) {
+        if (hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) ==
+            hipSuccess)
+            raised = lds;
+        else
+            (void)hipGetLastError();
+    }
+    hipLaunchKernelGGL(Kern, grid, blk, lds, s, a);
+}
+
 template <int G, int F>
-static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
+static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s, bool w8)
 {
     const int rows = dh_tile_rows((int)G, (int)F, a.H);
     const size_t lds = (size_t)rows * a.H * sizeof(float);
     const dim3 grid(a.nchunks * a.ntiles), blk(rows == 32 ? 512 : 256);
-    auto go = [&](auto kern) {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-            attr = true;
+#define go(...) launch_kern<__VA_ARGS__>(grid, blk, lds, s, a)
+    if (w8) {
+        // FP8 weights: the fused step's kernels (logits recomputed from labels)
+        if (src != DH_FROM_LABELS) return false;
+        if constexpr (G * F <= 2048 && F <= 64) {
+            if (rows == 32) {
+                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8, 2, true>);
+                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8, 2, true>);
+                return true;
+            }
         }
-        hipLaunchKernelGGL(kern, grid, blk, lds, s, a);
-    };
+        constexpr int RP = dh16_rpt(G, F, DH_FROM_LABELS);
+        if (det) go(k_group_dh<G, F, DH_FROM_LABELS, true, RP, true>);
+        else go(k_group_dh<G, F, DH_FROM_LABELS, false, RP, true>);
+        return true;
+    }
     if constexpr (G * F <= 2048 && F <= 64) {
         if (rows == 32) {
             if (src == DH_FROM_DZ) {
@@ -873,25 +912,26 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s)
         else go(k_group_dh<G, F, DH_FROM_LABELS, false, RP>);
     }
     return true;
+#undef go
 }
 
 template <int G>
-static bool launch_dh_g(int F, int src, bool det, const DhArgs& a, hipStream_t s)
+static bool launch_dh_g(int F, int src, bool det, const DhArgs& a, hipStream_t s, bool w8)
 {
     switch (F) {
-    case 32: return launch_dh_gf<G, 32>(src, det, a, s);
-    case 64: return launch_dh_gf<G, 64>(src, det, a, s);
-    case 128: return launch_dh_gf<G, 128>(src, det, a, s);
+    case 32: return launch_dh_gf<G, 32>(src, det, a, s, w8);
+    case 64: return launch_dh_gf<G, 64>(src, det, a, s, w8);
+    case 128: return launch_dh_gf<G, 128>(src, det, a, s, w8);
     }
     return false;
 }
 
-bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s)
+bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s, bool w8)
 {
     switch (G) {
-    case 16: return launch_dh_g<16>(F, src, det, a, s);
-    case 32: return launch_dh_g<32>(F, src, det, a, s);
-    case 64: return launch_dh_g<64>(F, src, det, a, s);
+    case 16: return launch_dh_g<16>(F, src, det, a, s, w8);
+    case 32: return launch_dh_g<32>(F, src, det, a, s, w8);
+    case 64: return launch_dh_g<64>(F, src, det, a, s, w8);
     }
     return false;
 }

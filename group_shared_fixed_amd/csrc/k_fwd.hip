@@ -53,7 +53,10 @@ __device__ __forceinline__ int tile_off(int f, int b)
 }
 
 // WZ: also write the fp32 logits (optional output of the BCE modes).
-template <int G, int F, int MODE, bool LOSS, bool WZ>
+// WQ: the weights come as FP8 E4M3 codes with one power-of-two scale per
+// group (a.W8, a.wexp); they are widened to exact bf16 values on their way
+// into LDS, so the arithmetic is that of the bf16 kernel on those values.
+template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ = false>
 __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(FwdArgs a)
 {
     constexpr int NT = F / 16;    // 16-slot tiles (gather units, dW columns)
@@ -128,13 +131,19 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         for (int t = 0; t < NT; ++t)
             cl[t] = a.idx[kk * F + 16 * t + qr];
     };
-    // W_k (G x F bf16, contiguous) as 16-byte pieces, lane + 64 p in order
+    // W_k (G x F, contiguous) as pieces of eight weights, lane + 64 p in
+    // order: 16 bytes of bf16, or 8 bytes of FP8 codes plus the group's exponent
     constexpr int NWP = FWD ? (G * F / 8 + 63) / 64 : 1;
-    auto load_w = [&](int64_t kk, u32x4_t (&wr)[NWP]) {
+    using WPiece = typename pick<WQ, u32x2_t, u32x4_t>::type;
+    int wex = 0;
+    auto load_w = [&](int64_t kk, WPiece (&wr)[NWP]) {
         if constexpr (FWD) {
 #pragma unroll
-            for (int p = 0; p < NWP; ++p)
-                wr[p] = ldg16_stream(a.W + kk * G * F + 8 * (lane + 64 * p));
+            for (int p = 0; p < NWP; ++p) {
+                if constexpr (WQ) wr[p] = ldg8_stream(a.W8 + kk * G * F + 8 * (lane + 64 * p));
+                else wr[p] = ldg16_stream(a.W + kk * G * F + 8 * (lane + 64 * p));
+            }
+            if constexpr (WQ) wex = a.wexp[kk];
         }
     };
     // gather: lane (slot 16t + qr, quad position qc) <- h[32c + 8qc .. +8, I_k[slot]];
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
 
     int col[NT], col_n[NT];
     uint32_t gp[NT];
-    u32x4_t wraw[NWP];                      // weights as loaded
+    WPiece wraw[NWP];                       // weights as loaded
     u32x4_t wreg[FWD ? GT : 1][FWD ? KS : 1];
     // Modes without per-chunk outputs (and registers to spare) run four-chunk
     // groups as two chunk pairs: a pair's inputs
@@ -278,11 +287,13 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             }
             // 16-byte piece j of label row g sits at piece j ^ (g % (F/8)) of the row
             constexpr int PR = F / 8;
+            const float wsc = WQ ? __builtin_amdgcn_ldexpf(1.0f, wex) : 1.0f;
 #pragma unroll
             for (int p = 0; p < NWP; ++p) {
                 const int u = lane + 64 * p;
                 if (u < G * PR)
-                    *reinterpret_cast<u32x4_t*>(wk + (u / PR) * F + 8 * ((u ^ (u / PR)) & (PR - 1))) = wraw[p];
+                    *reinterpret_cast<u32x4_t*>(wk + (u / PR) * F + 8 * ((u ^ (u / PR)) & (PR - 1))) =
+                        widen_w8(wraw[p], wsc);
             }
             wave_sync();
 #pragma unroll
@@ -637,54 +648,61 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     }
 }
 
-template <int G, int F, int MODE, bool LOSS, bool WZ>
+template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ>
 static void go(const FwdArgs& a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_group_fwd<G, F, MODE, LOSS, WZ>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_group_fwd<G, F, MODE, LOSS, WZ, WQ>), dim3(grid), dim3(256), 0, s, a);
 }
 
-template <int G, int F, int MODE>
+template <int G, int F, int MODE, bool WQ>
 static void go_bce(bool loss, bool wz, const FwdArgs& a, int grid, hipStream_t s)
 {
     if (loss) {
-        if (wz) go<G, F, MODE, true, true>(a, grid, s);
-        else go<G, F, MODE, true, false>(a, grid, s);
+        if (wz) go<G, F, MODE, true, true, WQ>(a, grid, s);
+        else go<G, F, MODE, true, false, WQ>(a, grid, s);
     } else {
-        if (wz) go<G, F, MODE, false, true>(a, grid, s);
-        else go<G, F, MODE, false, false>(a, grid, s);
+        if (wz) go<G, F, MODE, false, true, WQ>(a, grid, s);
+        else go<G, F, MODE, false, false, WQ>(a, grid, s);
     }
 }
 
 template <int G, int F>
-static bool launch_gf(int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s)
+static bool launch_gf(int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8)
 {
     const bool wz = a.Z != nullptr;
+    if (w8) {
+        switch (mode) {
+        case FWD_Z: go<G, F, FWD_Z, false, false, true>(a, grid, s); return true;
+        case STEP_DW: go_bce<G, F, STEP_DW, true>(loss, wz, a, grid, s); return true;
+        }
+        return false;
+    }
     switch (mode) {
-    case FWD_Z: go<G, F, FWD_Z, false, false>(a, grid, s); return true;
-    case FWD_BCE: go_bce<G, F, FWD_BCE>(loss, wz, a, grid, s); return true;
-    case STEP_DW: go_bce<G, F, STEP_DW>(loss, wz, a, grid, s); return true;
-    case BWD_W: go<G, F, BWD_W, false, false>(a, grid, s); return true;
+    case FWD_Z: go<G, F, FWD_Z, false, false, false>(a, grid, s); return true;
+    case FWD_BCE: go_bce<G, F, FWD_BCE, false>(loss, wz, a, grid, s); return true;
+    case STEP_DW: go_bce<G, F, STEP_DW, false>(loss, wz, a, grid, s); return true;
+    case BWD_W: go<G, F, BWD_W, false, false, false>(a, grid, s); return true;
     }
     return false;
 }
 
 template <int G>
-static bool launch_g(int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s)
+static bool launch_g(int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8)
 {
     switch (F) {
-    case 32: return launch_gf<G, 32>(mode, loss, a, grid, s);
-    case 64: return launch_gf<G, 64>(mode, loss, a, grid, s);
-    case 128: return launch_gf<G, 128>(mode, loss, a, grid, s);
+    case 32: return launch_gf<G, 32>(mode, loss, a, grid, s, w8);
+    case 64: return launch_gf<G, 64>(mode, loss, a, grid, s, w8);
+    case 128: return launch_gf<G, 128>(mode, loss, a, grid, s, w8);
     }
     return false;
 }
 
-bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s)
+bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8)
 {
     switch (G) {
-    case 16: return launch_g<16>(F, mode, loss, a, grid, s);
-    case 32: return launch_g<32>(F, mode, loss, a, grid, s);
-    case 64: return launch_g<64>(F, mode, loss, a, grid, s);
+    case 16: return launch_g<16>(F, mode, loss, a, grid, s, w8);
+    case 32: return launch_g<32>(F, mode, loss, a, grid, s, w8);
+    case 64: return launch_g<64>(F, mode, loss, a, grid, s, w8);
     }
     return false;
 }

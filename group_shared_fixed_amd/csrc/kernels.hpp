@@ -32,6 +32,8 @@ struct FwdArgs {
     uint16_t* dZ;         // B x L bf16 (FWD_BCE output, BWD_W input)
     float* dW;            // L x F fp32 (STEP_DW)
     double* loss;         // 1 double, accumulated (optional)
+    const uint8_t* W8;    // L x F FP8 E4M3 codes (FP8-weight variants, in place of W)
+    const int32_t* wexp;  // K group exponents: weight = decode(code) * 2^wexp[k]
 };
 
 struct DhArgs {
@@ -47,6 +49,8 @@ struct DhArgs {
     int nchunks, ntiles;
     float* dh;            // B x H fp32, pre-zeroed (atomic flush)
     float* part;          // nchunks x (ntiles*kDhRows) x H fp32 (deterministic flush)
+    const uint8_t* W8;    // FP8-weight variants: L x F E4M3 codes in place of W
+    const int32_t* wexp;  // K group exponents
 };
 
 struct FixedArgs {
@@ -64,14 +68,16 @@ struct FixedArgs {
 };
 
 // Each launcher returns false when no kernel exists for (G, F).
-bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s);
+// w8: weights as FP8 codes + group exponents (modes FWD_Z and STEP_DW only).
+bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8 = false);
 // Batch rows per feature-gradient workgroup: 32 (eight waves, one workgroup
 // per CU) when the per-wave tiles and a 32 x H accumulator fit in LDS, else 16.
 inline int dh_tile_rows(int G, int F, int64_t H)
 {
     return (G * F <= 2048 && F <= 64 && H <= 768) ? 32 : kDhRows;
 }
-bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s);
+// w8: weights as FP8 codes + group exponents (DH_FROM_LABELS only).
+bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s, bool w8 = false);
 void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
                       hipStream_t s);
 bool launch_fixed_fwd(int F, const FixedArgs& a, int grid, hipStream_t s);
@@ -98,6 +104,10 @@ constexpr size_t kHeadBlasWorkspace = 64ull << 20;
 // number of chunks (each leaves a 2B x H fp32 partial in the workspace).
 constexpr int64_t kHeadDhChunk = 1024;
 constexpr int64_t head_dh_chunks(int64_t L) { return (L + kHeadDhChunk - 1) / kHeadDhChunk; }
+
+// FP8 weights: W (L x F bf16) -> E4M3 codes W8 (L x F) and group exponents
+// wexp (K int32); false if (G, F) has no kernel.
+bool launch_quantize_w8(int G, int F, const uint16_t* W, uint8_t* W8, int32_t* wexp, int64_t K, hipStream_t s);
 
 // Rewiring (dynamic sparse training): grow[k, j] = sum over group k's labels
 // of |(dZ^T h)[l, j]| from hT (H x Bp, Bp = 32 * (1..8)) and bf16 dZ; then

@@ -203,6 +203,34 @@ int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
                      int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head, int dh_mode,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* FP8 weights ("limitations" section: pairing the layer with FP8
+ * quantisation is the named next step; the scheme is this library's
+ * reading).  W is stored as OCP FP8 E4M3 codes W8 (L x F bytes; 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448, no
+ * infinities) and one exponent per label group, wexp (K int32): weight
+ * [l, f] = decode(W8[l, f]) * 2^wexp[l / G], an exact bf16 value.  The
+ * FP8-weight calls compute exactly what haste_fwd / haste_step compute on
+ * those bf16 values (bitwise the same results), reading half the weight
+ * bytes.  haste_quantize_w8: wexp[k] = the smallest integer e with
+ * max |W_k| 2^-e <= 448 (0 for an all-zero group; clamped to [-120, 120])
+ * and W8 = the codes of W 2^-e rounded to nearest, ties to the even code.
+ * Shapes, limits, workspaces and errors as haste_fwd / haste_step; W8 and
+ * wexp 16-byte aligned. */
+int haste_quantize_w8(const haste_bf16* W, uint8_t* W8, int32_t* wexp, int64_t K, int64_t G, int64_t F,
+                      hipStream_t stream);
+int haste_fwd_w8(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp, float* Z,
+                 int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+int haste_step_w8(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp,
+                  const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+                  double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+/* haste_step_w8 with the events of haste_step_timed. */
+int haste_step_w8_timed(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp,
+                        const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+                        double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* Group-level rewiring of the index sets: the discrete phase of the dynamic
  * sparse training ("loss / training strategy" section: every so many steps
  * the group-level I_k are reselected RigL-style with |I_k| = F kept; the

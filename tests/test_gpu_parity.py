@@ -36,6 +36,9 @@ CASES = {
     "g16_f64_many_b120": (120, 512, 2500, 16, 64),
     "g32_f32_b97": (97, 256, 300, 32, 32),
     "g16_f32_b128": (128, 128, 40, 16, 32),
+    # G = 64 with F = 128: the 16-row feature-gradient kernel with its
+    # largest static LDS, first launched at a small H
+    "g64_f128_b45": (45, 200, 9, 64, 128),
 }
 
 _cache = {}
