@@ -379,6 +379,107 @@ def joint_bench(args):
             fh.write(line + "\n")
 
 
+def w8_bench(args):
+    """The fused step with FP8 (E4M3) weights (haste_step_w8) on the
+    Amazon-3M shape, next to the bf16 step on the same (dequantized) weights
+    in the same process.  One JSON line: samples/s of both, per-kernel event
+    averages, the dominant kernel against HBM bandwidth with the FP8
+    algorithmic bytes, and the quantizer's time."""
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import get_workload, make_inputs
+
+    w = get_workload(args.workload)
+    B, H, K, G, F, L = w.B, w.H, w.K, w.G, w.F, w.L
+    dev = torch.device("cuda:0")
+    log(f"[w8] generating {w.name}: L={L} G={G} K={K} F={F} H={H} B={B}")
+    d = make_inputs(w, dZ=False)
+    h, idx, W = bf16_dev(d["h"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev)
+    rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+    W8, wexp = hs.quantize_w8(W, G)
+    # the bf16 weights the FP8 step computes with, for the side-by-side step
+    Wq = torch.empty_like(W)
+    Wq.view(torch.int16).copy_(torch.from_numpy(dequant_host(W8.cpu().numpy(), wexp.cpu().numpy(), G)
+                                                ).view(torch.int16).to(dev))
+    s = 1.0 / B
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = {"dW": torch.empty(L, F, dtype=torch.float32, device=dev),
+           "dh": torch.empty(B, H, dtype=torch.float32, device=dev), "Z": None, "loss": None}
+    ws = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, args.mode)), dtype=torch.uint8, device=dev)
+    ev = HipEvents(5 * args.steps + 2)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn(None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn(None)
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / args.steps
+        for i in range(args.steps):
+            fn(ev.block(5 * i, 5))
+        torch.cuda.synchronize()
+
+        def avg(a, b):
+            return 1e3 * sum(ev.ms(5 * i + a, 5 * i + b) for i in range(args.steps)) / args.steps
+
+        return ms, {"fwd_bce_dw_us": round(avg(1, 2), 2), "dh_us": round(avg(2, 3), 2),
+                    "dh_reduce_us": round(avg(3, 4), 2)}
+
+    ms8, ph8 = timed(lambda e: hs.step_w8(h, idx, W8, wexp, rp, col, s, G, mode=args.mode, out=out, workspace=ws,
+                                          events=e))
+    ms16, ph16 = timed(lambda e: hs.step(h, idx, Wq, rp, col, s, G, mode=args.mode, out=out, workspace=ws,
+                                         events=e))
+    q_ms = time_call(lambda: hs.quantize_w8(W, G, W8=W8, wexp=wexp), 20, sh, ev)
+    log(f"[w8] fp8-weight step {ms8:.3f} ms {ph8}; bf16 step {ms16:.3f} ms {ph16}; quantize {1e3 * q_ms:.1f} us")
+    nnz = int(d["y_rowptr"][-1])
+    lab = (B + 1) * 4 + nnz * 4
+    bytes_a = L * F * 1 + K * 4 + K * F * 4 + B * H * 2 + lab + L * F * 4
+    bytes_b = L * F * 1 + K * 4 + K * F * 4 + B * H * 2 + lab + B * H * 4
+    dom_us, dom_b, dom_k = ((ph8["dh_us"], bytes_b, "k_group_dh32<..., FP8 weights> (feature gradient)")
+                            if ph8["dh_us"] >= ph8["fwd_bce_dw_us"] else
+                            (ph8["fwd_bce_dw_us"], bytes_a, "k_group_fwd<..., FP8 weights> (forward + BCE + dW)"))
+    ach = dom_b / (dom_us * 1e-6) / 1e9
+    res = {
+        "metric": "tail-layer fwd+bwd samples/s with FP8 (E4M3) weights, L=3M G=32",
+        "value": round(B / (ms8 * 1e-3), 1), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms8, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 compute, fp8 e4m3 weights", "data": "synthetic",
+        "config": {"workload": w.name, "L": L, "G": G, "K": K, "F": F, "H": H, "B": B, "dh_mode": args.mode,
+                   "step": "haste_step_w8: fused forward + BCE + dW + dh from E4M3 weights with group exponents"},
+        "kernels_us": ph8,
+        "bf16_step": {"ms_per_step": round(ms16, 4), "samples_per_s": round(B / (ms16 * 1e-3), 1),
+                      "kernels_us": ph16},
+        "speedup_vs_bf16_step": round(ms16 / ms8, 3),
+        "quantize_us": round(1e3 * q_ms, 2),
+        "roofline": {"kernel": dom_k, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dom_b, "avg_us": round(dom_us, 2)},
+    }
+    ev.close()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
+def dequant_host(W8, wexp, G):
+    """bf16 bits of decode(code) * 2^wexp: the E4M3 format's definition on the host
+    (used to build the bf16 step that runs beside the FP8 one)."""
+    import numpy as np
+    c = W8.astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.ldexp(1.0, e - 10))
+    val = np.where(c & 0x80, -mag, mag) * np.ldexp(1.0, np.repeat(wexp.astype(np.int64), G))[:, None]
+    return (val.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def rewire_bench(args):
     """Group-level rewiring (haste_rewire) on the Amazon-3M shape: K =
     93,748 groups of G = 32, F = 64, H = 768, B = 128, dZ ~ N(0, 1) bf16,
@@ -499,6 +600,8 @@ def main():
     ap.add_argument("--rewire", action="store_true",
                     help="group-level rewiring (haste_rewire) on the Amazon-3M shape, one JSON line")
     ap.add_argument("--n-swap", type=int, default=16, help="with --rewire: slots replaced per group")
+    ap.add_argument("--w8", action="store_true",
+                    help="the fused step with FP8 (E4M3) weights next to the bf16 step, one JSON line")
     args = ap.parse_args()
 
     if args.ingest:
@@ -516,6 +619,8 @@ def main():
         return joint_bench(args)
     if args.rewire:
         return rewire_bench(args)
+    if args.w8:
+        return w8_bench(args)
 
     import numpy as np
     import torch
