@@ -328,3 +328,71 @@ def oracle_dequantize_w8(W8, wexp, G):
     if not np.array_equal(back, vals):
         raise ValueError("dequantized weight not exact in bf16")
     return bits
+
+
+# ------------------------------------------------------------ label grouping
+#
+# HASTE notes, "group-shared fixed fan-in": labels are grouped by embedding
+# similarity, approximately, in two stages: mini-batch spherical k-means into
+# C ~ L / (beta G) coarse clusters, then, inside each cluster, greedy groups
+# of a seed and its G - 1 nearest neighbours.  Embeddings are given (L x H
+# bf16); similarity is the dot product (the cosine for unit vectors).
+
+def oracle_kmeans_assign(E, M):
+    """a[l] = argmax_c <E_l, M_c> (the lowest c among equal maxima) and the
+    maximum s[l]; E (L x H) and M (C x H) are bf16 bits."""
+    Ef, Mf = _bf16_f64(E), _bf16_f64(M)
+    S = Ef @ Mf.T
+    a = np.argmax(S, axis=1)                       # first maximum = lowest c
+    return a.astype(np.int32), S[np.arange(S.shape[0]), a]
+
+
+def oracle_kmeans_update(E, batch, a_batch, Mc, v):
+    """One mini-batch step of spherical k-means: Sculley's mini-batch update
+    (each batch member x of centre c moves it by (x - mu_c) / v_c after
+    v_c += 1, i.e. mu_c becomes the running mean of everything assigned to it
+    so far), then the centre is projected back onto the unit sphere.  Centres
+    without batch members are left as they are.  Mc: C x H fp64, v: C counts.
+    Returns (Mc_new, v_new)."""
+    Ef = _bf16_f64(E)
+    Mc = np.array(Mc, dtype=np.float64, copy=True)
+    v = np.array(v, dtype=np.int64, copy=True)
+    for c in np.unique(a_batch):
+        members = np.asarray(batch)[np.asarray(a_batch) == c]
+        m = members.size
+        mu = (v[c] * Mc[c] + Ef[members].sum(axis=0)) / (v[c] + m)
+        v[c] += m
+        Mc[c] = mu / np.linalg.norm(mu)
+    return Mc, v
+
+
+def oracle_group_greedy(E, a, C, G):
+    """Groups of exactly G labels from cluster assignments a (L,) in [0, C):
+    inside each cluster (members in increasing label id), while at least G
+    members are ungrouped, the lowest-id ungrouped member is the seed and the
+    G - 1 ungrouped members with the largest <E_seed, E_x> (lower id on
+    ties) join it; a group lists its members in increasing id.  Clusters are
+    taken in increasing id; the members left over (fewer than G per cluster)
+    are then concatenated in (cluster, id) order and cut into consecutive
+    groups of G.  Returns perm (L,) int32: group k = perm[kG : (k+1)G].
+    L must be a multiple of G."""
+    L = E.shape[0]
+    if L % G:
+        raise ValueError("L must be a multiple of G")
+    Ef = _bf16_f64(E)
+    groups, leftovers = [], []
+    for c in range(C):
+        free = [int(x) for x in np.nonzero(np.asarray(a) == c)[0]]      # increasing id
+        while len(free) >= G:
+            seed = free[0]
+            rest = free[1:]
+            sims = Ef[rest] @ Ef[seed]
+            order = sorted(range(len(rest)), key=lambda i: (-sims[i], rest[i]))[:G - 1]
+            chosen = sorted([seed] + [rest[i] for i in order])
+            groups.append(chosen)
+            taken = set(chosen)
+            free = [x for x in free if x not in taken]
+        leftovers.extend(free)
+    for i in range(0, len(leftovers), G):
+        groups.append(leftovers[i:i + G])
+    return np.array([x for g in groups for x in g], dtype=np.int32)

@@ -11,6 +11,8 @@ from .gen import (  # noqa: F401
     bf16_bits,
     bf16_value,
     head_tail_labels,
+    kmeans_draws,
+    label_embeddings,
     make_inputs,
     normal_bf16,
     sorted_subsets,

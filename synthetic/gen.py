@@ -4,7 +4,8 @@ Every tensor is drawn from ``np.random.SeedSequence([seed_no, tensor_no,
 chunk])`` so the result does not depend on the number of worker threads.
 Tensor numbers: 0 group index sets, 1 features h, 2 weights W, 3 upstream
 gradient dZ, 4 label-rank permutation, 5 positive labels, 6 per-label index
-sets of the G=1 fixed fan-in baseline, 7 dense-head weights.
+sets of the G=1 fixed fan-in baseline, 7 dense-head weights, 8 label
+embeddings, 9 their topics, 10 k-means draws (initial centres, mini-batches).
 
 bf16 values are carried as their uint16 bit patterns, rounded from float32
 to nearest with ties to even.
@@ -17,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-T_IDX, T_H, T_W, T_DZ, T_PERM, T_POS, T_IDX1, T_WHEAD = range(8)
+T_IDX, T_H, T_W, T_DZ, T_PERM, T_POS, T_IDX1, T_WHEAD, T_EMB, T_EMBTOPIC, T_KM = range(11)
 
 _CHUNK = 1 << 22  # elements per independently seeded chunk
 
@@ -196,3 +197,38 @@ def make_inputs(w, *, dZ: bool = True, labels: bool = True, idx1: bool = False, 
     if idx1:
         out["idx1"] = sorted_subsets(w.L, w.F, w.H, w.seed_no, T_IDX1)
     return out
+
+
+def label_embeddings(L: int, H: int, topics: int, noise: float, seed_no: int) -> np.ndarray:
+    """L x H bf16 bits: unit vectors normalize(t_{c(l)} + noise * n_l) with
+    `topics` random unit topic directions t, c(l) uniform, n_l ~ N(0, I/H)."""
+    rng_t = _rng(seed_no, T_EMBTOPIC)
+    T = rng_t.normal(size=(topics, H))
+    T /= np.linalg.norm(T, axis=1, keepdims=True)
+    c = rng_t.integers(0, topics, size=L)
+    out = np.empty((L, H), dtype=np.uint16)
+    step = max(1, _CHUNK // H)
+
+    def work(i):
+        lo, hi = i * step, min(L, (i + 1) * step)
+        x = T[c[lo:hi]] + noise * _rng(seed_no, T_EMB, i).normal(size=(hi - lo, H)) / np.sqrt(H)
+        x /= np.linalg.norm(x, axis=1, keepdims=True)
+        out[lo:hi] = bf16_bits(x.astype(np.float32))
+
+    nchunks = (L + step - 1) // step
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def kmeans_draws(L: int, C: int, batch: int, iters: int, seed_no: int):
+    """The random choices of mini-batch k-means, drawn here and passed to both
+    implementations: C distinct initial centre labels and `iters` mini-batches
+    of `batch` distinct labels each."""
+    rng = _rng(seed_no, T_KM)
+    init = np.sort(rng.choice(L, size=C, replace=False)).astype(np.int32)
+    batches = [np.sort(rng.choice(L, size=batch, replace=False)).astype(np.int32) for _ in range(iters)]
+    return init, batches

@@ -30,6 +30,10 @@ What pins what:
   E4M3 hand values              codes of 1, 448, 2^-9, -2, ties to even
   FP8 group scales              e_k minimal, dequantized weights exact in bf16, within the
                                 format's rounding bound of W, and encoding back to their codes
+  k-means assignment            brute-force loops over centres, ties to the lowest centre
+  k-means update                Sculley's per-sample rule (loops) == the closed form; full-batch
+                                steps from zero counts never lower the objective (Lloyd)
+  greedy grouping               planted clumps recovered exactly; partition and leftover rules
 """
 
 from __future__ import annotations
@@ -535,6 +539,136 @@ def pin_w8_group_scales(lib):
     assert (again == W8).all(), "codes do not round-trip"
 
 
+def pin_kmeans_assign_brute_force(lib):
+    """a[l] is the centre with the largest dot product, found by plain loops;
+    a repeated centre row must lose to its first copy."""
+    rng = np.random.default_rng(29)
+    L, C, H = 30, 7, 6
+    E = bf16_bits(rng.integers(-3, 4, size=(L, H)).astype(np.float32))
+    M = bf16_bits(rng.integers(-3, 4, size=(C, H)).astype(np.float32))
+    M[5] = M[2]                                     # exact ties between centres 2 and 5
+    a, smax = O.oracle_kmeans_assign(E, M)
+    ef, mf = _f(E), _f(M)
+    for l in range(L):
+        best, bc = None, -1
+        for c in range(C):
+            d = sum(ef[l, j] * mf[c, j] for j in range(H))
+            if best is None or d > best:
+                best, bc = d, c
+        assert a[l] == bc and smax[l] == best, f"label {l}: {a[l]} vs {bc}"
+
+
+def pin_kmeans_update(lib):
+    """The closed-form update equals Sculley's per-sample rule run as loops
+    (v += 1; mu += (x - mu) / v, in batch order), then normalised; and
+    full-batch steps from zero counts (spherical Lloyd) never lower
+    sum_l <E_l, mu_a(l)>."""
+    rng = np.random.default_rng(30)
+    L, C, H = 60, 5, 8
+    E = bf16_bits(rng.normal(size=(L, H)).astype(np.float32))
+    ef = _f(E)
+    Mc = ef[[3, 17, 29, 41, 55]].copy()
+    v = np.array([0, 4, 1, 0, 9])
+    batch = np.sort(rng.choice(L, size=25, replace=False)).astype(np.int32)
+    a_b = rng.integers(0, C - 1, size=25).astype(np.int32)        # centre C-1 gets nothing
+    got, v_got = O.oracle_kmeans_update(E, batch, a_b, Mc, v)
+    mu, cnt = Mc.copy(), v.copy()
+    touched = set()
+    for x, c in zip(batch, a_b):
+        cnt[c] += 1
+        mu[c] = mu[c] + (ef[x] - mu[c]) / cnt[c]
+        touched.add(int(c))
+    for c in touched:
+        mu[c] = mu[c] / np.sqrt(sum(t * t for t in mu[c]))
+    _close(got, mu, 1e-12, 1e-12, "k-means update vs per-sample rule")
+    assert (v_got == cnt).all(), "k-means counts"
+    # spherical Lloyd steps: objective non-decreasing
+    M = bf16_bits(ef[[0, 10, 20, 30, 40]].astype(np.float32))
+    Mc = _f(M)
+    prev = -np.inf
+    for _ in range(6):
+        a, _ = O.oracle_kmeans_assign(E, bf16_bits(Mc.astype(np.float32)))
+        Mc, _ = O.oracle_kmeans_update(E, np.arange(L, dtype=np.int32), a, Mc, np.zeros(C, np.int64))
+        obj = float(sum(ef[l] @ Mc[a[l]] for l in range(L)))
+        assert obj >= prev - 1e-9, f"objective fell: {obj} < {prev}"
+        prev = obj
+
+
+def pin_group_greedy(lib):
+    """Planted clumps: inside each cluster, clumps of G identical unit
+    vectors, orthogonal to each other, plus a few labels orthogonal to
+    everything with ids above every clump member (so no seed is one of
+    them); the greedy groups must be exactly the clumps (members in
+    increasing id), clusters in order, then the leftovers in (cluster, id)
+    order cut into groups of G."""
+    rng = np.random.default_rng(31)
+    G, H = 4, 32
+    clumps = {0: 2, 1: 1, 2: 3}                    # clumps per cluster
+    extra = {0: 1, 1: 3, 2: 0}                     # leftovers per cluster
+    n = sum(G * k + extra[c] for c, k in clumps.items())
+    n_pad = (-n) % G                               # a fourth cluster of leftovers only
+    L = n + n_pad
+    n_clump = G * sum(clumps.values())
+    # label ids in the order the loop below takes them: clump members get a
+    # shuffle of the low ids, leftovers a shuffle of the high ids
+    low, high = rng.permutation(n_clump), n_clump + rng.permutation(L - n_clump)
+    ids, il, ih = [], 0, 0
+    for c in range(3):
+        ids += list(low[il:il + G * clumps[c]])
+        il += G * clumps[c]
+        ids += list(high[ih:ih + extra[c]])
+        ih += extra[c]
+    ids += list(high[ih:])
+    ids = np.array(ids)
+    E = np.zeros((L, H), np.float32)
+    a = np.zeros(L, np.int32)
+    axis = 0
+    pos = 0
+    want_groups, left = [], []
+    for c in range(3):
+        for _ in range(clumps[c]):
+            members = ids[pos:pos + G]
+            pos += G
+            E[members, axis] = 1.0
+            axis += 1
+            a[members] = c
+            want_groups.append((c, sorted(int(x) for x in members)))
+        for _ in range(extra[c]):
+            x = ids[pos]
+            pos += 1
+            E[x, axis] = 1.0
+            axis += 1
+            a[x] = c
+            left.append((c, int(x)))
+    for _ in range(n_pad):
+        x = ids[pos]
+        pos += 1
+        E[x, axis] = 1.0
+        axis += 1
+        a[x] = 3
+        left.append((3, int(x)))
+    perm = O.oracle_group_greedy(bf16_bits(E), a, 4, G)
+    assert sorted(perm.tolist()) == list(range(L)), "not a permutation"
+    greedy = [g for _, g in sorted(want_groups, key=lambda t: (t[0], t[1][0]))]
+    lo = [x for _, x in sorted(left)]
+    want = [x for g in greedy for x in g] + lo
+    assert perm.tolist() == want, "planted clumps not recovered"
+    # random embeddings: a partition whose greedy groups stay inside one cluster
+    L2, C2 = 96, 5
+    E2 = bf16_bits(rng.normal(size=(L2, H)).astype(np.float32))
+    a2 = rng.integers(0, C2, size=L2).astype(np.int32)
+    p2 = O.oracle_group_greedy(E2, a2, C2, G)
+    assert sorted(p2.tolist()) == list(range(L2))
+    n_greedy = sum(int((a2 == c).sum()) // G for c in range(C2))
+    for k in range(n_greedy):
+        g = p2[k * G:(k + 1) * G]
+        assert len(set(a2[g].tolist())) == 1 and list(g) == sorted(g), f"greedy group {k}"
+    rest = p2[n_greedy * G:].tolist()
+    assert rest == sorted(rest, key=lambda x: (a2[x], x)), "leftovers not in (cluster, id) order"
+    for c in range(C2):
+        assert sum(1 for x in rest if a2[x] == c) == int((a2 == c).sum()) % G, f"leftovers of cluster {c}"
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -556,4 +690,7 @@ ALL_PINS = [
     pin_e4m3_codec_torch,
     pin_e4m3_hand_values,
     pin_w8_group_scales,
+    pin_kmeans_assign_brute_force,
+    pin_kmeans_update,
+    pin_group_greedy,
 ]

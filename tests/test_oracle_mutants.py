@@ -101,6 +101,15 @@ PY_MUTANTS = {
                           "scaled = _bf16_f64(W) * np.ldexp(1.0, 0 * np.repeat(wexp, G)"),
     "w8_exponent_one_high": ("    return np.clip(e, -120, 120).astype(np.int32)",
                              "    return np.clip(e + 1, -120, 120).astype(np.int32)"),
+    "kmeans_argmax_last": ("    a = np.argmax(S, axis=1)", "    a = S.shape[1] - 1 - np.argmax(S[:, ::-1], axis=1)"),
+    "kmeans_update_no_norm": ("        Mc[c] = mu / np.linalg.norm(mu)", "        Mc[c] = mu"),
+    "kmeans_update_ignores_counts": ("        mu = (v[c] * Mc[c] + Ef[members].sum(axis=0)) / (v[c] + m)",
+                                     "        mu = Ef[members].sum(axis=0) / m"),
+    "group_seed_highest": ("            seed = free[0]\n            rest = free[1:]",
+                           "            seed = free[-1]\n            rest = free[:-1]"),
+    "group_farthest": ("key=lambda i: (-sims[i], rest[i])", "key=lambda i: (sims[i], rest[i])"),
+    "group_unsorted_members": ("            chosen = sorted([seed] + [rest[i] for i in order])",
+                               "            chosen = [seed] + [rest[i] for i in order]"),
     "rewire_grown_keep_old_weight": (
         "            if c in kept:\n                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]",
         "            W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept.get(c, f_new)]"),
@@ -125,7 +134,8 @@ def test_head_mutant_is_caught(name, monkeypatch):
         monkeypatch.setattr(O, "oracle_head_step", mod.oracle_head_step)
         monkeypatch.setattr(O, "oracle_joint_step", mod.oracle_joint_step)
         for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire", "e4m3_decode", "e4m3_encode",
-                   "w8_group_exponent", "oracle_quantize_w8", "oracle_dequantize_w8"):
+                   "w8_group_exponent", "oracle_quantize_w8", "oracle_dequantize_w8", "oracle_kmeans_assign",
+                   "oracle_kmeans_update", "oracle_group_greedy"):
             monkeypatch.setattr(O, fn, getattr(mod, fn))
         failed = _pins_fail(lib)
     assert failed, f"mutant {name} passes every pin"
