@@ -480,6 +480,113 @@ def dequant_host(W8, wexp, G):
     return (val.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def grouping_bench(args):
+    """Semantic label grouping at the Amazon-3M label count: L = 2,999,936
+    synthetic unit embeddings (H = 768, 4,096 topics), C = L / (4 G) =
+    23,437 clusters for G = 32; k-means init, --km-iters mini-batch steps of
+    65,536 labels, the full assignment and the greedy groups.  One JSON line:
+    the whole pipeline's seconds, the phases (HIP events), the assignment
+    products against the bf16 matrix-core peak, and the oracle on the CPU."""
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    from synthetic import kmeans_draws, label_embeddings
+
+    L, H, G = 2_999_936, 768, 32
+    C, nb, iters = L // (4 * G), 65536, args.km_iters
+    dev = torch.device("cuda:0")
+    log(f"[grouping] generating {L} embeddings (H = {H}), C = {C}, {iters} mini-batch steps of {nb}")
+    E = label_embeddings(L, H, 4096, 0.6, 97)
+    init, batches = kmeans_draws(L, C, nb, iters, 97)
+    Ed = bf16_dev(E, dev)
+    init_d = i32_dev(init, dev)
+    batch_d = [i32_dev(b, dev) for b in batches]
+    ws_a = torch.empty(max(hs.binding.lib().haste_kmeans_assign_workspace_size(L, C, H, 0),
+                           hs.binding.lib().haste_kmeans_assign_workspace_size(nb, C, H, 1)), dtype=torch.uint8,
+                       device=dev)
+    ws_u = torch.empty(hs.binding.lib().haste_kmeans_update_workspace_size(nb, C), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(hs.binding.lib().haste_group_workspace_size(L, C), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ev = HipEvents(2 * iters + 8)
+
+    def pipeline(mark):
+        mark(0)
+        Mc, Mb, v = hs.kmeans_init(Ed, init_d)
+        for i, b in enumerate(batch_d):
+            a_b, _ = hs.kmeans_assign(Ed, Mb, rows=b, workspace=ws_a)
+            mark(1 + 2 * i)
+            hs.kmeans_update(Ed, b, a_b, Mc, Mb, v, workspace=ws_u)
+            mark(2 + 2 * i)
+        a, _ = hs.kmeans_assign(Ed, Mb, workspace=ws_a)
+        mark(2 * iters + 1)
+        perm = hs.group_greedy(Ed, a, C, G, workspace=ws_g)
+        mark(2 * iters + 2)
+        return perm
+
+    pipeline(lambda i: None)                       # warm-up (library code objects, caches)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pipeline(lambda i: None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pipeline(lambda i: ev.record(i, sh))
+    torch.cuda.synchronize()
+    step_assign = sum(ev.ms(2 * i, 2 * i + 1) for i in range(iters)) / iters
+    step_update = sum(ev.ms(2 * i + 1, 2 * i + 2) for i in range(iters)) / iters
+    full_assign = ev.ms(2 * iters, 2 * iters + 1)
+    greedy = ev.ms(2 * iters + 1, 2 * iters + 2)
+    flops_full = 2.0 * L * C * H
+    tf = flops_full / (full_assign * 1e-3) / 1e12
+    log(f"[grouping] pipeline {wall:.3f} s; step assign {step_assign:.2f} ms, update {step_update:.3f} ms; "
+        f"full assign {full_assign:.1f} ms ({tf:.0f} TFLOP/s); greedy {greedy:.1f} ms")
+    res = {
+        "metric": "label grouping time (mini-batch spherical k-means + greedy groups), 3M labels",
+        "value": round(wall, 4), "unit": "s", "n_gpus": 1, "steps": 1, "warmup": 1,
+        "ms_per_step": round(1e3 * wall, 2), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "grouping_3m", "L": L, "H": H, "G": G, "C": C, "minibatch": nb, "iters": iters,
+                   "step": "kmeans_init + iters x (assign batch + update) + full assign + group_greedy"},
+        "phases_ms": {"minibatch_assign": round(step_assign, 3), "minibatch_update": round(step_update, 3),
+                      "full_assign": round(full_assign, 2), "greedy": round(greedy, 2)},
+        "roofline": {"kernel": "full assignment (rocBLAS bf16 products in label chunks + k_row_argmax)",
+                     "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "algorithmic_flops": flops_full,
+                     "avg_us": round(1e3 * full_assign, 1)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        log("[grouping] timing the CPU oracle")
+        M = np.ascontiguousarray(E[init])
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 2 and done < L:
+            O.oracle_kmeans_assign(np.ascontiguousarray(E[done:done + 4096]), M)
+            done += 4096
+        t_assign = (time.perf_counter() - t0) / done                 # s per label
+        t0 = time.perf_counter()
+        n_lab = 0
+        for c in range(C):
+            if time.perf_counter() - t0 > args.cpu_seconds / 2:
+                break
+            sub = np.ascontiguousarray(E[c * 128:(c + 1) * 128])
+            O.oracle_group_greedy(sub, np.zeros(128, np.int32), 1, G)
+            n_lab += 128
+        t_greedy = (time.perf_counter() - t0) / max(n_lab, 1)
+        t_all = (L + iters * nb) * t_assign + L * t_greedy
+        res["cpu_baseline"] = {"value": round(t_all, 1), "unit": "s", "cores": O.num_threads(), "kind": "oracle",
+                               "sample": f"oracle assignment of {done} labels against all {C} centres and greedy "
+                                         f"groups of {n_lab} labels in clusters of 128, extrapolated to the "
+                                         f"pipeline ({L} + {iters} x {nb} assignments, {L} labels grouped)"}
+    ev.close()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "w") as fh:
+            fh.write(line + "\n")
+
+
 def rewire_bench(args):
     """Group-level rewiring (haste_rewire) on the Amazon-3M shape: K =
     93,748 groups of G = 32, F = 64, H = 768, B = 128, dZ ~ N(0, 1) bf16,
@@ -600,6 +707,9 @@ def main():
     ap.add_argument("--rewire", action="store_true",
                     help="group-level rewiring (haste_rewire) on the Amazon-3M shape, one JSON line")
     ap.add_argument("--n-swap", type=int, default=16, help="with --rewire: slots replaced per group")
+    ap.add_argument("--grouping", action="store_true",
+                    help="semantic label grouping (k-means + greedy groups) at 3M labels, one JSON line")
+    ap.add_argument("--km-iters", type=int, default=20, help="with --grouping: mini-batch k-means steps")
     ap.add_argument("--w8", action="store_true",
                     help="the fused step with FP8 (E4M3) weights next to the bf16 step, one JSON line")
     args = ap.parse_args()
@@ -621,6 +731,8 @@ def main():
         return rewire_bench(args)
     if args.w8:
         return w8_bench(args)
+    if args.grouping:
+        return grouping_bench(args)
 
     import numpy as np
     import torch

@@ -15,10 +15,14 @@ from .binding import (  # noqa: F401
     fwd,
     fwd_bce,
     fwd_w8,
+    group_greedy,
     head_step,
     head_workspace_size,
     joint_step,
     joint_workspace_size,
+    kmeans_assign,
+    kmeans_init,
+    kmeans_update,
     rewire,
     rewire_workspace_size,
     step,

@@ -46,6 +46,13 @@ SIGNATURES = {
     "haste_step_w8": (_M, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
     "haste_step_w8_timed": (_M, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P,
                                  _P]),
+    "haste_kmeans_assign_workspace_size": (_S, [_I, _I, _I, _M]),
+    "haste_kmeans_assign": (_M, [_P, _P, _I, _I, _P, _I, _I, _P, _P, _P, _S, _P]),
+    "haste_kmeans_init": (_M, [_P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "haste_kmeans_update_workspace_size": (_S, [_I, _I]),
+    "haste_kmeans_update": (_M, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "haste_group_workspace_size": (_S, [_I, _I]),
+    "haste_group_greedy": (_M, [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P]),
     "haste_rewire_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "haste_rewire": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
@@ -385,6 +392,66 @@ def step_w8(h, idx, W8, wexp, y_rowptr, y_col, scale, G, mode="atomic", want_Z=F
     else:
         _check("haste_step_w8_timed", lib().haste_step_w8_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
     return out
+
+
+def _ws(n, dev, workspace):
+    torch = _torch()
+    return workspace if workspace is not None else torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+
+
+def kmeans_assign(E, M, rows=None, want_score=False, workspace=None, stream=None):
+    """Nearest centre (largest dot product, lowest index on ties) of E rows
+    (all, or E[rows]).  Returns (assign int32, score fp32 or None)."""
+    torch = _torch()
+    _bits(E); _bits(M)
+    L, H = E.shape
+    C = M.shape[0]
+    n = L if rows is None else _i32(rows).numel()
+    a = torch.empty(n, dtype=torch.int32, device=E.device)
+    sc = torch.empty(n, dtype=torch.float32, device=E.device) if want_score else None
+    ws = _ws(int(lib().haste_kmeans_assign_workspace_size(n, C, H, int(rows is not None))), E.device, workspace)
+    _check("haste_kmeans_assign", lib().haste_kmeans_assign(_ptr(E), _ptr(rows), n, L, _ptr(M), C, H, _ptr(a),
+                                                             _ptr(sc), _ptr(ws), ws.numel(), _stream(E, stream)))
+    return a, sc
+
+
+def kmeans_init(E, init, stream=None):
+    """Centres from labels init: (Mc fp32 C x H, Mb bf16 C x H, counts int32 C)."""
+    torch = _torch()
+    _bits(E); _i32(init)
+    L, H = E.shape
+    C = init.numel()
+    Mc = torch.empty(C, H, dtype=torch.float32, device=E.device)
+    Mb = torch.empty(C, H, dtype=torch.bfloat16, device=E.device)
+    v = torch.empty(C, dtype=torch.int32, device=E.device)
+    _check("haste_kmeans_init", lib().haste_kmeans_init(_ptr(E), _ptr(init), L, C, H, _ptr(Mc), _ptr(Mb), _ptr(v),
+                                                         _stream(E, stream)))
+    return Mc, Mb, v
+
+
+def kmeans_update(E, batch, assign, Mc, Mb, counts, workspace=None, stream=None):
+    """One mini-batch step, in place on (Mc, Mb, counts)."""
+    _bits(E); _bits(Mb); _i32(batch); _i32(assign); _i32(counts)
+    L, H = E.shape
+    C = Mc.shape[0]
+    n = batch.numel()
+    ws = _ws(int(lib().haste_kmeans_update_workspace_size(n, C)), E.device, workspace)
+    _check("haste_kmeans_update", lib().haste_kmeans_update(_ptr(E), _ptr(batch), _ptr(assign), n, L, C, H, _ptr(Mc),
+                                                             _ptr(Mb), _ptr(counts), _ptr(ws), ws.numel(),
+                                                             _stream(E, stream)))
+    return Mc, Mb, counts
+
+
+def group_greedy(E, assign, C, G, workspace=None, stream=None):
+    """Label permutation whose consecutive G-blocks are the groups."""
+    torch = _torch()
+    _bits(E); _i32(assign)
+    L, H = E.shape
+    perm = torch.empty(L, dtype=torch.int32, device=E.device)
+    ws = _ws(int(lib().haste_group_workspace_size(L, C)), E.device, workspace)
+    _check("haste_group_greedy", lib().haste_group_greedy(_ptr(E), _ptr(assign), L, C, H, G, _ptr(perm), _ptr(ws),
+                                                           ws.numel(), _stream(E, stream)))
+    return perm
 
 
 def rewire_workspace_size(B, H, K, G, F) -> int:

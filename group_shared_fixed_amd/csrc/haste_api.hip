@@ -530,6 +530,126 @@ int haste_rewire(const haste_bf16* h, const haste_bf16* dZ, const int32_t* idx, 
                               workspace, workspace_bytes, stream, nullptr);
 }
 
+namespace {
+
+int check_emb(int64_t L, int64_t C, int64_t H)
+{
+    if (L < 1 || C < 1 || H < 8) return HASTE_ERR_DIM;
+    if (H % 8 != 0 || H > 1024 || C > L || L > ((int64_t)1 << 30)) return HASTE_ERR_UNSUPPORTED;
+    return HASTE_OK;
+}
+
+struct KmAssignLayout {
+    size_t gather, scores, blas, total;
+    KmAssignLayout(int64_t n_rows, int64_t C, int64_t H, bool rows)
+    {
+        gather = 0;
+        scores = rows ? align256((size_t)n_rows * (size_t)H * 2) : 0;
+        blas = scores + align256((size_t)kmeans_chunk_rows(n_rows, C) * (size_t)((C + 3) / 4 * 4) * 4);
+        total = blas + kHeadBlasWorkspace;
+    }
+};
+
+struct GroupLayout {
+    size_t keys, start, end, gbase, obase, ng, sim, taken, total;
+    GroupLayout(int64_t n, int64_t C, bool greedy)
+    {
+        keys = 0;
+        start = keys + align256((size_t)group_sort_size(n) * 8);
+        end = start + align256((size_t)C * 4);
+        gbase = end + align256((size_t)C * 4);
+        obase = gbase + (greedy ? align256((size_t)C * 4) : 0);
+        ng = obase + (greedy ? align256((size_t)C * 4) : 0);
+        sim = ng + (greedy ? 256 : 0);
+        taken = sim + (greedy ? align256((size_t)n * 4) : 0);
+        total = taken + (greedy ? align256((size_t)n) : 0);
+    }
+};
+
+}  // namespace
+
+size_t haste_kmeans_assign_workspace_size(int64_t n_rows, int64_t C, int64_t H, int with_rows)
+{
+    if (n_rows < 1 || C < 1 || H < 1) return 0;
+    return KmAssignLayout(n_rows, C, H, with_rows != 0).total;
+}
+
+int haste_kmeans_assign(const haste_bf16* E, const int32_t* rows, int64_t n_rows, int64_t L, const haste_bf16* M,
+                        int64_t C, int64_t H, int32_t* assign, float* score, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream)
+{
+    if (!E || !M || !assign) return HASTE_ERR_NULL;
+    HASTE_TRY(check_emb(L, C, H));
+    if (n_rows < 1 || (!rows && n_rows != L) || n_rows > L) return HASTE_ERR_DIM;
+    if (!aligned16(E) || !aligned16(M) || !aligned16(assign) || (rows && !aligned16(rows)) ||
+        (score && !aligned16(score)))
+        return HASTE_ERR_ALIGN;
+    const KmAssignLayout l(n_rows, C, H, rows != nullptr);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    char* w = (char*)workspace;
+    if (!run_kmeans_assign(E, rows, n_rows, M, C, H, assign, score, (uint16_t*)(w + l.gather), (float*)(w + l.scores),
+                           w + l.blas, kHeadBlasWorkspace, stream))
+        return HASTE_ERR_HIP;
+    return hip_status();
+}
+
+int haste_kmeans_init(const haste_bf16* E, const int32_t* init, int64_t L, int64_t C, int64_t H, float* Mc,
+                      haste_bf16* Mb, int32_t* counts, hipStream_t stream)
+{
+    if (!E || !init || !Mc || !Mb || !counts) return HASTE_ERR_NULL;
+    HASTE_TRY(check_emb(L, C, H));
+    if (!aligned16(E) || !aligned16(init) || !aligned16(Mc) || !aligned16(Mb) || !aligned16(counts))
+        return HASTE_ERR_ALIGN;
+    run_kmeans_init(E, init, C, H, Mc, Mb, counts, stream);
+    return hip_status();
+}
+
+size_t haste_kmeans_update_workspace_size(int64_t n, int64_t C)
+{
+    if (n < 1 || C < 1) return 0;
+    return GroupLayout(n, C, false).total;
+}
+
+int haste_kmeans_update(const haste_bf16* E, const int32_t* batch, const int32_t* assign, int64_t n, int64_t L,
+                        int64_t C, int64_t H, float* Mc, haste_bf16* Mb, int32_t* counts, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    if (!E || !batch || !assign || !Mc || !Mb || !counts) return HASTE_ERR_NULL;
+    HASTE_TRY(check_emb(L, C, H));
+    if (n < 1 || n > L) return HASTE_ERR_DIM;
+    if (!aligned16(E) || !aligned16(batch) || !aligned16(assign) || !aligned16(Mc) || !aligned16(Mb) ||
+        !aligned16(counts))
+        return HASTE_ERR_ALIGN;
+    const GroupLayout l(n, C, false);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    char* w = (char*)workspace;
+    run_kmeans_update(E, batch, assign, n, C, H, Mc, Mb, counts, (uint64_t*)(w + l.keys), (int32_t*)(w + l.start),
+                      (int32_t*)(w + l.end), stream);
+    return hip_status();
+}
+
+size_t haste_group_workspace_size(int64_t L, int64_t C)
+{
+    if (L < 1 || C < 1) return 0;
+    return GroupLayout(L, C, true).total;
+}
+
+int haste_group_greedy(const haste_bf16* E, const int32_t* assign, int64_t L, int64_t C, int64_t H, int64_t G,
+                       int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!E || !assign || !perm) return HASTE_ERR_NULL;
+    HASTE_TRY(check_emb(L, C, H));
+    if (G < 1 || G > 64 || L % G != 0) return HASTE_ERR_DIM;
+    if (!aligned16(E) || !aligned16(assign) || !aligned16(perm)) return HASTE_ERR_ALIGN;
+    const GroupLayout l(L, C, true);
+    HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
+    char* w = (char*)workspace;
+    run_group_greedy(E, assign, L, C, H, (int)G, perm, (uint64_t*)(w + l.keys), (int32_t*)(w + l.start),
+                     (int32_t*)(w + l.end), (int32_t*)(w + l.gbase), (int32_t*)(w + l.obase), (int32_t*)(w + l.ng),
+                     (float*)(w + l.sim), (uint8_t*)(w + l.taken), stream);
+    return hip_status();
+}
+
 const char* haste_status_string(int status)
 {
     switch (status) {

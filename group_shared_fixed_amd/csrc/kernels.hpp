@@ -117,4 +117,21 @@ bool launch_rewire_score(const uint16_t* hT, int64_t Bp, int64_t B, int64_t H, c
 bool launch_rewire_select(int G, int F, const int32_t* idx, const uint16_t* W, const float* grow, int64_t K,
                           int64_t H, int n_swap, int32_t* idx_out, uint16_t* W_out, float* prune_out, hipStream_t s);
 
+// Label grouping (mini-batch spherical k-means and greedy groups).
+// Keys sorted for a segment list of n entries take group_sort_size(n) x 8 bytes.
+int64_t group_sort_size(int64_t n);
+// Rows per product chunk of the k-means assignment (scores chunk x C fp32).
+int64_t kmeans_chunk_rows(int64_t n_rows, int64_t C);
+bool run_kmeans_assign(const uint16_t* E, const int32_t* rows, int64_t n_rows, const uint16_t* M, int64_t C,
+                       int64_t H, int32_t* a, float* smax, uint16_t* gather, float* scores, void* blas_ws,
+                       size_t blas_ws_bytes, hipStream_t s);
+void run_kmeans_init(const uint16_t* E, const int32_t* init, int64_t C, int64_t H, float* Mc, uint16_t* Mb,
+                     int32_t* v, hipStream_t s);
+void run_kmeans_update(const uint16_t* E, const int32_t* batch, const int32_t* a_batch, int64_t n, int64_t C,
+                       int64_t H, float* Mc, uint16_t* Mb, int32_t* v, uint64_t* keys, int32_t* start, int32_t* end,
+                       hipStream_t s);
+void run_group_greedy(const uint16_t* E, const int32_t* a, int64_t L, int64_t C, int64_t H, int G, int32_t* perm,
+                      uint64_t* keys, int32_t* start, int32_t* end, int32_t* gbase, int32_t* obase, int32_t* ngroups,
+                      float* sim, uint8_t* taken, hipStream_t s);
+
 }  // namespace haste

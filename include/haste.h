@@ -231,6 +231,49 @@ int haste_step_w8_timed(const haste_bf16* h, const int32_t* idx, const uint8_t* 
                         double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
                         void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
+/* Semantic label grouping ("group-shared fixed fan-in" section: labels are
+ * grouped by the similarity of their embeddings, approximately, by
+ * mini-batch spherical k-means into C ~ L / (beta G) coarse clusters and
+ * then, inside each cluster, greedy groups of a seed and its G - 1 nearest
+ * neighbours).  Embeddings E: L x H bf16 (H % 8 == 0, H <= 1024), similarity
+ * = dot product.  All results are bitwise repeatable.
+ *
+ * haste_kmeans_assign: assign[i] = argmax_c <E_r, M_c> (lowest c on ties)
+ * for r = rows[i] (rows NULL: r = i, n_rows = L); score (nullable) gets
+ * the maximum.  M: C x H bf16.  The products run on rocBLAS in label
+ * chunks (fp32 accumulate), the arg-max is a libhaste kernel.  Workspace:
+ * haste_kmeans_assign_workspace_size(n_rows, C, H, rows != NULL).
+ * haste_kmeans_init: centre c starts as E[init[c]]: Mc (C x H fp32), Mb
+ * (its bf16 copy, the operand of the assignment) and counts[c] = 0.
+ * haste_kmeans_update: one mini-batch step (Sculley's update) for the n
+ * batch labels batch[] with their centres assign[]: a centre with m batch
+ * members becomes mu = (counts[c] Mc[c] + sum of the members, in batch
+ * order) / (counts[c] + m), is normalised to unit length, and counts[c] +=
+ * m; Mb follows.  Centres without members are unchanged.  Workspace:
+ * haste_kmeans_update_workspace_size(n, C).
+ * haste_group_greedy: perm (L int32, a permutation of the labels) such
+ * that group k = perm[kG .. kG + G): per cluster (assign[] in [0, C)),
+ * members in increasing id, the lowest-id ungrouped member seeds a group
+ * and the G - 1 ungrouped members with the largest dot product with it
+ * (lower id on ties) join; a group lists its members in increasing id;
+ * clusters' groups come in cluster order; the members left over (fewer
+ * than G per cluster) follow, concatenated in (cluster, id) order and cut
+ * into groups of G.  L % G == 0, G <= 64.  Workspace:
+ * haste_group_workspace_size(L, C). */
+size_t haste_kmeans_assign_workspace_size(int64_t n_rows, int64_t C, int64_t H, int with_rows);
+int haste_kmeans_assign(const haste_bf16* E, const int32_t* rows, int64_t n_rows, int64_t L, const haste_bf16* M,
+                        int64_t C, int64_t H, int32_t* assign, float* score, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+int haste_kmeans_init(const haste_bf16* E, const int32_t* init, int64_t L, int64_t C, int64_t H, float* Mc,
+                      haste_bf16* Mb, int32_t* counts, hipStream_t stream);
+size_t haste_kmeans_update_workspace_size(int64_t n, int64_t C);
+int haste_kmeans_update(const haste_bf16* E, const int32_t* batch, const int32_t* assign, int64_t n, int64_t L,
+                        int64_t C, int64_t H, float* Mc, haste_bf16* Mb, int32_t* counts, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+size_t haste_group_workspace_size(int64_t L, int64_t C);
+int haste_group_greedy(const haste_bf16* E, const int32_t* assign, int64_t L, int64_t C, int64_t H, int64_t G,
+                       int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Group-level rewiring of the index sets: the discrete phase of the dynamic
  * sparse training ("loss / training strategy" section: every so many steps
  * the group-level I_k are reselected RigL-style with |I_k| = F kept; the
