@@ -118,3 +118,81 @@ def test_validate_rejects(L):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(hb.HasteError):
         hb.lib(str(tmp_path / "nope.so"))
+
+
+def test_head_and_joint_reject(L):
+    ws_h = L.haste_head_workspace_size(128, 768, 89088)
+    assert ws_h > 128 * 89088 * 4 and ws_h % 256 == 0
+    assert L.haste_head_workspace_size(0, 768, 10) == 0
+
+    def head(h=A, W=A, rp=A, col=A, s=0.5, dW=A, dh=A, Z=None, loss=None, B=16, H=64, Lh=10, ws=A,
+             wsb=1 << 30):
+        return L.haste_head_step(h, W, rp, col, ctypes.c_float(s), dW, dh, Z, loss, B, H, Lh, ws, wsb, None)
+
+    assert head(h=None) == NULL
+    assert head(dh=None) == NULL
+    assert head(B=0) == DIM
+    assert head(s=0.0) == DIM
+    assert head(W=MIS) == ALIGN
+    assert head(ws=None) == WS
+    assert head(wsb=16) == WS
+
+    def joint(idx=A, Wt=A, st=0.5, sh=0.5, G=32, F=64, mode=0, wsb=1 << 30):
+        return L.haste_joint_step(A, idx, Wt, A, A, A, A, A, ctypes.c_float(st), ctypes.c_float(sh), A, A, A, None,
+                                  16, 768, 10, G, F, 100, mode, A, wsb, None)
+
+    assert joint(idx=None) == NULL
+    assert joint(st=0.0) == DIM
+    assert joint(G=8) == UNSUP
+    assert joint(mode=5) == UNSUP
+    assert joint(Wt=MIS) == ALIGN
+    assert joint(wsb=16) == WS
+
+
+def test_rewire_rejects(L):
+    B, H, K, G, F = 64, 256, 10, 32, 64
+    need = L.haste_rewire_workspace_size(B, H, K, G, F)
+    assert need == 256 * 64 * 2 + ((K * H * 4 + 255) // 256) * 256
+
+    def rw(h=A, idx=A, idx_out=P(0x900000), W=A, W_out=P(0xA00000), n=4, B=B, H=H, G=G, F=F, ws=A,
+           wsb=1 << 30):
+        return L.haste_rewire(h, A, idx, W, n, idx_out, W_out, None, None, B, H, K, G, F, ws, wsb, None)
+
+    assert rw(h=None) == NULL
+    assert rw(n=-1) == DIM
+    assert rw(n=F + 1) == DIM
+    assert rw(B=257) == UNSUP
+    assert rw(G=8) == UNSUP
+    assert rw(W=MIS) == ALIGN
+    assert rw(idx_out=P(0x100000 + 256)) == DIM    # overlaps idx without being idx
+    assert rw(ws=None) == WS
+
+
+def test_w8_reject(L):
+    assert L.haste_quantize_w8(None, A, A, 10, 32, 64, None) == NULL
+    assert L.haste_quantize_w8(A, A, A, 0, 32, 64, None) == DIM
+    assert L.haste_quantize_w8(A, A, A, 10, 8, 64, None) == UNSUP
+    assert L.haste_quantize_w8(A, MIS, A, 10, 32, 64, None) == ALIGN
+    assert L.haste_fwd_w8(A, A, None, A, A, 128, 768, 10, 32, 64, A, 1 << 30, None) == NULL
+    assert L.haste_fwd_w8(A, A, A, None, A, 128, 768, 10, 32, 64, A, 1 << 30, None) == NULL
+    assert L.haste_fwd_w8(A, A, MIS, A, A, 128, 768, 10, 32, 64, A, 1 << 30, None) == ALIGN
+    assert L.haste_step_w8(A, A, A, A, A, A, ctypes.c_float(0.5), A, A, None, None, 300, 768, 10, 32, 64, 0, A,
+                           1 << 30, None) == UNSUP          # B above the label-driven limit
+    assert L.haste_step_w8(A, A, None, A, A, A, ctypes.c_float(0.5), A, A, None, None, 128, 768, 10, 32, 64, 0, A,
+                           1 << 30, None) == NULL
+
+
+def test_grouping_reject(L):
+    assert L.haste_kmeans_assign_workspace_size(0, 10, 64, 0) == 0
+    assert L.haste_group_workspace_size(1000, 0) == 0
+    assert L.haste_kmeans_assign(None, None, 100, 100, A, 10, 64, A, None, A, 1 << 30, None) == NULL
+    assert L.haste_kmeans_assign(A, None, 50, 100, A, 10, 64, A, None, A, 1 << 30, None) == DIM   # rows NULL: n = L
+    assert L.haste_kmeans_assign(A, None, 100, 100, A, 10, 60, A, None, A, 1 << 30, None) == UNSUP  # H % 8
+    assert L.haste_kmeans_assign(A, None, 100, 100, A, 200, 64, A, None, A, 1 << 30, None) == UNSUP  # C > L
+    assert L.haste_kmeans_assign(A, None, 100, 100, A, 10, 64, A, None, A, 16, None) == WS
+    assert L.haste_kmeans_update(A, A, A, 0, 100, 10, 64, A, A, A, A, 1 << 30, None) == DIM
+    assert L.haste_kmeans_update(A, A, A, 10, 100, 10, 64, MIS, A, A, A, 1 << 30, None) == ALIGN
+    assert L.haste_kmeans_init(A, None, 100, 10, 64, A, A, A, None) == NULL
+    assert L.haste_group_greedy(A, A, 100, 10, 64, 32, A, A, 1 << 30, None) == DIM      # L % G
+    assert L.haste_group_greedy(A, A, 128, 10, 64, 128, A, A, 1 << 30, None) == DIM     # G > 64
+    assert L.haste_group_greedy(A, A, 128, 10, 64, 32, A, A, 16, None) == WS
