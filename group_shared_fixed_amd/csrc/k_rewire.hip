@@ -23,7 +23,6 @@ namespace haste {
 
 namespace {
 
-constexpr int kRwWaves = 8;     // waves per score workgroup
 constexpr int kRwCols = 64;     // feature columns per pass
 constexpr int kRwColTiles = kRwCols / 16;
 
@@ -37,28 +36,29 @@ __host__ __device__ constexpr int pow2_at_least(int x)
 }  // namespace
 
 // grow[k, j] for every group and column.  KS: 32-row k-steps of the batch
-// (Bp = 32 KS); RT: 16-label row tiles per wave.  A workgroup owns
-// kRwWaves * RT * 16 consecutive labels; each wave keeps the matrix-core
-// operands of its labels' dZ (transposed through LDS once) in registers and
-// sweeps the feature columns in passes of 64, with the hT block of the pass
-// staged in LDS for all waves.  Per pass and wave: RT x 4 result tiles; their
-// absolute values are summed over each tile's 16 labels, and the row-tile
-// sums of one group are added in LDS in a fixed order.
-template <int KS, int RT>
-__global__ __launch_bounds__(512) void k_rewire_score(const uint16_t* __restrict__ hT, int64_t Bp, int64_t B,
+// (Bp = 32 KS); RT: 16-label row tiles per wave (4: a wave's 64 labels
+// hold whole groups).  A workgroup owns NW * 64 consecutive labels;
+// each wave keeps the matrix-core operands of its labels' dZ (transposed
+// through LDS once) in registers and sweeps the feature columns in passes of
+// 64, with the hT blocks of the passes staged in two LDS buffers for all
+// waves (one barrier per pass).  Per pass and wave: RT x 4 result tiles;
+// their absolute values are summed over each tile's 16 labels, then over
+// the row tiles of each group in increasing order, in registers.
+template <int KS, int RT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_rewire_score(const uint16_t* __restrict__ hT, int64_t Bp, int64_t B,
                                                       int64_t H, const uint16_t* __restrict__ dZ, int64_t L, int G,
                                                       float* __restrict__ grow)
 {
     constexpr int CH = pow2_at_least(4 * KS);     // 16-byte chunks per staged hT row (swizzle span)
     constexpr int LW = RT * 16;                    // labels per wave
     constexpr int ZROW = LW + 8;                   // staged dZ row (bf16), padded against bank conflicts
-    __shared__ u32x4_t sH[kRwCols * CH];
-    __shared__ uint16_t sZ[kRwWaves][32 * ZROW];
-    __shared__ float sP[kRwWaves * RT][kRwCols];
+    static_assert(RT == 4, "a wave's 64 labels hold whole groups of G <= 64");
+    __shared__ u32x4_t sH[2][kRwCols * CH];
+    __shared__ uint16_t sZ[NW][32 * ZROW];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int q = lane >> 4, i16 = lane & 15;
-    const int64_t lab0 = (int64_t)blockIdx.x * (kRwWaves * LW);
+    const int64_t lab0 = (int64_t)blockIdx.x * (NW * LW);
     const int64_t wl0 = lab0 + (int64_t)w * LW;
 
     // 1. this wave's dZ operands: a[ks][r] holds labels wl0 + 16r + i16,
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(512) void k_rewire_score(const uint16_t* __restrict
     }
 
     const int npass = (int)((H + kRwCols - 1) / kRwCols);
-    const int ntid = kRwWaves * 64;
+    const int ntid = NW * 64;
     constexpr int NCH = kRwCols * 4 * KS;          // staged 16-byte pieces per pass
-    constexpr int PER = (NCH + kRwWaves * 64 - 1) / (kRwWaves * 64);     // per thread
+    constexpr int PER = (NCH + NW * 64 - 1) / (NW * 64);     // per thread
     u32x4_t pre[PER];
     auto fetch = [&](int pass) {
 #pragma unroll
@@ -104,23 +104,28 @@ __global__ __launch_bounds__(512) void k_rewire_score(const uint16_t* __restrict
             pre[i] = (c < NCH && j < H) ? ldg16(hT + j * Bp + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int c = threadIdx.x + ntid * i;
             const int jc = c / (4 * KS), ch = c % (4 * KS);
-            if (c < NCH) sH[jc * CH + (ch ^ (jc & (CH - 1)))] = pre[i];
+            if (c < NCH) sH[buf][jc * CH + (ch ^ (jc & (CH - 1)))] = pre[i];
         }
     };
     fetch(0);
     const int gpw = G / 16;                        // row tiles per group
-    const int64_t groups_wg = (kRwWaves * LW) / G;
-    const int64_t k0 = lab0 / G, K = L / G;
+    const int64_t K = L / G;
+    stage(0);
+    if (npass > 1) fetch(1);
     for (int pass = 0; pass < npass; ++pass) {
-        __syncthreads();                           // previous pass done with sH and sP
-        stage();
+        const int buf = pass & 1;
+        // one barrier per pass: stage `buf` is complete, and every wave is
+        // past the pass that read stage buf ^ 1, which is refilled here
         __syncthreads();
-        if (pass + 1 < npass) fetch(pass + 1);
+        if (pass + 1 < npass) {
+            stage(buf ^ 1);
+            if (pass + 2 < npass) fetch(pass + 2);
+        }
 
         f32x4_t acc[RT][kRwColTiles];
 #pragma unroll
@@ -132,32 +137,45 @@ __global__ __launch_bounds__(512) void k_rewire_score(const uint16_t* __restrict
 #pragma unroll
             for (int t = 0; t < kRwColTiles; ++t) {
                 const int jc = 16 * t + i16, ch = 4 * ks + q;
-                const u32x4_t bop = sH[jc * CH + (ch ^ (jc & (CH - 1)))];
+                const u32x4_t bop = sH[buf][jc * CH + (ch ^ (jc & (CH - 1)))];
 #pragma unroll
                 for (int r = 0; r < RT; ++r) acc[r][t] = mfma16(a[ks][r], bop, acc[r][t]);
             }
         }
-        // |gradient| summed over each row tile's 16 labels, per column
+        // |gradient| summed over each row tile's 16 labels, per column (in
+        // lane, then across the four lane groups), then over the row tiles
+        // of a group in increasing order; the wave's labels hold whole groups
+        float rs[RT][kRwColTiles];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
 #pragma unroll
             for (int t = 0; t < kRwColTiles; ++t) {
                 const f32x4_t v = acc[r][t];
-                float s = ((fabsf(v[0]) + fabsf(v[1])) + fabsf(v[2])) + fabsf(v[3]);
-                s += __shfl_xor(s, 16, 64);
-                s += __shfl_xor(s, 32, 64);
-                if (q == 0) sP[w * RT + r][16 * t + i16] = s;
+                float x = ((fabsf(v[0]) + fabsf(v[1])) + fabsf(v[2])) + fabsf(v[3]);
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                rs[r][t] = x;
             }
         }
-        __syncthreads();
-        // group sums, row tiles in increasing order
-        for (int o = threadIdx.x; o < groups_wg * kRwCols; o += ntid) {
-            const int gl = o / kRwCols, jc = o % kRwCols;
-            const int64_t k = k0 + gl, j = (int64_t)pass * kRwCols + jc;
-            if (k >= K || j >= H) continue;
-            float s = 0.f;
-            for (int u = 0; u < gpw; ++u) s += sP[gl * gpw + u][jc];
-            grow[k * H + j] = s;
+        // lane group q writes column tile q (16 lanes, 64 contiguous bytes)
+        static_assert(kRwColTiles == 4, "one column tile per lane group");
+#pragma unroll
+        for (int r0 = 0; r0 < RT; ++r0) {
+            if (r0 % gpw != 0) continue;
+            float s[kRwColTiles];
+#pragma unroll
+            for (int t = 0; t < kRwColTiles; ++t) {
+                s[t] = rs[r0][t];
+#pragma unroll
+                for (int u = 1; u < RT; ++u)
+                    if (u < gpw && r0 + u < RT) s[t] += rs[r0 + u][t];
+            }
+            float mine = s[0];
+#pragma unroll
+            for (int t = 1; t < kRwColTiles; ++t) mine = q == t ? s[t] : mine;
+            const int64_t k = (wl0 + 16 * r0) / G;
+            const int64_t j = (int64_t)pass * kRwCols + 16 * q + i16;
+            if (k < K && j < H) grow[k * H + j] = mine;
         }
     }
 }
@@ -187,6 +205,15 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
     if (k >= K) return;                            // whole wave; no workgroup barrier below
 
     const uint16_t* Wk = W + k * G * F;
+    // the group's grow scores, lane owns columns lane + 64 t (H <= 1024);
+    // requested first so their latency overlaps the slot ranking
+    constexpr int NT = 16;
+    float v[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t j = lane + 64 * t;
+        v[t] = j < H ? grow[k * H + j] : -1.0f;
+    }
 #pragma unroll
     for (int i = 0; i < (NCHUNK + 63) / 64; ++i) {
         const int c = lane + 64 * i;
@@ -240,14 +267,11 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
     wave_sync();
 
     // grow: n_swap rounds of a wave arg-max over the columns not kept
-    // (largest score, then lowest id); lane owns columns lane + 64 t
-    constexpr int NT = 16;                         // H <= 1024
-    float v[NT];
+    // (largest score, then lowest id)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int64_t j = lane + 64 * t;
-        const bool cand = j < H && !((sKept[w][j >> 5] >> (j & 31)) & 1u);
-        v[t] = cand ? grow[k * H + j] : -1.0f;
+        if (j < H && ((sKept[w][j >> 5] >> (j & 31)) & 1u)) v[t] = -1.0f;
     }
     for (int round = 0; round < n_swap; ++round) {
         float bv = -2.0f;
@@ -321,13 +345,15 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
     }
 }
 
+// Eight waves per workgroup (two per SIMD, up to 256 registers each); four
+// for the longest batches, whose operands need more registers.
 template <int KS>
 static void score_launch(const uint16_t* hT, int64_t Bp, int64_t B, int64_t H, const uint16_t* dZ, int64_t L, int G,
                          float* grow, hipStream_t s)
 {
-    constexpr int RT = KS <= 4 ? 4 : 2;
-    const int64_t per = kRwWaves * RT * 16;
-    hipLaunchKernelGGL((k_rewire_score<KS, RT>), dim3((unsigned)((L + per - 1) / per)), dim3(kRwWaves * 64), 0, s, hT,
+    constexpr int RT = 4, NW = KS <= 6 ? 8 : 4;
+    const int64_t per = NW * RT * 16;
+    hipLaunchKernelGGL((k_rewire_score<KS, RT, NW>), dim3((unsigned)((L + per - 1) / per)), dim3(NW * 64), 0, s, hT,
                        Bp, B, H, dZ, L, G, grow);
 }
 
