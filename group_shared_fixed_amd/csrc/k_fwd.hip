@@ -136,12 +136,17 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     constexpr int NWP = FWD ? (G * F / 8 + 63) / 64 : 1;
     using WPiece = typename pick<WQ, u32x2_t, u32x4_t>::type;
     int wex = 0;
+    // Non-temporal weight loads (read once; they leave L2 to the gathered
+    // rows): measured faster in every mode and shape but the logits-only
+    // forward at F = 128 (381 against 213 us at the 670K shape).
+    constexpr bool W_STREAM = !(MODE == FWD_Z && F == 128);
     auto load_w = [&](int64_t kk, WPiece (&wr)[NWP]) {
         if constexpr (FWD) {
 #pragma unroll
             for (int p = 0; p < NWP; ++p) {
                 if constexpr (WQ) wr[p] = ldg8_stream(a.W8 + kk * G * F + 8 * (lane + 64 * p));
-                else wr[p] = ldg16_stream(a.W + kk * G * F + 8 * (lane + 64 * p));
+                else if constexpr (W_STREAM) wr[p] = ldg16_stream(a.W + kk * G * F + 8 * (lane + 64 * p));
+                else wr[p] = ldg16(a.W + kk * G * F + 8 * (lane + 64 * p));
             }
             if constexpr (WQ) wex = a.wexp[kk];
         }
