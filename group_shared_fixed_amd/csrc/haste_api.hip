@@ -383,7 +383,11 @@ struct HeadLayout {
         dz = z + align256(bl * 4);
         hcat = dz + align256(bl * 4);
         dhcat = hcat + align256(bh * 4);
-        blas = dhcat + align256(bh * 8 * (size_t)head_dh_chunks(L));
+        // partials: 2B x H per rocBLAS chunk, or B x H per matrix-core chunk
+        const size_t np = (size_t)head_dh_chunks(L) * 2 > (size_t)head_dh_mfma_chunks(B, H, L)
+                              ? (size_t)head_dh_chunks(L) * 2
+                              : (size_t)head_dh_mfma_chunks(B, H, L);
+        blas = dhcat + align256(bh * 4 * np);
         total = blas + kHeadBlasWorkspace;
     }
 };

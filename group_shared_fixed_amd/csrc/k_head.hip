@@ -102,18 +102,133 @@ __global__ __launch_bounds__(256) void k_head_bce(const float* __restrict__ Z, c
 }
 
 
-// dh = base + sum over the S label chunks of (top + bottom), with top and
-// bottom the two B x H halves of each chunk's stacked product (base = dh
-// when accumulating, else 0), in a fixed order.
+// dh = base + the sum over the S label chunks of their partial products, in
+// chunk order (base = dh when accumulating, else 0).  halves = 2: each
+// chunk's partial is the stacked 2B x H product, whose two B x H halves
+// (hi, lo) are added first; halves = 1: a B x H partial.
 __global__ __launch_bounds__(256) void k_head_dh_sum(const float* __restrict__ part, float* __restrict__ dh, int64_t n,
-                                                     int S, bool accumulate)
+                                                     int S, int halves, bool accumulate)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float r = 0.f;
+    if (halves == 2) {
 #pragma unroll 4
-    for (int s = 0; s < S; ++s) r += part[(int64_t)s * 2 * n + i] + part[(int64_t)s * 2 * n + n + i];
+        for (int s = 0; s < S; ++s) r += part[(int64_t)s * 2 * n + i] + part[(int64_t)s * 2 * n + n + i];
+    } else {
+#pragma unroll 4
+        for (int s = 0; s < S; ++s) r += part[(int64_t)s * n + i];
+    }
     dh[i] = accumulate ? dh[i] + r : r;
+}
+
+// The feature-gradient product of one label chunk (Lc labels, a multiple of
+// 32 chosen so that the grid is at most one workgroup per CU) on the matrix
+// cores: part[c][b, j] = sum over the chunk's labels l of (hi + lo)[b, l]
+// W[l, j], for a block of 128 batch rows and 256 feature columns; wave w
+// owns columns 32 w .. 32 w + 31 of the block for all 128 rows, so every
+// staged operand is read by one wave only.  The chunk is walked in steps
+// of 32 labels; each step's W tile (32 labels x 256 columns) and dZ tile
+// (hi and lo, 128 rows x 32 labels) go through two LDS buffers (the next
+// step's pieces are loaded into registers a step ahead).  W is read with
+// ds_read_b64_tr_b16 as the label-contiguous operand, dZ rows with plain
+// 16-byte reads; hi and lo accumulate into the same registers.  Needs
+// L % 8 == 0 and H % 8 == 0 (16-byte pieces).
+__global__ __launch_bounds__(512) void k_head_dh(const uint16_t* __restrict__ dzcat, const uint16_t* __restrict__ W,
+                                                 float* __restrict__ part, int64_t B, int64_t H, int64_t L,
+                                                 int64_t Lc)
+{
+    constexpr int CB = 256, WROW = CB + 16, ZROW = 32 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sW[2][32 * WROW];
+    __shared__ __attribute__((aligned(16))) uint16_t sZ[2][2 * 128 * ZROW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3;
+    const int64_t c = blockIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.y * CB, b0 = (int64_t)blockIdx.z * 128;
+    const int64_t l0 = c * Lc, l1 = (l0 + Lc < L) ? l0 + Lc : L;
+
+    // two register sets of pieces: set st % 2 holds step st, loaded two steps
+    // before it is staged
+    u32x4_t pw2[2][2], pz2[2][2];
+    auto fetch = [&](int64_t l, u32x4_t (&pw)[2], u32x4_t (&pz)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = tid + 512 * i;
+            {   // W: row r (label l + r), 16-byte piece pc (columns j0 + 8 pc ..)
+                const int r = p >> 5, pc = p & 31;
+                const int64_t ll = l + r, jj = j0 + 8 * pc;
+                pw[i] = (ll < l1 && jj < H) ? ldg16(W + ll * H + jj) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            {   // dZ: part hl (hi / lo), batch row b0 + row, labels l + 8 pc ..
+                const int hl = p >> 9, row = (p >> 2) & 127, pc = p & 3;
+                const int64_t b = b0 + row, ll = l + 8 * pc;
+                pz[i] = (b < B && ll < l1) ? ldg16(dzcat + (hl * B + b) * L + ll) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto stage = [&](int buf, const u32x4_t (&pw)[2], const u32x4_t (&pz)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = tid + 512 * i;
+            *reinterpret_cast<u32x4_t*>(&sW[buf][(p >> 5) * WROW + 8 * (p & 31)]) = pw[i];
+            *reinterpret_cast<u32x4_t*>(&sZ[buf][((p >> 9) * 128 + ((p >> 2) & 127)) * ZROW + 8 * (p & 3)]) = pz[i];
+        }
+    };
+
+    f32x4_t acc[8][2];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+        acc[rt][0] = zero4();
+        acc[rt][1] = zero4();
+    }
+    const int nsteps = (int)((l1 - l0 + 31) / 32);
+    fetch(l0, pw2[0], pz2[0]);
+    fetch(l0 + 32, pw2[1], pz2[1]);
+    stage(0, pw2[0], pz2[0]);
+    fetch(l0 + 64, pw2[0], pz2[0]);           // fetches past the chunk load zeros
+    for (int s0 = 0; s0 < nsteps; s0 += 2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int s = s0 + u;
+        if (s >= nsteps) break;
+        const int buf = u;        // s & 1
+        __syncthreads();          // stage buf is complete; nobody still reads buf ^ 1
+        if (s + 1 < nsteps) {
+            stage(buf ^ 1, pw2[u ^ 1], pz2[u ^ 1]);
+            fetch(l0 + 32 * (s + 3), pw2[u ^ 1], pz2[u ^ 1]);
+        }
+        // B: the wave's two column tiles, labels 8q .. 8q + 7
+        u32x4_t bo[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint16_t* base = &sW[buf][(8 * q + rr) * WROW + 32 * w + 16 * t + 4 * cc];
+            bo[t] = cat(lds_tr16(base), lds_tr16(base + 4 * WROW));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const int row = 16 * rt + i16;
+            const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(&sZ[buf][row * ZROW + 8 * q]);
+            const u32x4_t al = *reinterpret_cast<const u32x4_t*>(&sZ[buf][(128 + row) * ZROW + 8 * q]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                acc[rt][t] = mfma16(ah, bo[t], acc[rt][t]);
+                acc[rt][t] = mfma16(al, bo[t], acc[rt][t]);
+            }
+        }
+    }
+    // lane: column j0 + 32 w + 16 t + i16, batch rows b0 + 16 rt + 4 q + i
+    float* out = part + c * B * H;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int64_t j = j0 + 32 * w + 16 * t + i16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t b = b0 + 16 * rt + 4 * q + i;
+                if (b < B && j < H) out[b * H + j] = acc[rt][t][i];
+            }
+        }
 }
 
 // The head pass on `stream`: Z (B x L fp32, in zbuf), the BCE gradient as a
@@ -141,7 +256,17 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
                        dzcat, dzcat + B * L, loss, B, L);
     // dW = [hi; lo]^T [h; h] (L x H)
     if (gemm_rm(bh, true, false, L, H, 2 * B, dzcat, L, hcat, H, 0.f, dW, H) != rocblas_status_success) return false;
-    // per label chunk c: [dh_hi; dh_lo]_c = [hi; lo][:, chunk c] W[chunk c, :] (2B x H)
+    const int64_t m = B * H;
+    if (L % 8 == 0 && H % 8 == 0) {
+        // per label chunk c: (hi + lo)[:, chunk c] W[chunk c, :] (B x H) on libhaste's kernel
+        const int64_t S = head_dh_mfma_chunks(B, H, L), Lc = head_dh_mfma_chunk_len(B, H, L);
+        const dim3 grid((unsigned)S, (unsigned)((H + 255) / 256), (unsigned)((B + 127) / 128));
+        hipLaunchKernelGGL(k_head_dh, grid, dim3(512), 0, stream, dzcat, W, dhcat, B, H, L, Lc);
+        hipLaunchKernelGGL(k_head_dh_sum, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, dhcat, dh, m,
+                           (int)S, 1, accumulate_dh);
+        return true;
+    }
+    // otherwise on rocBLAS: per label chunk c, [dh_hi; dh_lo]_c = [hi; lo][:, chunk c] W[chunk c, :] (2B x H)
     const int64_t Lc = kHeadDhChunk, full = L / Lc, rem = L % Lc;
     const float one = 1.0f, zero = 0.0f;
     if (full > 0 &&
@@ -156,9 +281,8 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
     if (rem > 0 && gemm_rm(bh, false, false, 2 * B, H, rem, dzcat + full * Lc, L, W + full * Lc * H, H, 0.f,
                            dhcat + full * 2 * B * H, H) != rocblas_status_success)
         return false;
-    const int64_t m = B * H;
     hipLaunchKernelGGL(k_head_dh_sum, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, dhcat, dh, m,
-                       (int)head_dh_chunks(L), accumulate_dh);
+                       (int)head_dh_chunks(L), 2, accumulate_dh);
     return true;
 }
 

@@ -104,6 +104,23 @@ constexpr size_t kHeadBlasWorkspace = 64ull << 20;
 // number of chunks (each leaves a 2B x H fp32 partial in the workspace).
 constexpr int64_t kHeadDhChunk = 1024;
 constexpr int64_t head_dh_chunks(int64_t L) { return (L + kHeadDhChunk - 1) / kHeadDhChunk; }
+// The matrix-core feature-gradient kernel of the head splits the labels into
+// chunks (a multiple of 32 labels each) so that chunks x column blocks x row
+// blocks stays within one workgroup per CU (256): a second round of
+// workgroups would double the kernel's time.
+constexpr int64_t head_dh_mfma_chunk_len(int64_t B, int64_t H, int64_t L)
+{
+    const int64_t blocks = ((H + 255) / 256) * ((B + 127) / 128);
+    int64_t s = 256 / blocks;
+    if (s < 1) s = 1;
+    const int64_t len = (L + s - 1) / s;
+    return (len + 31) / 32 * 32;
+}
+constexpr int64_t head_dh_mfma_chunks(int64_t B, int64_t H, int64_t L)
+{
+    const int64_t len = head_dh_mfma_chunk_len(B, H, L);
+    return (L + len - 1) / len;
+}
 
 // FP8 weights: W (L x F bf16) -> E4M3 codes W8 (L x F) and group exponents
 // wexp (K int32); false if (G, F) has no kernel.

@@ -15,10 +15,12 @@ from synthetic import get_workload, make_inputs, normal_bf16, zipf_labels
 pytestmark = pytest.mark.gpu
 
 # (B, H, L_head): one label, a ragged label count (BCE tail stores), label
-# counts that are multiples of 8 (16-byte stores), batches around 128, and
-# label counts past one or several feature-gradient chunks of 1024 labels
+# counts that are multiples of 8 (16-byte stores, and the matrix-core
+# feature-gradient kernel, here with two 128-row blocks and a partial
+# column block), batches around 128, and label counts past one or several
+# feature-gradient chunks of 1024 labels
 HEAD_CASES = [(1, 16, 1), (5, 40, 13), (64, 128, 256), (37, 96, 73), (130, 264, 1001), (128, 768, 2048),
-              (64, 256, 5000)]
+              (64, 256, 5000), (130, 200, 1000), (3, 8, 8)]
 
 
 def _head_inputs(B, H, L, seed):
