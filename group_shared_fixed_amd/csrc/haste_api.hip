@@ -372,17 +372,18 @@ int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t
 namespace {
 
 // Head workspace: Z (B x L fp32), stacked dZ hi / lo (2B x L bf16), [h; h]
-// (2B x H bf16), the stacked dh products of the label chunks (2B x H fp32
-// each), rocBLAS's workspace.
+// (2B x H bf16), hT (H x Bp bf16), the dh partials of the label chunks,
+// rocBLAS's workspace.
 struct HeadLayout {
-    size_t z, dz, hcat, dhcat, blas, total;
+    size_t z, dz, hcat, hT, dhcat, blas, total;
     HeadLayout(int64_t B, int64_t H, int64_t L)
     {
         const size_t bl = (size_t)B * (size_t)L, bh = (size_t)B * (size_t)H;
         z = 0;
         dz = z + align256(bl * 4);
         hcat = dz + align256(bl * 4);
-        dhcat = hcat + align256(bh * 4);
+        hT = hcat + align256(bh * 4);
+        dhcat = hT + align256((size_t)H * (size_t)round_up(B, 32) * 2);
         // partials: 2B x H per rocBLAS chunk, or B x H per matrix-core chunk
         const size_t np = (size_t)head_dh_chunks(L) * 2 > (size_t)head_dh_mfma_chunks(B, H, L)
                               ? (size_t)head_dh_chunks(L) * 2
@@ -425,7 +426,8 @@ int head_pass(const haste_bf16* h, const haste_bf16* W, const int32_t* y_rowptr,
     char* w = (char*)workspace;
     float* zbuf = Z ? Z : (float*)(w + l.z);
     if (!run_head(h, W, y_rowptr, y_col, scale, dW, dh, zbuf, loss, B, H, L, accumulate, (uint16_t*)(w + l.dz),
-                  (uint16_t*)(w + l.hcat), (float*)(w + l.dhcat), w + l.blas, kHeadBlasWorkspace, stream))
+                  (uint16_t*)(w + l.hcat), (float*)(w + l.dhcat), (uint16_t*)(w + l.hT), w + l.blas,
+                  kHeadBlasWorkspace, stream))
         return HASTE_ERR_HIP;
     return hip_status();
 }

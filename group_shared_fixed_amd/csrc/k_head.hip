@@ -231,6 +231,87 @@ __global__ __launch_bounds__(512) void k_head_dh(const uint16_t* __restrict__ dz
         }
 }
 
+// dW = [hi; lo]^T [h; h] on the matrix cores, without the stacked copies:
+// a workgroup owns 64 labels and 768 feature columns; the labels' dZ (hi
+// and lo, Bp <= 128 batch rows x 64 labels) is staged in LDS once and read
+// transposed (ds_read_b64_tr_b16) as the label-row operand; the batch-
+// contiguous operand comes from the feature-major copy hT (H x Bp, zero
+// rows past B) in L2; wave w owns 96 columns for the 64 labels (24 result
+// tiles), hi and lo accumulating into the same registers.  dW rows are
+// written once, through LDS as 16-byte pieces.  Needs L % 8 == 0,
+// H % 4 == 0 and Bp <= 128.
+__global__ __launch_bounds__(512) void k_head_dw(const uint16_t* __restrict__ dzcat, const uint16_t* __restrict__ hT,
+                                                 int64_t Bp, float* __restrict__ dW, int64_t B, int64_t H, int64_t L)
+{
+    constexpr int LB = 64, ZROW = LB + 8, CW = 96, CT = CW / 16, OROW = CW + 4;
+    __shared__ __attribute__((aligned(16))) uint16_t sZ[2][128 * ZROW];
+    __shared__ __attribute__((aligned(16))) float sO[8][16 * OROW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3;
+    const int64_t l0 = (int64_t)blockIdx.x * LB;
+    const int64_t jw = (int64_t)blockIdx.y * (8 * CW) + CW * w;   // the wave's first column
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + 512 * i;                // 2 x 128 rows x 8 pieces
+        const int hl = p >> 10, row = (p >> 3) & 127, pc = p & 7;
+        const int64_t ll = l0 + 8 * pc;
+        const u32x4_t v = (row < B && ll < L) ? ldg16(dzcat + ((int64_t)hl * B + row) * L + ll)
+                                              : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(&sZ[hl][row * ZROW + 8 * pc]) = v;
+    }
+    __syncthreads();
+    f32x4_t acc[4][CT];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < CT; ++t) acc[rt][t] = zero4();
+    const int nks = (int)(Bp / 32);
+    // batch-contiguous operands of step ks, requested a step ahead
+    auto load_b = [&](int ks, u32x4_t (&bo)[CT]) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int64_t j = jw + 16 * t + i16;
+            bo[t] = (j < H && ks < nks) ? ldg16(hT + j * Bp + 32 * ks + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    u32x4_t bo[CT], bn[CT];
+    load_b(0, bn);
+    for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) bo[t] = bn[t];
+        load_b(ks + 1, bn);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const uint16_t* base = &sZ[hl][(32 * ks + 8 * q + rr) * ZROW + 16 * rt + 4 * cc];
+                const u32x4_t a = cat(lds_tr16(base), lds_tr16(base + 4 * ZROW));
+#pragma unroll
+                for (int t = 0; t < CT; ++t) acc[rt][t] = mfma16(a, bo[t], acc[rt][t]);
+            }
+        }
+    }
+    // out through LDS, one 16-label tile at a time, so dW rows go out as
+    // 16-byte pieces of 384-byte runs (lane: column jw + 16 t + i16, labels
+    // l0 + 16 rt + 4 q + i)
+    float* so = sO[w];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[(4 * q + i) * OROW + 16 * t + i16] = acc[rt][t][i];
+        wave_sync();
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {                // 16 rows x 24 pieces
+            const int pc = lane + 64 * u, row = pc / 24, c4 = pc % 24;
+            const int64_t l = l0 + 16 * rt + row, j = jw + 4 * c4;
+            if (l < L && j < H) stg_stream(dW + l * H + j, *reinterpret_cast<const f32x4_t*>(&so[row * OROW + 4 * c4]));
+        }
+        wave_sync();
+    }
+}
+
 // The head pass on `stream`: Z (B x L fp32, in zbuf), the BCE gradient as a
 // stacked bf16 hi / lo matrix dzcat (2B x L), hcat = [h; h] (2B x H bf16),
 // dW = dzcat^T hcat (L x H fp32), the stacked dh products of the
@@ -241,21 +322,32 @@ __global__ __launch_bounds__(512) void k_head_dh(const uint16_t* __restrict__ dz
 // it over the chip.  Returns false if a rocBLAS call or a copy fails.
 bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
               float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
-              uint16_t* dzcat, uint16_t* hcat, float* dhcat, void* blas_ws, size_t blas_ws_bytes,
+              uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws, size_t blas_ws_bytes,
               hipStream_t stream)
 {
     rocblas_handle bh = blas_handle(stream, blas_ws, blas_ws_bytes);
     if (!bh) return false;
-    const size_t hbytes = (size_t)B * (size_t)H * 2;
-    if (hipMemcpyAsync(hcat, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
-    if (hipMemcpyAsync(hcat + B * H, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
+    const int64_t Bp = (B + 31) / 32 * 32;
+    const bool own_dw = L % 8 == 0 && H % 4 == 0 && Bp <= 128;
+    if (own_dw) {
+        launch_transpose_h(h, hT, B, H, Bp, stream);
+    } else {
+        const size_t hbytes = (size_t)B * (size_t)H * 2;
+        if (hipMemcpyAsync(hcat, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
+        if (hipMemcpyAsync(hcat + B * H, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
+    }
     // Z = h W^T (B x L)
     if (gemm_rm(bh, false, true, B, L, H, h, H, W, H, 0.f, zbuf, L) != rocblas_status_success) return false;
     const int64_t n = B * ((L + 7) / 8);
     hipLaunchKernelGGL(k_head_bce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zbuf, rowptr, col, scale,
                        dzcat, dzcat + B * L, loss, B, L);
     // dW = [hi; lo]^T [h; h] (L x H)
-    if (gemm_rm(bh, true, false, L, H, 2 * B, dzcat, L, hcat, H, 0.f, dW, H) != rocblas_status_success) return false;
+    if (own_dw) {
+        hipLaunchKernelGGL(k_head_dw, dim3((unsigned)((L + 63) / 64), (unsigned)((H + 767) / 768)), dim3(512), 0,
+                           stream, dzcat, hT, Bp, dW, B, H, L);
+    } else if (gemm_rm(bh, true, false, L, H, 2 * B, dzcat, L, hcat, H, 0.f, dW, H) != rocblas_status_success) {
+        return false;
+    }
     const int64_t m = B * H;
     if (L % 8 == 0 && H % 8 == 0) {
         // per label chunk c: (hi + lo)[:, chunk c] W[chunk c, :] (B x H) on libhaste's kernel

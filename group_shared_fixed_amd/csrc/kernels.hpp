@@ -96,7 +96,7 @@ void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B
 // as bf16 hi / lo, dW = dZ^T h, dh (+)= dZ W; false if rocBLAS fails.
 bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
               float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
-              uint16_t* dzcat, uint16_t* hcat, float* dhcat, void* blas_ws, size_t blas_ws_bytes,
+              uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws, size_t blas_ws_bytes,
               hipStream_t stream);
 // Bytes of caller workspace the head pass hands to rocBLAS.
 constexpr size_t kHeadBlasWorkspace = 64ull << 20;
