@@ -41,7 +41,8 @@ Layout layout(int op, int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
     // grouped dh kernels pick their tile height by shape; the G = 1 baseline uses 16 rows.
     // About two workgroups per CU for 16-row tiles, one for 32-row tiles; the
     // chunk count is a multiple of the 8 XCDs.
-    l.rows = (op == HASTE_OP_BWD_H || op == HASTE_OP_STEP) ? dh_tile_rows((int)G, (int)F, H) : kDhRows;
+    l.rows = (op == HASTE_OP_BWD_H || op == HASTE_OP_STEP) ? dh_tile_rows((int)G, (int)F, H, op == HASTE_OP_STEP)
+                                                           : kDhRows;
     l.ntiles = (int)((B + l.rows - 1) / l.rows);
     const int target = l.rows == 32 ? 256 : 512;
     int nc = (target / l.ntiles) / 8 * 8;

@@ -461,7 +461,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     constexpr int NHH = F / 32;                  // gathered 16-byte pieces per lane per 16-row half
     constexpr int DCH = G / 8;                   // 16-byte chunks of a dZ row
     constexpr int NDH = (16 * DCH + 63) / 64;    // dZ pieces per lane per 16-row half
-    static_assert(G * F <= 2048 && F <= 64, "per-wave tiles sized for eight waves");
+    static_assert(G * F <= 4096 && F <= 128, "per-wave tiles sized for the 32-row workgroup");
+    static_assert(NWV * (G * F + (LAB ? F * 16 : 16 * G)) * 2 + 32 * 768 * 4 + 8 <= 160 * 1024,
+                  "per-wave tiles and a 32 x 768 accumulator fit in LDS");
 
     extern __shared__ __attribute__((aligned(16))) float acc[];   // acc[j * 32 + row], quads swizzled
     __shared__ __attribute__((aligned(16))) uint16_t sW[NWV][G * F];
@@ -775,6 +777,25 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
     for (int64_t i = 0; i < nbatch; ++i) {
         const int64_t rd = RPT * i;
+        if constexpr (F > 64) {
+            // wide tiles (P of both halves is 2 F / 16 result tiles): each
+            // round's P goes into the accumulator at once, a turn per round
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                In& c = (r % 2 == 0) ? sa : sb;
+                In& n = (r % 2 == 0) ? sb : sa;
+                f32x4_t p[2][NT];
+                round(rd + r, c, n, p);
+                const int turn = (int)(NWV * (rd + r)) + wv;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    wait_turn(&sTurn[hf], turn);
+                    if (kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, c.col);
+                    pass_turn(&sTurn[hf], turn);
+                }
+            }
+            continue;
+        }
         f32x4_t p[RPT][2][NT];
         int cl[RPT][NT];
         // every round of the batch runs (past the last round it only issues
@@ -869,40 +890,55 @@ static void launch_kern(dim3 grid, dim3 blk, size_t lds, hipStream_t s, const Dh
     hipLaunchKernelGGL(Kern, grid, blk, lds, s, a);
 }
 
+// Waves of the 32-row kernel: eight, or seven where eight sets of per-wave
+// tiles and the 32 x H accumulator would not fit in LDS (G F = 2048 with the
+// gathered tile of F = 128).
+constexpr int dh32_waves(int G, int F, int src)
+{
+    const int n = (160 * 1024 - 32 * 768 * 4 - 8) / ((G * F + (src == DH_FROM_LABELS ? F * 16 : 16 * G)) * 2);
+    return n < 8 ? n : 8;
+}
+
 template <int G, int F>
 static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s, bool w8)
 {
-    const int rows = dh_tile_rows((int)G, (int)F, a.H);
+    const int rows = dh_tile_rows((int)G, (int)F, a.H, src == DH_FROM_LABELS);
     const size_t lds = (size_t)rows * a.H * sizeof(float);
-    const dim3 grid(a.nchunks * a.ntiles), blk(rows == 32 ? 512 : 256);
+    constexpr int NWL = dh32_waves(G, F, DH_FROM_LABELS), NWZ = dh32_waves(G, F, DH_FROM_DZ);
+    const dim3 grid(a.nchunks * a.ntiles);
+    const dim3 blk(rows == 32 ? 64 * (src == DH_FROM_DZ ? NWZ : NWL) : 256);
 #define go(...) launch_kern<__VA_ARGS__>(grid, blk, lds, s, a)
     if (w8) {
         // FP8 weights: the fused step's kernels (logits recomputed from labels)
         if (src != DH_FROM_LABELS) return false;
-        if constexpr (G * F <= 2048 && F <= 64) {
+        if constexpr (dh32_fits(G, F, true)) {
             if (rows == 32) {
-                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8, 2, true>);
-                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8, 2, true>);
+                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, NWL, 2, true>);
+                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, NWL, 2, true>);
                 return true;
             }
         }
+        if (rows != kDhRows) return false;
         constexpr int RP = dh16_rpt(G, F, DH_FROM_LABELS);
         if (det) go(k_group_dh<G, F, DH_FROM_LABELS, true, RP, true>);
         else go(k_group_dh<G, F, DH_FROM_LABELS, false, RP, true>);
         return true;
     }
-    if constexpr (G * F <= 2048 && F <= 64) {
-        if (rows == 32) {
-            if (src == DH_FROM_DZ) {
-                if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true, 8, 4>);
-                else go(k_group_dh32<G, F, DH_FROM_DZ, false, 8, 4>);
-            } else {
-                if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, 8, 2>);
-                else go(k_group_dh32<G, F, DH_FROM_LABELS, false, 8, 2>);
-            }
+    if constexpr (dh32_fits(G, F, false)) {
+        if (rows == 32 && src == DH_FROM_DZ) {
+            if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true, NWZ, 4>);
+            else go(k_group_dh32<G, F, DH_FROM_DZ, false, NWZ, 4>);
             return true;
         }
     }
+    if constexpr (dh32_fits(G, F, true)) {
+        if (rows == 32 && src == DH_FROM_LABELS) {
+            if (det) go(k_group_dh32<G, F, DH_FROM_LABELS, true, NWL, 2>);
+            else go(k_group_dh32<G, F, DH_FROM_LABELS, false, NWL, 2>);
+            return true;
+        }
+    }
+    if (rows != kDhRows) return false;   // tile height and kernel disagree
     if (src == DH_FROM_DZ) {
         constexpr int RP = dh16_rpt(G, F, DH_FROM_DZ);
         if (det) go(k_group_dh<G, F, DH_FROM_DZ, true, RP>); else go(k_group_dh<G, F, DH_FROM_DZ, false, RP>);

@@ -70,11 +70,20 @@ struct FixedArgs {
 // Each launcher returns false when no kernel exists for (G, F).
 // w8: weights as FP8 codes + group exponents (modes FWD_Z and STEP_DW only).
 bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8 = false);
-// Batch rows per feature-gradient workgroup: 32 (eight waves, one workgroup
-// per CU) when the per-wave tiles and a 32 x H accumulator fit in LDS, else 16.
-inline int dh_tile_rows(int G, int F, int64_t H)
+// Whether the 32-row feature-gradient kernel exists for (G, F) and the dZ
+// source: its per-wave tiles, for at least six waves, and a 32 x 768
+// accumulator fit in LDS without spilling registers.  With a given dZ it is
+// built for F <= 64 only (at F = 128 the 16-row kernel is faster: its P
+// tiles leave room for two groups per accumulator turn).
+constexpr bool dh32_fits(int G, int F, bool from_labels)
 {
-    return (G * F <= 2048 && F <= 64 && H <= 768) ? 32 : kDhRows;
+    return from_labels ? (G * F <= 2048 || (G * F == 4096 && F == 64)) : (G * F <= 2048 && F <= 64);
+}
+// Batch rows per feature-gradient workgroup: 32 (six to eight waves, one
+// workgroup per CU) where that kernel exists and H <= 768, else 16.
+inline int dh_tile_rows(int G, int F, int64_t H, bool from_labels)
+{
+    return (H <= 768 && dh32_fits(G, F, from_labels)) ? 32 : kDhRows;
 }
 // w8: weights as FP8 codes + group exponents (DH_FROM_LABELS only).
 bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s, bool w8 = false);
