@@ -926,8 +926,10 @@ static bool launch_dh_gf(int src, bool det, const DhArgs& a, hipStream_t s, bool
     }
     if constexpr (dh32_fits(G, F, false)) {
         if (rows == 32 && src == DH_FROM_DZ) {
-            if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true, NWZ, 4>);
-            else go(k_group_dh32<G, F, DH_FROM_DZ, false, NWZ, 4>);
+            // four groups per accumulator turn where their P tiles fit in registers
+            constexpr int RZ = G * F <= 2048 ? 4 : 2;
+            if (det) go(k_group_dh32<G, F, DH_FROM_DZ, true, NWZ, RZ>);
+            else go(k_group_dh32<G, F, DH_FROM_DZ, false, NWZ, RZ>);
             return true;
         }
     }

@@ -72,12 +72,13 @@ struct FixedArgs {
 bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8 = false);
 // Whether the 32-row feature-gradient kernel exists for (G, F) and the dZ
 // source: its per-wave tiles, for at least six waves, and a 32 x 768
-// accumulator fit in LDS without spilling registers.  With a given dZ it is
-// built for F <= 64 only (at F = 128 the 16-row kernel is faster: its P
-// tiles leave room for two groups per accumulator turn).
+// accumulator fit in LDS without spilling registers (G F <= 2048, or G = 64
+// with F = 64).  With a given dZ it is built for F <= 64 only (at F = 128
+// the 16-row kernel is faster: its P tiles leave room for two groups per
+// accumulator turn).
 constexpr bool dh32_fits(int G, int F, bool from_labels)
 {
-    return from_labels ? (G * F <= 2048 || (G * F == 4096 && F == 64)) : (G * F <= 2048 && F <= 64);
+    return (G * F <= 2048 || (G * F == 4096 && F == 64)) && (F <= 64 || from_labels);
 }
 // Batch rows per feature-gradient workgroup: 32 (six to eight waves, one
 // workgroup per CU) where that kernel exists and H <= 768, else 16.
