@@ -496,29 +496,44 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                                 }
                         }
                     } else {
+                        // with the loss l = max(z, 0) + ln(1 + e^-|z|) - y z per
+                        // valid row: the logarithms of the lane's 8 GT terms are
+                        // taken once, as the log of their product (each factor
+                        // 1 + e^-|z| lies in [1, 2], so the product stays below 2^32)
+                        float prod = 1.f, lin = 0.f;
 #pragma unroll
                         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const int64_t b = bq + 4 * mt + i;
-                                const bool valid = b < a.B;
-                                const uint64_t mrow = anypos ? sM[wv][b & (kMaxLabelBatch - 1)] : 0ull;
+                                const bool valid = bq + 4 * mt + i < a.B;
 #pragma unroll
                                 for (int gt = 0; gt < GT; ++gt) {
                                     const float zz = z[mt][gt][i];
-                                    const bool y = (mrow >> (16 * gt + r16)) & 1ull;
                                     // u = e^-|z|; sigmoid(|z|) = 1/(1+u); sigmoid(-|z|) = u/(1+u)
                                     const float u = __builtin_amdgcn_exp2f(-fabsf(zz) * kLog2e);
-                                    const float r = __builtin_amdgcn_rcpf(1.0f + u);
-                                    const float sg = zz >= 0.f ? r : u * r;
-                                    float d = scale * sg;
-                                    const float le = fmaxf(zz, 0.f) + __builtin_amdgcn_logf(1.0f + u) * kLn2 -
-                                                     (y ? zz : 0.f);
-                                    lsum += valid ? le : 0.f;
-                                    if (y) d -= scale;
-                                    dz[mt][gt][i] = d;
+                                    const float w1 = 1.0f + u;
+                                    const float r = __builtin_amdgcn_rcpf(w1);
+                                    dz[mt][gt][i] = scale * (zz >= 0.f ? r : u * r);
+                                    prod *= valid ? w1 : 1.0f;
+                                    lin += valid ? fmaxf(zz, 0.f) : 0.f;
                                 }
                             }
+                        if (anypos) {   // rare: positive labels in this group
+#pragma unroll
+                            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const int64_t b = bq + 4 * mt + i;
+                                    const uint64_t mrow = sM[wv][b & (kMaxLabelBatch - 1)];
+#pragma unroll
+                                    for (int gt = 0; gt < GT; ++gt)
+                                        if ((mrow >> (16 * gt + r16)) & 1ull) {
+                                            dz[mt][gt][i] -= scale;
+                                            if (b < a.B) lin -= z[mt][gt][i];
+                                        }
+                                }
+                        }
+                        lsum += lin + __builtin_amdgcn_logf(prod) * kLn2;
                     }
                     if constexpr (STORE_DZ) {
                         uint16_t* so = sDo[wv][ZB > 1 ? (c & 1) : 0];
