@@ -39,6 +39,10 @@ CASES = {
     # G = 64 with F = 128: the 16-row feature-gradient kernel with its
     # largest static LDS, first launched at a small H
     "g64_f128_b45": (45, 200, 9, 64, 128),
+    # the 32-row feature-gradient kernel with seven waves (G = 16, F = 128)
+    # and with six (G = 64, F = 64), each at a small H and a ragged last tile
+    "g16_f128_h200_b45": (45, 200, 23, 16, 128),
+    "g64_f64_h96_b33": (33, 96, 19, 64, 64),
 }
 
 _cache = {}
