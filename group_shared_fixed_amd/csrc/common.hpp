@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -215,5 +217,32 @@ struct LabelCursor {
         return m;
     }
 };
+
+// Raises the dynamic-LDS limit of kernel Kern on the current device to
+// `bytes` when a launch needs more than the default 64 KB (the attribute is
+// per device, and it is only ever raised).  A refused raise is cleared from
+// the thread's last error, so the launch that follows reports its own
+// failure.  Safe to call from several host threads.
+constexpr int kMaxDevices = 64;
+template <auto Kern>
+inline void raise_dyn_lds(size_t bytes)
+{
+    if (bytes <= 64 * 1024) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return;
+    }
+    static std::atomic<size_t> raised[kMaxDevices];
+    size_t cur = raised[dev].load(std::memory_order_relaxed);
+    if (bytes <= cur) return;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    while (cur < bytes && !raised[dev].compare_exchange_weak(cur, bytes, std::memory_order_relaxed)) {
+    }
+}
 
 }  // namespace haste

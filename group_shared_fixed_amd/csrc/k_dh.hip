@@ -873,20 +873,11 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
     }
 }
 
-// Launch with the kernel's dynamic-LDS limit raised to what this launch
-// needs (per kernel, only when it grows).  A refused raise is not left
-// behind as the thread's last error: the launch reports its own failure.
+// Launch with the kernel's dynamic-LDS limit raised to what this launch needs.
 template <void (*Kern)(DhArgs)>
 static void launch_kern(dim3 grid, dim3 blk, size_t lds, hipStream_t s, const DhArgs& a)
 {
-    static size_t raised = 64 * 1024;
-    if (lds > raised) {
-        if (hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) ==
-            hipSuccess)
-            raised = lds;
-        else
-            (void)hipGetLastError();
-    }
+    raise_dyn_lds<Kern>(lds);
     hipLaunchKernelGGL(Kern, grid, blk, lds, s, a);
 }
 

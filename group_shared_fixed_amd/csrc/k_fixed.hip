@@ -235,9 +235,15 @@ bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s)
 {
     const size_t lds = (size_t)kDhRows * dh_stride(a.H) * sizeof(float);
     const dim3 grid(a.nchunks * a.ntiles), blk(256);
+    // 16 x (H + pad) fp32 passes 64 KB for H > 1008
 #define HASTE_FIXED_DH(FF)                                                                           \
-    if (det) hipLaunchKernelGGL((k_fixed_bwd_h<FF, true>), grid, blk, lds, s, a);                    \
-    else hipLaunchKernelGGL((k_fixed_bwd_h<FF, false>), grid, blk, lds, s, a);                       \
+    if (det) {                                                                                       \
+        raise_dyn_lds<k_fixed_bwd_h<FF, true>>(lds);                                                 \
+        hipLaunchKernelGGL((k_fixed_bwd_h<FF, true>), grid, blk, lds, s, a);                         \
+    } else {                                                                                         \
+        raise_dyn_lds<k_fixed_bwd_h<FF, false>>(lds);                                                \
+        hipLaunchKernelGGL((k_fixed_bwd_h<FF, false>), grid, blk, lds, s, a);                        \
+    }                                                                                                \
     return true;
     switch (F) {
     case 32: HASTE_FIXED_DH(32)
