@@ -110,8 +110,16 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     const int64_t L = a.K * G;
     const int64_t nw = (int64_t)gridDim.x * 4;
     const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
-    const int64_t k0 = gw * a.K / nw;
-    const int64_t k1 = (gw + 1) * a.K / nw;
+    // Group order.  The logits-only forward and the standalone dW take groups
+    // gw, gw + nw, gw + 2 nw, ...: the waves in flight then write (Z) or read
+    // (dZ) neighbouring column blocks of the same B x L rows, which measured
+    // 2-12 % faster than one contiguous range per wave.  The label-driven
+    // modes keep contiguous ranges (strided, the fused step measured 11-14 %
+    // slower and the standalone BCE forward 8 % slower at the 3M shape).
+    constexpr bool STRIDED = (MODE == FWD_Z || MODE == BWD_W);
+    const int64_t kstep = STRIDED ? nw : 1;
+    const int64_t k0 = STRIDED ? gw : gw * a.K / nw;
+    const int64_t k1 = STRIDED ? a.K : (gw + 1) * a.K / nw;
     const int nchunk = (int)(a.Bp / 32);
     const int wchunk = nchunk >= 2 ? 1 : 0;   // chunk that requests the next group's weights
     const float scale = a.scale;
@@ -278,8 +286,8 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         if constexpr (PAIRS) load_w(k0, wraw);
     }
 
-    for (int64_t k = k0; k < k1; ++k) {
-        const int64_t kn = k + 1 < k1 ? k + 1 : k;
+    for (int64_t k = k0; k < k1; k += kstep) {
+        const int64_t kn = k + kstep < k1 ? k + kstep : k;
         // the next group's index entries: needed by the last chunk's request,
         // so they are loaded before any chunk of this group
         load_col(kn, col_n);
