@@ -351,10 +351,10 @@ def joint_bench(args):
         "data": "synthetic",
         "config": {"workload": "ht3m_joint_shaped", "L_head": Lh, "L_tail": L, "G": G, "K": K, "F": F, "H": H,
                    "B": B, "positives_per_sample": w.m, "dh_mode": args.mode,
-                   "step": "haste_joint_step: tail haste_step, then the dense head (rocBLAS products + BCE kernel)"},
+                   "step": "haste_joint_step: tail haste_step, then the dense head (logits + BCE, dW and dh kernels)"},
         "useful_tflops": round((head_flops + tail_flops) / (ms_step * 1e-3) / 1e12, 2),
         "branches_us": {"tail_step": round(tail_us, 2), "head_step": round(head_us, 2)},
-        "roofline_head": {"kernel": "head pass (3 rocBLAS GEMMs + BCE + dh sum)", "bound": "hbm",
+        "roofline_head": {"kernel": "head pass (logits + BCE, dW, dh, dh sum)", "bound": "hbm",
                           "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": head_bytes,
                           "avg_us": round(head_us, 2), "head_tflops": round(head_flops / (head_us * 1e-6) / 1e12, 2)},

@@ -426,7 +426,7 @@ int head_pass(const haste_bf16* h, const haste_bf16* W, const int32_t* y_rowptr,
     const HeadLayout l(B, H, L);
     char* w = (char*)workspace;
     float* zbuf = Z ? Z : (float*)(w + l.z);
-    if (!run_head(h, W, y_rowptr, y_col, scale, dW, dh, zbuf, loss, B, H, L, accumulate, (uint16_t*)(w + l.dz),
+    if (!run_head(h, W, y_rowptr, y_col, scale, dW, dh, zbuf, Z != nullptr, loss, B, H, L, accumulate, (uint16_t*)(w + l.dz),
                   (uint16_t*)(w + l.hcat), (float*)(w + l.dhcat), (uint16_t*)(w + l.hT), w + l.blas,
                   kHeadBlasWorkspace, stream))
         return HASTE_ERR_HIP;

@@ -3,15 +3,16 @@
 // HASTE "head-tail split" section: the most frequent labels go to a dense
 // head (every label sees all H features) and the rest to the group-shared
 // sparse tail; one BCE objective covers both.  The head's three products are
-// plain dense GEMMs (Z = h W^T, dW = dZ^T h, dh = dZ W) and run on rocBLAS
-// (bf16 in, fp32 accumulate and out); the BCE gradient between them is the
-// kernel below.  dZ goes to the GEMMs as two bf16 matrices, hi and the
-// rounding residual lo, so the two weight-side products carry about 16
-// significant bits of dZ, as the tail's fused kernels do.  The two parts are
-// stacked (hi rows 0..B-1, lo rows B..2B-1) so that each weight-side product
-// is one GEMM that reads W or writes dW once: dW = [hi; lo]^T [h; h] (a
-// 2B-deep contraction) and dh = [hi; lo] W (2B rows, whose halves are then
-// added).
+// plain dense GEMMs (Z = h W^T, dW = dZ^T h, dh = dZ W), bf16 in, fp32
+// accumulate and out.  For B <= 128, H % 64 == 0 and L % 8 == 0 they run on
+// the kernels below (logits and BCE gradient fused in k_head_zbce); other
+// shapes use rocBLAS for the products and k_head_bce between them.  dZ goes
+// to the weight-side products as two bf16 matrices, hi and the rounding
+// residual lo, so they carry about 16 significant bits of dZ, as the tail's
+// fused kernels do.  The two parts are stacked (hi rows 0..B-1, lo rows
+// B..2B-1) so that each weight-side product reads W or writes dW once:
+// dW = [hi; lo]^T [h; h] (a 2B-deep contraction) and dh = [hi; lo] W (2B
+// rows, whose halves are then added).
 #include "blas.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -101,6 +102,195 @@ __global__ __launch_bounds__(256) void k_head_bce(const float* __restrict__ Z, c
     }
 }
 
+
+// Logits and BCE gradient of the dense head in one pass: Z = h W^T on matrix
+// cores with the epilogue of k_head_bce applied to the accumulators, so Z
+// never goes through HBM unless asked for.  A workgroup owns 128 labels
+// (wave wv: labels 32 wv .. +31, two 16-label tiles) and all rows (B <= 128,
+// up to eight 16-row tiles); the contraction over H runs in stages of 64:
+// h[:, stage] is staged in LDS for the four waves (rows' 16-byte chunks
+// XOR-swizzled with (row / 2) % 8 so the operand reads of 16 rows spread over
+// the banks), the weights go from global memory straight into the B operand
+// (a label's four lanes read 64 contiguous bytes) with plain loads, so the dh
+// product that reads W next can find it in the last-level cache.  The
+// epilogue stages each 16-row tile's hi / lo parts in LDS and stores 64
+// contiguous bytes per row; Z (optional) is stored directly.
+constexpr int kHzLabels = 128;   // labels per workgroup
+constexpr int kHzStage = 64;     // contraction width per LDS stage
+__global__ __launch_bounds__(256) void k_head_zbce(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                   const int32_t* __restrict__ rowptr,
+                                                   const int32_t* __restrict__ col, float scale,
+                                                   float* __restrict__ Z, uint16_t* __restrict__ dz_hi,
+                                                   uint16_t* __restrict__ dz_lo, double* __restrict__ loss,
+                                                   int64_t B, int64_t H, int64_t L)
+{
+    constexpr int NRT = 8;                      // row tiles (B <= 128)
+    constexpr int CH = kHzStage / 8;            // 16-byte chunks per staged row
+    __shared__ __attribute__((aligned(16))) uint16_t sh[2][128 * kHzStage];
+    __shared__ uint32_t sY[128][4];             // label bits per row: word wv <-> the wave's 32 labels
+    __shared__ __attribute__((aligned(16))) uint16_t sD[4][2][16 * 32];   // per wave: hi / lo, 16 rows x 32 labels
+    __shared__ float red[4];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t L0 = (int64_t)blockIdx.x * kHzLabels;
+    const int64_t lw = L0 + 32 * wv;            // the wave's first label
+    const int nrt = (int)((B + 15) / 16);
+    const int nst = (int)(H / kHzStage);
+
+    // label bits of the block's 128 labels, one row per thread, found before
+    // the first loads are issued (issuing the loads first and searching under
+    // them measured 10 % slower per head pass)
+    auto label_bits = [&]() {
+        if (threadIdx.x < 128) {
+            uint32_t m[4] = {0u, 0u, 0u, 0u};
+            const int64_t b = threadIdx.x;
+            if (b < B) {
+                int lo = rowptr[b], hi = rowptr[b + 1];
+                const int end = hi;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if ((int64_t)col[mid] < L0) lo = mid + 1; else hi = mid;
+                }
+                for (int p = lo; p < end && (int64_t)col[p] < L0 + kHzLabels; ++p) {
+                    const int c = (int)((int64_t)col[p] - L0);
+                    m[c >> 5] |= 1u << (c & 31);
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) sY[threadIdx.x][w] = m[w];
+        }
+    };
+
+    // h stage loads: piece u = threadIdx.x + 256 j is row u / CH, chunk u % CH
+    auto load_h = [&](int st, u32x4_t (&hv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int u = threadIdx.x + 256 * j;
+            const int64_t b = u / CH;
+            hv[j] = b < B ? ldg16(h + b * H + (int64_t)st * kHzStage + 8 * (u % CH)) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_h = [&](int buf, const u32x4_t (&hv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int u = threadIdx.x + 256 * j;
+            const int r = u / CH, c = u % CH;
+            *reinterpret_cast<u32x4_t*>(&sh[buf][r * kHzStage + 8 * (c ^ ((r >> 1) & 7))]) = hv[j];
+        }
+    };
+    // B operand: label lw + 16 lt + r16 (clamped into range), k = stage + 32 s + 8 q ..
+    auto load_w = [&](int st, u32x4_t (&wv4)[2][2]) {
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+            int64_t l = lw + 16 * lt + r16;
+            l = l < L ? l : L - 1;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                wv4[lt][s] = ldg16(W + l * H + (int64_t)st * kHzStage + 32 * s + 8 * q);
+        }
+    };
+
+    f32x4_t acc[NRT][2];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        acc[rt][0] = zero4();
+        acc[rt][1] = zero4();
+    }
+    // the weights of stage st + 2 are requested while stage st runs (a ring of
+    // three register sets; every wait for the current stage's weights leaves
+    // the next two stages' loads in flight)
+    u32x4_t hv[4], w0[2][2], w1[2][2], w2[2][2];
+    label_bits();
+    load_w(0, w0);
+    if (nst > 1) load_w(1, w1);
+    load_h(0, hv);
+    store_h(0, hv);
+    __syncthreads();
+    auto stage = [&](int st, const u32x4_t (&cur)[2][2], u32x4_t (&far)[2][2]) {
+        if (st >= nst) return;                 // uniform over the workgroup
+        const bool more = st + 1 < nst;
+        if (more) load_h(st + 1, hv);
+        if (st + 2 < nst) load_w(st + 2, far);
+        const uint16_t* tile = sh[st & 1];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                if (rt < nrt) {
+                    const int r = 16 * rt + r16, c = 4 * s + q;
+                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&tile[r * kHzStage + 8 * (c ^ ((r >> 1) & 7))]);
+                    acc[rt][0] = mfma16(av, cur[0][s], acc[rt][0]);
+                    acc[rt][1] = mfma16(av, cur[1][s], acc[rt][1]);
+                }
+            }
+        }
+        if (more) store_h((st + 1) & 1, hv);
+        __syncthreads();
+    };
+    for (int st = 0; st < nst; st += 3) {
+        stage(st, w0, w2);
+        stage(st + 1, w1, w0);
+        stage(st + 2, w2, w1);
+    }
+
+    // epilogue: lane holds label lw + 16 lt + r16, rows 16 rt + 4 q + i
+    float lsum = 0.f;
+    uint16_t* th = sD[wv][0];
+    uint16_t* tl = sD[wv][1];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        if (rt >= nrt) break;
+        float prod = 1.f, lin = 0.f;
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+            const int64_t l = lw + 16 * lt + r16;
+            const bool lok = l < L;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rt + 4 * q + i;
+                const bool ok = lok && r < B;
+                const float z = acc[rt][lt][i];
+                const bool y = (sY[r][wv] >> (16 * lt + r16)) & 1u;
+                // u = e^-|z|: sigmoid(|z|) = 1 / (1 + u), sigmoid(-|z|) = u / (1 + u)
+                const float u = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
+                const float w1 = 1.0f + u;
+                const float rc = __builtin_amdgcn_rcpf(w1);
+                const float sg = z >= 0.f ? rc : u * rc;          // sigmoid(z)
+                const float om = z >= 0.f ? u * rc : rc;          // 1 - sigmoid(z)
+                const float d = y ? -scale * om : scale * sg;
+                const uint32_t hb = pack_bf16(d, 0.f) & 0xffffu;
+                const uint32_t lb = pack_bf16(d - __uint_as_float(hb << 16), 0.f) & 0xffffu;
+                th[(4 * q + i) * 32 + 16 * lt + r16] = (uint16_t)hb;
+                tl[(4 * q + i) * 32 + 16 * lt + r16] = (uint16_t)lb;
+                if (Z && ok) Z[(int64_t)r * L + l] = z;
+                if (loss) {
+                    prod *= ok ? w1 : 1.0f;
+                    lin += ok ? fmaxf(z, 0.f) - (y ? z : 0.f) : 0.f;
+                }
+            }
+        }
+        if (loss) lsum += lin + __builtin_amdgcn_logf(prod) * kLn2;
+        wave_sync();
+        // 16 rows x 32 labels: lane -> row lane / 4, labels 8 (lane % 4) ..
+        const int64_t b = 16 * rt + (lane >> 2);
+        const int64_t l0 = lw + 8 * (lane & 3);
+        const u32x4_t vh = *reinterpret_cast<const u32x4_t*>(&th[(lane >> 2) * 32 + 8 * (lane & 3)]);
+        const u32x4_t vl = *reinterpret_cast<const u32x4_t*>(&tl[(lane >> 2) * 32 + 8 * (lane & 3)]);
+        if (b < B && l0 < L) {
+            *reinterpret_cast<u32x4_t*>(dz_hi + b * L + l0) = vh;
+            *reinterpret_cast<u32x4_t*>(dz_lo + b * L + l0) = vl;
+        }
+        wave_sync();
+    }
+    if (loss) {
+        const float w = wave_sum(lsum);
+        if (lane == 0) red[wv] = w;
+        __syncthreads();
+        if (threadIdx.x == 0) atomicAdd(loss, (double)((red[0] + red[1]) + (red[2] + red[3])) * (double)scale);
+    }
+}
 
 // dh = base + the sum over the S label chunks of their partial products, in
 // chunk order (base = dh when accumulating, else 0).  halves = 2: each
@@ -321,9 +511,9 @@ __global__ __launch_bounds__(512) void k_head_dw(const uint16_t* __restrict__ dz
 // contraction into label chunks (a strided batch of GEMMs) is what spreads
 // it over the chip.  Returns false if a rocBLAS call or a copy fails.
 bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
-              float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
-              uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws, size_t blas_ws_bytes,
-              hipStream_t stream)
+              float* dW, float* dh, float* zbuf, bool want_z, double* loss, int64_t B, int64_t H, int64_t L,
+              bool accumulate_dh, uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws,
+              size_t blas_ws_bytes, hipStream_t stream)
 {
     rocblas_handle bh = blas_handle(stream, blas_ws, blas_ws_bytes);
     if (!bh) return false;
@@ -336,11 +526,17 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
         if (hipMemcpyAsync(hcat, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
         if (hipMemcpyAsync(hcat + B * H, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
     }
-    // Z = h W^T (B x L)
-    if (gemm_rm(bh, false, true, B, L, H, h, H, W, H, 0.f, zbuf, L) != rocblas_status_success) return false;
-    const int64_t n = B * ((L + 7) / 8);
-    hipLaunchKernelGGL(k_head_bce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zbuf, rowptr, col, scale,
-                       dzcat, dzcat + B * L, loss, B, L);
+    if (B <= 128 && H % kHzStage == 0 && L % 8 == 0) {
+        // Z and the BCE gradient in one kernel (Z stored only when asked for)
+        hipLaunchKernelGGL(k_head_zbce, dim3((unsigned)((L + kHzLabels - 1) / kHzLabels)), dim3(256), 0, stream, h,
+                           W, rowptr, col, scale, want_z ? zbuf : nullptr, dzcat, dzcat + B * L, loss, B, H, L);
+    } else {
+        // Z = h W^T (B x L) on rocBLAS, then the BCE gradient
+        if (gemm_rm(bh, false, true, B, L, H, h, H, W, H, 0.f, zbuf, L) != rocblas_status_success) return false;
+        const int64_t n = B * ((L + 7) / 8);
+        hipLaunchKernelGGL(k_head_bce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zbuf, rowptr, col,
+                           scale, dzcat, dzcat + B * L, loss, B, L);
+    }
     // dW = [hi; lo]^T [h; h] (L x H)
     if (own_dw) {
         hipLaunchKernelGGL(k_head_dw, dim3((unsigned)((L + 63) / 64), (unsigned)((H + 767) / 768)), dim3(512), 0,

@@ -102,12 +102,13 @@ void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s);
 void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B, int64_t L, int32_t* bad,
                             hipStream_t s);
-// Dense head pass (head-tail split): Z = h W^T into zbuf, the BCE gradient
-// as bf16 hi / lo, dW = dZ^T h, dh (+)= dZ W; false if rocBLAS fails.
+// Dense head pass (head-tail split): Z = h W^T (into zbuf when want_z; the
+// rocBLAS path always fills it), the BCE gradient as bf16 hi / lo,
+// dW = dZ^T h, dh (+)= dZ W; false if rocBLAS fails.
 bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const int32_t* col, float scale,
-              float* dW, float* dh, float* zbuf, double* loss, int64_t B, int64_t H, int64_t L, bool accumulate_dh,
-              uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws, size_t blas_ws_bytes,
-              hipStream_t stream);
+              float* dW, float* dh, float* zbuf, bool want_z, double* loss, int64_t B, int64_t H, int64_t L,
+              bool accumulate_dh, uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws,
+              size_t blas_ws_bytes, hipStream_t stream);
 // Bytes of caller workspace the head pass hands to rocBLAS.
 constexpr size_t kHeadBlasWorkspace = 64ull << 20;
 // Labels per chunk of the head's split feature-gradient product, and the

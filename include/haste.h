@@ -169,13 +169,16 @@ int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf1
  * dW_head = dZ^T h and dh = dZ W_head.  W_head is L_head x H bf16
  * row-major, dW_head L_head x H fp32 and dh B x H fp32 (both overwritten),
  * Z_head (nullable) B x L_head fp32, loss (nullable) 1 double, set to
- * scale * sum [max(z,0) + log(1 + e^-|z|) - y z].  The three products run on
- * rocBLAS (bf16 in, fp32 accumulate and out, atomics off: Z, dW_head and dh
- * are bitwise repeatable; the loss is summed with atomics).  dZ reaches the
- * two weight-side products as stacked bf16 hi + lo parts (about 16
- * significant bits).  The BCE gradient is a libhaste kernel.  The rocBLAS
- * handle is created on the first call of a host thread on a device and kept
- * for the process; each call hands it part of `workspace`.  Limits: B <=
+ * scale * sum [max(z,0) + log(1 + e^-|z|) - y z].  Products: bf16 in, fp32
+ * accumulate and out.  For B <= 128, H % 64 == 0 and L_head % 8 == 0 all
+ * three run on libhaste's matrix-core kernels (the logits fused with the
+ * BCE gradient); other shapes run them on rocBLAS (atomics off) with a
+ * libhaste BCE kernel between them.  Either way Z, dW_head and dh are
+ * bitwise repeatable; the loss is summed with atomics.  dZ reaches the two
+ * weight-side products as stacked bf16 hi + lo parts (about 16 significant
+ * bits).  The rocBLAS handle is created on the first call of a host thread
+ * on a device and kept for the process; each call hands it part of
+ * `workspace`.  Limits: B <=
  * 2^24, H <= 2^20, L_head < 2^31 - 64.  Errors as haste_step.  Workspace:
  * haste_head_workspace_size(B, H, L_head) bytes, 256-byte aligned. */
 size_t haste_head_workspace_size(int64_t B, int64_t H, int64_t L_head);

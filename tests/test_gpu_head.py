@@ -19,8 +19,11 @@ pytestmark = pytest.mark.gpu
 # feature-gradient kernel, here with two 128-row blocks and a partial
 # column block), batches around 128, and label counts past one or several
 # feature-gradient chunks of 1024 labels
+# B <= 128, H % 64 == 0 and L % 8 == 0 take the fused logits + BCE kernel
+# (e.g. (64, 128, 256), (128, 768, 2048), (64, 256, 5000), (37, 192, 200));
+# the others the rocBLAS logits and the separate BCE kernel
 HEAD_CASES = [(1, 16, 1), (5, 40, 13), (64, 128, 256), (37, 96, 73), (130, 264, 1001), (128, 768, 2048),
-              (64, 256, 5000), (130, 200, 1000), (3, 8, 8)]
+              (64, 256, 5000), (130, 200, 1000), (3, 8, 8), (37, 192, 200), (1, 64, 8)]
 
 
 def _head_inputs(B, H, L, seed):
@@ -47,8 +50,9 @@ def test_head_step(shape):
     assert abs(loss - ref["loss"]) <= 1e-5 * abs(ref["loss"])
 
 
-def test_head_step_repeatable_and_optional_outputs():
-    B, H, L = 96, 256, 777
+@pytest.mark.parametrize("L", [777, 776])
+def test_head_step_repeatable_and_optional_outputs(L):
+    B, H = 96, 256
     h, W, rp, col = _head_inputs(B, H, L, 41)
     d = [to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(rp), to_dev_i32(col)]
     a = hs.head_step(*d, 1.0 / B, want_Z=True, want_loss=True)
