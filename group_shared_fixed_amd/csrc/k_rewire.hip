@@ -142,37 +142,38 @@ __global__ __launch_bounds__(64 * NW) void k_rewire_score(const uint16_t* __rest
                 for (int r = 0; r < RT; ++r) acc[r][t] = mfma16(a[ks][r], bop, acc[r][t]);
             }
         }
-        // |gradient| summed over each row tile's 16 labels, per column (in
-        // lane, then across the four lane groups), then over the row tiles
-        // of a group in increasing order; the wave's labels hold whole groups
-        float rs[RT][kRwColTiles];
+        // |gradient| summed over each row tile's 16 labels in lane, over the
+        // row tiles of a group in increasing order (the wave's labels hold
+        // whole groups), then across the four lane groups by an exchange in
+        // two steps that leaves lane group q with column tile q: three lane
+        // shuffles per group
+        float xs[RT][kRwColTiles];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
 #pragma unroll
             for (int t = 0; t < kRwColTiles; ++t) {
                 const f32x4_t v = acc[r][t];
-                float x = ((fabsf(v[0]) + fabsf(v[1])) + fabsf(v[2])) + fabsf(v[3]);
-                x += __shfl_xor(x, 16, 64);
-                x += __shfl_xor(x, 32, 64);
-                rs[r][t] = x;
+                xs[r][t] = ((fabsf(v[0]) + fabsf(v[1])) + fabsf(v[2])) + fabsf(v[3]);
             }
         }
-        // lane group q writes column tile q (16 lanes, 64 contiguous bytes)
         static_assert(kRwColTiles == 4, "one column tile per lane group");
+        const int hq = q >> 1, lq = q & 1;
 #pragma unroll
         for (int r0 = 0; r0 < RT; ++r0) {
             if (r0 % gpw != 0) continue;
             float s[kRwColTiles];
 #pragma unroll
             for (int t = 0; t < kRwColTiles; ++t) {
-                s[t] = rs[r0][t];
+                s[t] = xs[r0][t];
 #pragma unroll
                 for (int u = 1; u < RT; ++u)
-                    if (u < gpw && r0 + u < RT) s[t] += rs[r0 + u][t];
+                    if (u < gpw && r0 + u < RT) s[t] += xs[r0 + u][t];
             }
-            float mine = s[0];
-#pragma unroll
-            for (int t = 1; t < kRwColTiles; ++t) mine = q == t ? s[t] : mine;
+            // step 1 (lane groups q, q ^ 2): keep tiles 2 hq, 2 hq + 1
+            const float u0 = (hq ? s[2] : s[0]) + __shfl_xor(hq ? s[0] : s[2], 32, 64);
+            const float u1 = (hq ? s[3] : s[1]) + __shfl_xor(hq ? s[1] : s[3], 32, 64);
+            // step 2 (lane groups q, q ^ 1): keep tile q
+            const float mine = (lq ? u1 : u0) + __shfl_xor(lq ? u0 : u1, 16, 64);
             const int64_t k = (wl0 + 16 * r0) / G;
             const int64_t j = (int64_t)pass * kRwCols + 16 * q + i16;
             if (k < K && j < H) grow[k * H + j] = mine;
@@ -345,13 +346,16 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
     }
 }
 
-// Eight waves per workgroup (two per SIMD, up to 256 registers each); four
-// for the longest batches, whose operands need more registers.
+// Waves per workgroup: eight (two per SIMD) in general; four at 128 rows,
+// where two four-wave workgroups still fit on a CU and run their passes out
+// of step, so one's lane reductions overlap the other's products (733
+// against 769 us for eight waves); four for the longest batches, whose
+// operands need more registers.
 template <int KS>
 static void score_launch(const uint16_t* hT, int64_t Bp, int64_t B, int64_t H, const uint16_t* dZ, int64_t L, int G,
                          float* grow, hipStream_t s)
 {
-    constexpr int RT = 4, NW = KS <= 6 ? 8 : 4;
+    constexpr int RT = 4, NW = (KS == 4 || KS >= 7) ? 4 : 8;
     const int64_t per = NW * RT * 16;
     hipLaunchKernelGGL((k_rewire_score<KS, RT, NW>), dim3((unsigned)((L + per - 1) / per)), dim3(NW * 64), 0, s, hT,
                        Bp, B, H, dZ, L, G, grow);
