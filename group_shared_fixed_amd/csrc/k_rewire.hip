@@ -24,6 +24,18 @@ namespace haste {
 namespace {
 
 constexpr int kRwCols = 64;     // feature columns per pass
+
+// Lane moves within rows of 16 lanes (DPP), every lane reading a valid lane.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
 constexpr int kRwColTiles = kRwCols / 16;
 
 __host__ __device__ constexpr int pow2_at_least(int x)
@@ -284,15 +296,21 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
                 bj = lane + 64 * t;
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oj = __shfl_xor(bj, o, 64);
+        // wave arg-max; the pick (larger score, then lower id) is a total
+        // order, so any pairing of lanes works: within quads, 8-lane halves
+        // and 16-lane rows by DPP moves, then across rows by lane shuffles
+        auto take = [&](float ov, int oj) {
             if (ov > bv || (ov == bv && oj < bj)) {
                 bv = ov;
                 bj = oj;
             }
-        }
+        };
+        take(dpp_f32<0xB1>(bv), dpp_i32<0xB1>(bj));    // quad_perm [1, 0, 3, 2]
+        take(dpp_f32<0x4E>(bv), dpp_i32<0x4E>(bj));    // quad_perm [2, 3, 0, 1]
+        take(dpp_f32<0x141>(bv), dpp_i32<0x141>(bj));  // row_half_mirror
+        take(dpp_f32<0x140>(bv), dpp_i32<0x140>(bj));  // row_mirror
+        take(__shfl_xor(bv, 16, 64), __shfl_xor(bj, 16, 64));
+        take(__shfl_xor(bv, 32, 64), __shfl_xor(bj, 32, 64));
         if ((bj & 63) == lane) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
