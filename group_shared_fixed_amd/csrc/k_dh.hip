@@ -852,6 +852,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
     f32x4_t s = zero4();
     if (ok) {
         const float* p = part + b * H + j;
+#pragma unroll 4
         for (int c = sub; c < nchunks; c += 4)
             s += *reinterpret_cast<const f32x4_t*>(p + c * stride);
     }
