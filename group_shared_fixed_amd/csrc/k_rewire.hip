@@ -286,21 +286,40 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
         const int64_t j = lane + 64 * t;
         if (j < H && ((sKept[w][j >> 5] >> (j & 31)) & 1u)) v[t] = -1.0f;
     }
-    for (int round = 0; round < n_swap; ++round) {
-        float bv = -2.0f;
-        int bj = 0x7fffffff;
+    // Each lane keeps its best two candidates (larger score, then lower id);
+    // a round reduces the lanes' bests, the winning lane promotes its second,
+    // and a lane that has won twice since its last scan rescans its values
+    // (taken ones marked below every candidate).
+    auto better = [](float a, int ja, float b, int jb) { return a > b || (a == b && ja < jb); };
+    struct Top2 {
+        float v1, v2;
+        int j1, j2;
+    };
+    auto scan = [&]() -> Top2 {
+        Top2 r{-2.0f, -2.0f, 0x7fffffff, 0x7fffffff};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (v[t] > bv) {
-                bv = v[t];
-                bj = lane + 64 * t;
-            }
+            const float x = v[t];
+            const int jx = lane + 64 * t;
+            const bool b1 = better(x, jx, r.v1, r.j1);
+            const bool b2 = better(x, jx, r.v2, r.j2);
+            r.v2 = b1 ? r.v1 : (b2 ? x : r.v2);
+            r.j2 = b1 ? r.j1 : (b2 ? jx : r.j2);
+            r.v1 = b1 ? x : r.v1;
+            r.j1 = b1 ? jx : r.j1;
         }
-        // wave arg-max; the pick (larger score, then lower id) is a total
-        // order, so any pairing of lanes works: within quads, 8-lane halves
-        // and 16-lane rows by DPP moves, then across rows by lane shuffles
+        return r;
+    };
+    Top2 c = scan();
+    int have = 2;
+    for (int round = 0; round < n_swap; ++round) {
+        float bv = c.v1;
+        int bj = c.j1;
+        // wave arg-max; the pick is a total order, so any pairing of lanes
+        // works: within quads, 8-lane halves and 16-lane rows by DPP moves,
+        // then across rows by lane shuffles
         auto take = [&](float ov, int oj) {
-            if (ov > bv || (ov == bv && oj < bj)) {
+            if (better(ov, oj, bv, bj)) {
                 bv = ov;
                 bj = oj;
             }
@@ -316,6 +335,16 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
             for (int t = 0; t < NT; ++t)
                 if (t == (bj >> 6)) v[t] = -3.0f;
             atomicOr(&sNew[w][bj >> 5], 1u << (bj & 31));
+            c.v1 = c.v2;
+            c.j1 = c.j2;
+            --have;
+        }
+        if (__any(have == 0)) {
+            const Top2 r = scan();
+            if (have == 0) {
+                c = r;
+                have = 2;
+            }
         }
     }
     wave_sync();
