@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_head_zbce(const uint16_t* __restrict__ 
                 }
                 for (int p = lo; p < end && (int64_t)col[p] < L0 + kHzLabels; ++p) {
                     const int c = (int)((int64_t)col[p] - L0);
-                    m[c >> 5] |= 1u << (c & 31);
+                    if (c >= 0) m[c >> 5] |= 1u << (c & 31);   // rows are sorted; guards a malformed one
                 }
             }
 #pragma unroll
