@@ -194,8 +194,9 @@ __global__ __launch_bounds__(64 * NW) void k_rewire_score(const uint16_t* __rest
 }
 
 // One wave per group: prune scores, the drop set, the grown columns, the new
-// sorted index row and the permuted weights.  W_k and the index row are read
-// into LDS before anything is written, so idx_out / W_out may be idx / W.
+// sorted index row and the permuted weights.  W_k is read into LDS and the
+// index row into registers (every lane's columns are used by every lane's
+// rank before anything is written), so idx_out / W_out may be idx / W.
 template <int G, int F>
 __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const uint16_t* W,
                                                        const float* __restrict__ grow, int64_t K, int64_t H,
@@ -206,8 +207,6 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
     constexpr int NCHUNK = G * F / 8;              // 16-byte pieces of W_k
     constexpr int FPL = (F + 63) / 64;             // slots per lane
     __shared__ uint16_t sW[NW][G * F];
-    __shared__ int32_t sCol[NW][F];
-    __shared__ float sPr[NW][F];
     __shared__ uint32_t sKept[NW][32];
     __shared__ uint32_t sNew[NW][32];
     __shared__ int16_t sSlot[NW][1024];
@@ -232,13 +231,12 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
         const int c = lane + 64 * i;
         if (c < NCHUNK) *reinterpret_cast<u32x4_t*>(&sW[w][8 * c]) = ldg16(Wk + 8 * c);
     }
+    int colr[FPL];                                 // the lane's slots' columns
 #pragma unroll
     for (int i = 0; i < FPL; ++i) {
         const int f = lane + 64 * i;
-        if (f < F) {
-            sCol[w][f] = idx[k * F + f];
-            sSrc[w][f] = -1;
-        }
+        colr[i] = f < F ? idx[k * F + f] : 0;
+        if (f < F) sSrc[w][f] = -1;
     }
     if (lane < 32) {
         sKept[w][lane] = 0u;
@@ -254,27 +252,31 @@ __global__ __launch_bounds__(256) void k_rewire_select(const int32_t* idx, const
         float s = 0.f;
         if (f < F) {
             for (int g = 0; g < G; ++g) s += fabsf(__uint_as_float((uint32_t)sW[w][g * F + f] << 16));
-            sPr[w][f] = s;
             if (prune_out) prune_out[k * F + f] = s;
         }
         pr[i] = s;
     }
     wave_sync();
-    // drop the n_swap smallest (prune score, column id); record the kept columns
+    // drop the n_swap smallest (prune score, column id); record the kept
+    // columns.  A slot's rank counts the slots below it; the other slots'
+    // scores and columns come from their lanes' registers (lane reads).
 #pragma unroll
     for (int i = 0; i < FPL; ++i) {
         const int f = lane + 64 * i;
-        if (f < F) {
-            const int col = sCol[w][f];
-            int rank = 0;
-            for (int u = 0; u < F; ++u) {
-                const float pu = sPr[w][u];
-                rank += (pu < pr[i] || (pu == pr[i] && sCol[w][u] < col)) ? 1 : 0;
+        int rank = 0;
+#pragma unroll
+        for (int i2 = 0; i2 < FPL; ++i2) {
+            const int nu = F - 64 * i2 < 64 ? F - 64 * i2 : 64;
+            for (int u = 0; u < nu; ++u) {
+                const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr[i2]), u));
+                const int cu = __builtin_amdgcn_readlane(colr[i2], u);
+                rank += (pu < pr[i] || (pu == pr[i] && cu < colr[i])) ? 1 : 0;
             }
-            if (rank >= n_swap) {
-                atomicOr(&sKept[w][col >> 5], 1u << (col & 31));
-                sSlot[w][col] = (int16_t)f;
-            }
+        }
+        if (f < F && rank >= n_swap) {
+            const int col = colr[i];
+            atomicOr(&sKept[w][col >> 5], 1u << (col & 31));
+            sSlot[w][col] = (int16_t)f;
         }
     }
     wave_sync();
