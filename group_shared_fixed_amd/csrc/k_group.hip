@@ -288,13 +288,16 @@ __global__ __launch_bounds__(1024) void k_group_scan(const int32_t* __restrict__
 
 // One wave per cluster.  Members are the sorted keys' positions start[c] ..
 // end[c] (label ids increasing); member i belongs to lane i % 64, which alone
-// reads and writes its similarity and taken flag (in the workspace, at the
-// member's key position).  Per group: the seed is the lowest untaken member
-// (wave minimum of the lanes' cursors); its embedding goes to LDS as fp32;
-// each lane computes the dot products of its untaken members (h ascending);
+// reads and writes its similarity and taken flag (in LDS for clusters of up
+// to kGreedyLds members, else in the workspace at the member's key
+// position).  Per group: the seed is the lowest untaken member (wave minimum
+// of the lanes' cursors); its embedding goes to LDS as fp32; each lane
+// computes the dot products of its untaken members (four partial sums over
+// interleaved 8-feature pieces, four loads in flight, added pairwise);
 // G - 1 rounds of a wave arg-max (larger similarity, then lower index) pick
 // the neighbours; the group's member indices are sorted and written out.
 // Leftovers go out in index order after the cluster's groups.
+constexpr int kGreedyLds = 1024;   // members per cluster kept in LDS
 __global__ __launch_bounds__(256) void k_group_greedy(const uint16_t* __restrict__ E, const uint64_t* __restrict__ keys,
                                                       const int32_t* __restrict__ start,
                                                       const int32_t* __restrict__ end,
@@ -306,6 +309,8 @@ __global__ __launch_bounds__(256) void k_group_greedy(const uint16_t* __restrict
 {
     __shared__ float seedv[4][1024];
     __shared__ int gidx[4][64];
+    __shared__ float sSim[4][kGreedyLds];
+    __shared__ uint8_t sTaken[4][kGreedyLds];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * 4 + w;
     if (c >= C) return;                            // whole wave; no block barrier below
@@ -313,40 +318,61 @@ __global__ __launch_bounds__(256) void k_group_greedy(const uint16_t* __restrict
     if (m <= 0) return;
     const int ng = m / G;
     auto label = [&](int i) { return (int32_t)(uint32_t)keys[s0 + i]; };
+    // per-member state: LDS for small clusters (cleared here), else the
+    // workspace (cleared by the launcher)
+    const bool small = m <= kGreedyLds;
+    float* const simp = small ? sSim[w] : sim + s0;
+    uint8_t* const tk = small ? sTaken[w] : taken + s0;
+    if (small)
+        for (int i = lane; i < m; i += 64) tk[i] = 0;
+    wave_sync();
     int cur = lane;                                // lane's lowest member not yet taken
     for (int gi = 0; gi < ng; ++gi) {
-        while (cur < m && taken[s0 + cur]) cur += 64;
+        while (cur < m && tk[cur]) cur += 64;
         int seed = cur < m ? cur : 0x7fffffff;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             const int x = __shfl_xor(seed, o, 64);
             seed = x < seed ? x : seed;
         }
-        if ((seed & 63) == lane) taken[s0 + seed] = 1;
+        if ((seed & 63) == lane) tk[seed] = 1;
         const uint16_t* es = E + (int64_t)label(seed) * H;
         for (int64_t h = lane; h < H; h += 64) seedv[w][h] = __uint_as_float((uint32_t)es[h] << 16);
         wave_sync();
         for (int i = lane; i < m; i += 64) {
-            if (taken[s0 + i]) continue;
+            if (tk[i]) continue;
             const uint16_t* e = E + (int64_t)label(i) * H;
-            float d = 0.f;
-            for (int64_t h = 0; h < H; h += 8) {
+            float d[4] = {0.f, 0.f, 0.f, 0.f};      // partial sums over pieces h / 8 mod 4
+            int64_t h = 0;
+            for (; h + 32 <= H; h += 32) {
+                u32x4_t p[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) p[u] = ldg16(e + h + 8 * u);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        d[u] = fmaf(bf16lo_to_f32(p[u][q]), seedv[w][h + 8 * u + 2 * q], d[u]);
+                        d[u] = fmaf(bf16hi_to_f32(p[u][q]), seedv[w][h + 8 * u + 2 * q + 1], d[u]);
+                    }
+            }
+            for (int u = 0; h < H; h += 8, ++u) {       // H % 32 pieces (H % 8 == 0)
                 const u32x4_t p = ldg16(e + h);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    d = fmaf(bf16lo_to_f32(p[q]), seedv[w][h + 2 * q], d);
-                    d = fmaf(bf16hi_to_f32(p[q]), seedv[w][h + 2 * q + 1], d);
+                    d[u] = fmaf(bf16lo_to_f32(p[q]), seedv[w][h + 2 * q], d[u]);
+                    d[u] = fmaf(bf16hi_to_f32(p[q]), seedv[w][h + 2 * q + 1], d[u]);
                 }
             }
-            sim[s0 + i] = d;
+            simp[i] = (d[0] + d[1]) + (d[2] + d[3]);
         }
         if (lane == 0) gidx[w][0] = seed;
         for (int r = 1; r < G; ++r) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
             for (int i = lane; i < m; i += 64) {
-                if (taken[s0 + i]) continue;
-                const float d = sim[s0 + i];
+                if (tk[i]) continue;
+                const float d = simp[i];
                 if (d > bv || bi == 0x7fffffff) {  // indices rise within a lane
                     bv = d;
                     bi = i;
@@ -361,7 +387,7 @@ __global__ __launch_bounds__(256) void k_group_greedy(const uint16_t* __restrict
                     bi = oi;
                 }
             }
-            if ((bi & 63) == lane) taken[s0 + bi] = 1;
+            if ((bi & 63) == lane) tk[bi] = 1;
             if (lane == 0) gidx[w][r] = bi;
         }
         wave_sync();
@@ -379,7 +405,7 @@ __global__ __launch_bounds__(256) void k_group_greedy(const uint16_t* __restrict
     int done = 0;
     for (int i0 = 0; i0 < m; i0 += 64) {
         const int i = i0 + lane;
-        const bool left = i < m && !taken[s0 + i];
+        const bool left = i < m && !tk[i];
         const uint64_t mask = __ballot(left);
         const int before = __popcll(mask & ((1ull << lane) - 1ull));
         if (left) perm[lbase + done + before] = label(i);
