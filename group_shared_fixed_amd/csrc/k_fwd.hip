@@ -113,10 +113,12 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     // Group order.  The logits-only forward and the standalone dW take groups
     // gw, gw + nw, gw + 2 nw, ...: the waves in flight then write (Z) or read
     // (dZ) neighbouring column blocks of the same B x L rows, which measured
-    // 2-12 % faster than one contiguous range per wave.  The label-driven
-    // modes keep contiguous ranges (strided, the fused step measured 11-14 %
-    // slower and the standalone BCE forward 8 % slower at the 3M shape).
-    constexpr bool STRIDED = (MODE == FWD_Z || MODE == BWD_W);
+    // 2-12 % faster than one contiguous range per wave; so does the
+    // standalone BCE forward at G = 16 (its plain dZ stores of neighbouring
+    // groups then meet in L2: 339 -> 297 us at the 670K shape).  The other
+    // label-driven cases keep contiguous ranges (strided, the fused step
+    // measured 11-14 % slower and the BCE forward 8 % slower at 3M).
+    constexpr bool STRIDED = (MODE == FWD_Z || MODE == BWD_W || (MODE == FWD_BCE && G < 32));
     const int64_t kstep = STRIDED ? nw : 1;
     const int64_t k0 = STRIDED ? gw : gw * a.K / nw;
     const int64_t k1 = STRIDED ? a.K : (gw + 1) * a.K / nw;
