@@ -58,6 +58,8 @@ SIGNATURES = {
     "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
     "haste_validate_idx": (_M, [_P, _I, _I, _I, _P, _P]),
     "haste_validate_labels": (_M, [_P, _P, _I, _I, _P, _P]),
+    "haste_workspace_status": (_M, [_P, _P, _P]),
+    "haste_test_set_turn_spins": (None, [_M]),
     "haste_status_string": (ctypes.c_char_p, [_M]),
     "haste_version": (ctypes.c_char_p, []),
 }
@@ -69,6 +71,16 @@ class HasteError(RuntimeError):
     def __init__(self, fn, code):
         self.code = code
         super().__init__(f"{fn} returned {code} ({STATUS.get(code, '?')})")
+
+
+class HandoffError(RuntimeError):
+    """A feature-gradient call reported a bounded turn wait that gave up (its dh is invalid)."""
+
+
+# When true, every call that runs the grouped feature gradient reads its
+# workspace status word afterwards (a stream synchronisation) and raises
+# HandoffError if it is set.  The tests turn this on; timing code leaves it off.
+CHECK_DH_STATUS = False
 
 
 def lib(path: str | None = None):
@@ -129,6 +141,27 @@ def _i32(t):
     return t
 
 
+def workspace_status(workspace, stream=None) -> int:
+    """The status word of the last feature-gradient call on `workspace`
+    (0 = ok, 1 = a turn wait gave up); synchronises the stream."""
+    out = ctypes.c_int32(-1)
+    _check("haste_workspace_status", lib().haste_workspace_status(_ptr(workspace), ctypes.byref(out),
+                                                                   _stream(workspace, stream)))
+    return int(out.value)
+
+
+def _check_dh(fn, workspace, stream):
+    if CHECK_DH_STATUS and workspace is not None:
+        st = workspace_status(workspace, stream)
+        if st != 0:
+            raise HandoffError(f"{fn}: status word {st}: a feature-gradient turn wait gave up")
+
+
+def test_set_turn_spins(spins: int) -> None:
+    """Test hook: bound of the feature-gradient turn waits (negative: default)."""
+    lib().haste_test_set_turn_spins(int(spins))
+
+
 def workspace_size(op: str, B, H, K, G, F, dh_mode="atomic") -> int:
     return int(lib().haste_workspace_size(OP[op], B, H, K, G, F, DH_MODE[dh_mode]))
 
@@ -183,6 +216,7 @@ def bwd_h(dZ, idx, W, G, H, mode="atomic", dh=None, workspace=None, stream=None)
     ws, n = _workspace("bwd_h", B, H, K, G, F, m, dZ.device, workspace)
     _check("haste_bwd_h", lib().haste_bwd_h(_ptr(dZ), _ptr(idx), _ptr(W), _ptr(dh), B, H, K, G, F, m,
                                              _ptr(ws), ws.numel() if ws is not None else 0, _stream(dZ, stream)))
+    _check_dh("haste_bwd_h", ws, stream)
     return dh
 
 
@@ -227,6 +261,7 @@ def step(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want
         _check("haste_step", lib().haste_step(*args))
     else:
         _check("haste_step_timed", lib().haste_step_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+    _check_dh("haste_step", ws, stream)
     return out
 
 
@@ -330,6 +365,7 @@ def joint_step(h, idx, W_tail, yt_rowptr, yt_col, W_head, yh_rowptr, yh_col, sca
         _ptr(h), _ptr(idx), _ptr(W_tail), _ptr(yt_rowptr), _ptr(yt_col), _ptr(W_head), _ptr(yh_rowptr),
         _ptr(yh_col), float(scale_tail), float(scale_head), _ptr(out["dW_tail"]), _ptr(out["dW_head"]),
         _ptr(out["dh"]), _ptr(out.get("loss")), B, H, K, G, F, L, m, _ptr(ws), ws.numel(), _stream(h, stream)))
+    _check_dh("haste_joint_step", ws, stream)
     return out
 
 
@@ -391,6 +427,7 @@ def step_w8(h, idx, W8, wexp, y_rowptr, y_col, scale, G, mode="atomic", want_Z=F
         _check("haste_step_w8", lib().haste_step_w8(*args))
     else:
         _check("haste_step_w8_timed", lib().haste_step_w8_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+    _check_dh("haste_step_w8", ws, stream)
     return out
 
 

@@ -152,19 +152,27 @@ __device__ __forceinline__ float wave_sum(float v)
 // v + 1.  LDS executes the DS instructions of one wave in issue order, so the
 // LDS writes a wave made before pass_turn are visible to the wave that next
 // sees the counter move; only the compiler has to be kept from reordering
-// them.  The wait is bounded (2^24 polls); a caller whose turn sequence is
-// complete never reaches the bound.  While it holds the turn the wave runs
-// at a raised issue priority, so the waves queued behind it (and spinning
-// on the counter) do not slow it down.
-__device__ __forceinline__ void wait_turn(const int* t, int v)
+// them.  The wait is bounded (`spins` polls, by default kTurnSpins, far
+// beyond any legitimate wait): wait_turn returns false when the bound is
+// reached, and the caller then skips its update and reports the failure, so
+// a broken turn sequence cannot hang the GPU or pass unnoticed.  While it
+// holds the turn the wave runs at a raised issue priority, so the waves
+// queued behind it (and spinning on the counter) do not slow it down.
+constexpr int kTurnSpins = 1 << 24;
+__device__ __forceinline__ bool wait_turn(const int* t, int v, int spins)
 {
+    bool got = false;
 #pragma unroll 1
-    for (int spin = 0; spin < (1 << 24); ++spin) {
+    for (int spin = 0; spin < spins; ++spin) {
         const int cur = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(t, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (cur == v) break;
+        if (cur == v) {
+            got = true;
+            break;
+        }
     }
     __builtin_amdgcn_s_setprio(2);
+    return got;
 }
 
 __device__ __forceinline__ void pass_turn(int* t, int v)

@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
+#include "common.hpp"
 #include "kernels.hpp"
 
 using namespace haste;
@@ -13,18 +16,28 @@ namespace {
 
 constexpr int64_t kMaxLabels = 2147483647LL - 64;
 
+// Bound of the feature-gradient turn waits; only haste_test_set_turn_spins
+// changes it (to force the give-up path in tests).
+std::atomic<int> g_turn_spins{kTurnSpins};
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
     int64_t Bp;          // batch padded to 32 (feature-major copy of h)
-    size_t hT_bytes;     // H x Bp bf16
-    size_t part_bytes;   // deterministic dh partials
+    size_t status;       // offset of the status word (grouped feature gradient), or npos
+    size_t flags;        // offset of the per-workgroup hand-off reports (deterministic), or npos
+    size_t hT;           // offset of hT, H x Bp bf16
+    size_t hT_bytes;
+    size_t part;         // offset of the deterministic dh partials
+    size_t part_bytes;
     int nchunks, ntiles; // dh split: label chunks x batch tiles
     int rows;            // batch rows per dh tile
     size_t total;
 };
+
+constexpr size_t kNone = ~(size_t)0;
 
 bool op_needs_hT(int op)
 {
@@ -34,6 +47,11 @@ bool op_needs_hT(int op)
 
 bool op_has_dh(int op) { return op == HASTE_OP_BWD_H || op == HASTE_OP_STEP || op == HASTE_OP_FIXED_BWD_H; }
 
+// The grouped feature-gradient kernels report a broken accumulator hand-off.
+bool op_has_status(int op) { return op == HASTE_OP_BWD_H || op == HASTE_OP_STEP; }
+
+// Workspace: [status word, 256 B][hand-off flags][hT][dh partials], each
+// part present only where the op needs it, each 256-byte aligned.
 Layout layout(int op, int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
 {
     Layout l{};
@@ -47,12 +65,35 @@ Layout layout(int op, int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
     const int target = l.rows == 32 ? 256 : 512;
     int nc = (target / l.ntiles) / 8 * 8;
     l.nchunks = nc < 8 ? 8 : nc;
+    const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
+    size_t at = 0;
+    l.status = l.flags = l.hT = l.part = kNone;
+    if (op_has_status(op)) {
+        l.status = at;
+        at += 256;
+        if (det) {
+            l.flags = at;
+            at += align256((size_t)l.nchunks * l.ntiles * 4);
+        }
+    }
     l.hT_bytes = op_needs_hT(op) ? align256((size_t)H * (size_t)l.Bp * 2) : 0;
-    l.part_bytes = (op_has_dh(op) && dh_mode == HASTE_DH_DETERMINISTIC)
-                       ? align256((size_t)l.nchunks * l.ntiles * l.rows * (size_t)H * 4)
-                       : 0;
-    l.total = l.hT_bytes + l.part_bytes;
+    if (l.hT_bytes) {
+        l.hT = at;
+        at += l.hT_bytes;
+    }
+    l.part_bytes = (op_has_dh(op) && det) ? align256((size_t)l.nchunks * l.ntiles * l.rows * (size_t)H * 4) : 0;
+    if (l.part_bytes) {
+        l.part = at;
+        at += l.part_bytes;
+    }
+    l.total = at;
     return l;
+}
+
+template <class T>
+T* at_off(void* ws, size_t off)
+{
+    return off == kNone ? nullptr : (T*)((char*)ws + off);
 }
 
 int check_shape(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, bool fixed)
@@ -84,6 +125,12 @@ int fwd_grid(int64_t K)
     int64_t g = (K + 3) / 4;
     return (int)(g > 512 ? 512 : (g < 1 ? 1 : g));
 }
+
+}  // namespace
+
+int haste::turn_spins() { return g_turn_spins.load(std::memory_order_relaxed); }
+
+namespace {
 
 #define HASTE_TRY(x)                 \
     do {                             \
@@ -117,7 +164,7 @@ int fwd_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const
         return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_FWD, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
-    uint16_t* hT = (uint16_t*)workspace;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.W8 = W8; a.wexp = wexp; a.K = K; a.scale = 1.f;
@@ -161,7 +208,7 @@ int haste_bwd_w(const haste_bf16* h, const int32_t* idx, const haste_bf16* dZ, f
     if (!aligned16(h) || !aligned16(idx) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_BWD_W, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
-    uint16_t* hT = (uint16_t*)workspace;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.K = K; a.scale = 1.f;
@@ -183,10 +230,14 @@ int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, f
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
     DhArgs a{};
     a.Bp = l.Bp; a.B = B; a.H = H; a.idx = idx; a.W = W; a.K = K; a.dZ = dZ; a.scale = 1.f;
-    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
-    if (!det) launch_fill_f32(dh, B * H, stream);
+    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = at_off<float>(workspace, l.part);
+    a.status = at_off<int32_t>(workspace, l.status); a.flags = at_off<int32_t>(workspace, l.flags);
+    a.spins = turn_spins();
+    if (!det) launch_fill_f32_i32(dh, B * H, a.status, stream);
     if (!launch_dh((int)G, (int)F, DH_FROM_DZ, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
-    if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
+    if (det)
+        launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream, a.flags, l.nchunks * l.ntiles,
+                         a.status);
     return hip_status();
 }
 
@@ -203,7 +254,7 @@ int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, 
         return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_FWD_BCE, B, H, G, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
-    uint16_t* hT = (uint16_t*)workspace;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
     launch_transpose_h(h, hT, B, H, l.Bp, stream, nullptr, 0, loss);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.K = K;
@@ -234,13 +285,15 @@ int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, cons
     const Layout l = layout(HASTE_OP_STEP, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
-    uint16_t* hT = (uint16_t*)workspace;
-    float* part = det ? (float*)((char*)workspace + l.hT_bytes) : nullptr;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
+    float* part = at_off<float>(workspace, l.part);
+    int32_t* status = at_off<int32_t>(workspace, l.status);
+    int32_t* flags = at_off<int32_t>(workspace, l.flags);
     auto mark = [&](int i) {
         if (events) (void)hipEventRecord(events[i], stream);
     };
     mark(0);
-    launch_transpose_h(h, hT, B, H, l.Bp, stream, det ? nullptr : dh, B * H, loss);
+    launch_transpose_h(h, hT, B, H, l.Bp, stream, det ? nullptr : dh, B * H, loss, det ? nullptr : status);
     mark(1);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.W8 = W8; a.wexp = wexp; a.K = K;
@@ -251,10 +304,11 @@ int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, cons
     DhArgs d{};
     d.hT = hT; d.Bp = l.Bp; d.B = B; d.H = H; d.idx = idx; d.W = W; d.W8 = W8; d.wexp = wexp; d.K = K;
     d.y_rowptr = y_rowptr; d.y_col = y_col; d.scale = scale;
-    d.nchunks = l.nchunks; d.ntiles = l.ntiles; d.dh = dh; d.part = part;
+    d.nchunks = l.nchunks; d.ntiles = l.ntiles; d.dh = dh; d.part = part; d.status = status; d.flags = flags;
+    d.spins = turn_spins();
     if (!launch_dh((int)G, (int)F, DH_FROM_LABELS, det, d, stream, w8)) return HASTE_ERR_UNSUPPORTED;
     mark(3);
-    if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
+    if (det) launch_dh_reduce(part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream, flags, l.nchunks * l.ntiles, status);
     mark(4);
     return hip_status();
 }
@@ -307,7 +361,7 @@ int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* 
     if (!aligned16(h) || !aligned16(idx1) || !aligned16(W) || !aligned16(Z)) return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_FIXED_FWD, B, H, 1, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
-    uint16_t* hT = (uint16_t*)workspace;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FixedArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.W = W; a.L = L; a.Z = Z;
@@ -323,7 +377,7 @@ int haste_fixed_bwd_w(const haste_bf16* h, const int32_t* idx1, const haste_bf16
     if (!aligned16(h) || !aligned16(idx1) || !aligned16(dZ) || !aligned16(dW)) return HASTE_ERR_ALIGN;
     const Layout l = layout(HASTE_OP_FIXED_BWD_W, B, H, 1, F, 0);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
-    uint16_t* hT = (uint16_t*)workspace;
+    uint16_t* hT = at_off<uint16_t>(workspace, l.hT);
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FixedArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.L = L; a.dZ = dZ; a.dW = dW;
@@ -344,7 +398,7 @@ int haste_fixed_bwd_h(const haste_bf16* dZ, const int32_t* idx1, const haste_bf1
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
     FixedArgs a{};
     a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.W = W; a.L = L; a.dZ = dZ;
-    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = det ? (float*)workspace : nullptr;
+    a.nchunks = l.nchunks; a.ntiles = l.ntiles; a.dh = dh; a.part = at_off<float>(workspace, l.part);
     if (!det) launch_fill_f32(dh, B * H, stream);
     if (!launch_fixed_bwd_h((int)F, det, a, stream)) return HASTE_ERR_UNSUPPORTED;
     if (det) launch_dh_reduce(a.part, dh, B, H, l.nchunks, l.ntiles * l.rows, stream);
@@ -446,13 +500,26 @@ int haste_head_step(const haste_bf16* h, const haste_bf16* W_head, const int32_t
                      stream);
 }
 
+namespace {
+
+// The head pass of the joint step runs on the workspace past the tail's
+// status word and hand-off flags, which stay readable after the call.
+size_t joint_head_offset(int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
+{
+    return layout(HASTE_OP_STEP, B, H, G, F, dh_mode).hT;
+}
+
+}  // namespace
+
 size_t haste_joint_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int64_t L_head,
                                   int dh_mode)
 {
+    if (B < 1 || H < 1) return 0;
     const size_t tail = haste_workspace_size(HASTE_OP_STEP, B, H, K, G, F, dh_mode);
     const size_t head = haste_head_workspace_size(B, H, L_head);
     if (head == 0) return 0;
-    return tail > head ? tail : head;
+    const size_t head_end = joint_head_offset(B, H, G, F, dh_mode) + head;
+    return tail > head_end ? tail : head_end;
 }
 
 int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W_tail, const int32_t* yt_rowptr,
@@ -474,8 +541,8 @@ int haste_joint_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
     // tail: writes dh and clears + accumulates the loss; head: adds to both
     HASTE_TRY(haste_step(h, idx, W_tail, yt_rowptr, yt_col, scale_tail, dW_tail, dh, nullptr, loss, B, H, K, G, F,
                          dh_mode, workspace, workspace_bytes, stream));
-    return head_pass(h, W_head, yh_rowptr, yh_col, scale_head, dW_head, dh, nullptr, loss, B, H, L_head, true, workspace,
-                     stream);
+    return head_pass(h, W_head, yh_rowptr, yh_col, scale_head, dW_head, dh, nullptr, loss, B, H, L_head, true,
+                     (char*)workspace + joint_head_offset(B, H, G, F, dh_mode), stream);
 }
 
 size_t haste_rewire_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F)
@@ -655,6 +722,18 @@ int haste_group_greedy(const haste_bf16* E, const int32_t* assign, int64_t L, in
                      (int32_t*)(w + l.end), (int32_t*)(w + l.gbase), (int32_t*)(w + l.obase), (int32_t*)(w + l.ng),
                      (float*)(w + l.sim), (uint8_t*)(w + l.taken), stream);
     return hip_status();
+}
+
+void haste_test_set_turn_spins(int spins) { g_turn_spins.store(spins < 0 ? kTurnSpins : spins); }
+
+int haste_workspace_status(const void* workspace, int32_t* status, hipStream_t stream)
+{
+    if (!workspace || !status) return HASTE_ERR_NULL;
+    if (((uintptr_t)workspace & 255u) != 0) return HASTE_ERR_WORKSPACE;
+    if (hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return HASTE_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return HASTE_ERR_HIP;
+    return HASTE_OK;
 }
 
 const char* haste_status_string(int status)

@@ -20,11 +20,14 @@
 //
 // Reduction of the per-workgroup accumulators:
 //   atomic:        fp32 atomic adds into dh (order of the adds varies);
-//   deterministic: the four waves of a workgroup add their P_k into acc in a
-//                  fixed order (barrier-separated turns), each workgroup
-//                  writes its accumulator to its own slice of a partials
-//                  buffer, and a second kernel sums the slices in chunk
-//                  order: bitwise reproducible for a fixed shape.
+//   deterministic: the waves of a workgroup add their P_k into acc in a
+//                  fixed order (turns handed on through a counter in LDS),
+//                  each workgroup writes its accumulator to its own slice of
+//                  a partials buffer, and a second kernel sums the slices in
+//                  chunk order: bitwise reproducible for a fixed shape.
+// The turn waits are bounded; a wave whose wait gives up skips its update and
+// the workgroup reports it (DhArgs::status / DhArgs::flags), so a broken
+// hand-off is an error the caller sees, never a silent wrong result.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t sW[4][G * F];
     __shared__ __attribute__((aligned(16))) uint16_t sT[4][LAB ? F * 16 : 16 * G];
     __shared__ int sTurn;                     // accumulator hand-off counter
+    __shared__ int sLost;                     // a turn wait gave up
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -115,7 +119,10 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     for (int64_t i = threadIdx.x; i < R * H; i += 256)
         acc[i] = 0.f;
-    if (threadIdx.x == 0) sTurn = 0;
+    if (threadIdx.x == 0) {
+        sTurn = 0;
+        sLost = 0;
+    }
 
     LabelCursor cur;
     if constexpr (LAB)
@@ -393,8 +400,9 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 f32x4_t p[NT];
                 round(rd + r, c, n, p);
                 const int turn = (int)(4 * (rd + r)) + wv;
-                wait_turn(&sTurn, turn);
-                if (kc0 + 4 * (rd + r) + wv < kc1) rmw(p, c.col);
+                const bool got = wait_turn(&sTurn, turn, a.spins);
+                if (got && kc0 + 4 * (rd + r) + wv < kc1) rmw(p, c.col);
+                if (!got) sLost = 1;
                 pass_turn(&sTurn, turn);
             }
         } else {
@@ -410,10 +418,14 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                     cl[r][t] = c.col[t];
             }
             const int turn = (int)(4 * i) + wv;
-            wait_turn(&sTurn, turn);
+            const bool got = wait_turn(&sTurn, turn, a.spins);
+            if (got) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                if (kc0 + 4 * (rd + r) + wv < kc1) rmw(p[r], cl[r]);
+                for (int r = 0; r < RPT; ++r)
+                    if (kc0 + 4 * (rd + r) + wv < kc1) rmw(p[r], cl[r]);
+            } else {
+                sLost = 1;
+            }
             pass_turn(&sTurn, turn);
         }
     }
@@ -423,11 +435,13 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += 256)
             dst[i] = acc[acc_off((int)(i % H), (int)(i / H))];
+        if (threadIdx.x == 0) a.flags[blockIdx.x] = sLost;
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += 256) {
             const int64_t b = b0 + i / H;
             if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc_off((int)(i % H), (int)(i / H))]);
         }
+        if (threadIdx.x == 0 && sLost) *a.status = 1;
     }
 }
 
@@ -469,6 +483,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t sW[NWV][G * F];
     __shared__ __attribute__((aligned(16))) uint16_t sT[NWV][LAB ? F * 16 : 16 * G];   // one 16-row half
     __shared__ int sTurn[2];                  // accumulator hand-off counters, one per 16-row half
+    __shared__ int sLost;                     // a turn wait gave up
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -489,6 +504,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     for (int64_t i = threadIdx.x; i < R * H; i += NT_)
         acc[i] = 0.f;
     if (threadIdx.x < 2) sTurn[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sLost = 0;
 
     // each lane's A rows: b0 + r16 (tile 0) and b0 + 16 + r16 (tile 1)
     LabelCursor cur[2];
@@ -789,8 +805,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                 const int turn = (int)(NWV * (rd + r)) + wv;
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    wait_turn(&sTurn[hf], turn);
-                    if (kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, c.col);
+                    const bool got = wait_turn(&sTurn[hf], turn, a.spins);
+                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, c.col);
+                    if (!got) sLost = 1;
                     pass_turn(&sTurn[hf], turn);
                 }
             }
@@ -814,10 +831,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         const int turn = (int)(NWV * i) + wv;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            wait_turn(&sTurn[hf], turn);
+            const bool got = wait_turn(&sTurn[hf], turn, a.spins);
+            if (got) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                if (kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p[r], cl[r]);
+                for (int r = 0; r < RPT; ++r)
+                    if (kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p[r], cl[r]);
+            } else {
+                sLost = 1;
+            }
             pass_turn(&sTurn[hf], turn);
         }
     }
@@ -827,11 +848,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
         for (int64_t i = threadIdx.x; i < R * H; i += NT_)
             dst[i] = acc[acc32_off((int)(i % H), (int)(i / H))];
+        if (threadIdx.x == 0) a.flags[blockIdx.x] = sLost;
     } else {
         for (int64_t i = threadIdx.x; i < R * H; i += NT_) {
             const int64_t b = b0 + i / H;
             if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc32_off((int)(i % H), (int)(i / H))]);
         }
+        if (threadIdx.x == 0 && sLost) *a.status = 1;
     }
 }
 
@@ -839,8 +862,19 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 // per 4 consecutive outputs each add every fourth chunk (c = lane % 4 + 4i,
 // in i order), then the four partial sums are combined as (s0 + s1) + (s2 + s3).
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, float* __restrict__ dh,
-                                                   int64_t B, int64_t H, int nchunks, int rows_per_chunk)
+                                                   int64_t B, int64_t H, int nchunks, int rows_per_chunk,
+                                                   const int32_t* __restrict__ flags, int nflags,
+                                                   int32_t* __restrict__ status)
 {
+    // the first workgroup folds the feature-gradient workgroups' hand-off
+    // reports into the call's status word (written every call)
+    if (status && blockIdx.x == 0) {
+        int bad = 0;
+        for (int i = threadIdx.x; i < nflags; i += 256)
+            bad |= flags[i];
+        bad = __syncthreads_or(bad);
+        if (threadIdx.x == 0) *status = bad ? 1 : 0;
+    }
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t o4 = t >> 2;               // index of 4 consecutive outputs
     const int sub = (int)(t & 3);
@@ -967,13 +1001,13 @@ bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s, 
 }
 
 void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
-                      hipStream_t s)
+                      hipStream_t s, const int32_t* flags, int nflags, int32_t* status)
 {
     // four threads per four consecutive outputs (the partials of a chunk hold
     // at least B rows, so a last partial quad stays inside them)
     const int64_t nthreads = (B * H + 3) / 4 * 4;
     hipLaunchKernelGGL(k_dh_reduce, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, part, dh, B, H,
-                       nchunks, rows_per_chunk);
+                       nchunks, rows_per_chunk, flags, nflags, status);
 }
 
 }  // namespace haste

@@ -6,10 +6,11 @@ namespace haste {
 
 // hT[j, b] = h[b, j] for b < B, 0 for B <= b < Bp (64 x 64 tiles via LDS).
 // Also clears the optional outputs zf[0, nzf) and *zd that later kernels of
-// the same call accumulate into (saves separate launches).
+// the same call accumulate into, and the status word *zi (saves separate
+// launches).
 __global__ __launch_bounds__(256) void k_transpose_h(const uint16_t* __restrict__ h, uint16_t* __restrict__ hT,
                                                      int64_t B, int64_t H, int64_t Bp, float* __restrict__ zf,
-                                                     int64_t nzf, double* __restrict__ zd)
+                                                     int64_t nzf, double* __restrict__ zd, int32_t* __restrict__ zi)
 {
     {
         const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * 256;
@@ -17,6 +18,7 @@ __global__ __launch_bounds__(256) void k_transpose_h(const uint16_t* __restrict_
         for (int64_t i = tid; i < nzf; i += nthreads)
             zf[i] = 0.f;
         if (zd && tid == 0) *zd = 0.0;
+        if (zi && tid == 0) *zi = 0;
     }
     // tile of 32 batch rows x 64 features; each thread moves one 16-byte
     // piece in (row b, features j .. j+8) and one out (feature j, rows b .. b+8)
@@ -59,6 +61,13 @@ __global__ __launch_bounds__(256) void k_fill_zero(T* __restrict__ p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         p[i] = T(0);
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero_f32_i32(float* __restrict__ p, int64_t n, int32_t* __restrict__ zi)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0.f;
+    if (zi && blockIdx.x == 0 && threadIdx.x == 0) *zi = 0;
 }
 
 // One thread per row: entries in [0, H) and strictly increasing.
@@ -104,16 +113,21 @@ static unsigned fill_grid(int64_t n)
 }
 
 void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s,
-                        float* zero_f, int64_t n_zero_f, double* zero_d)
+                        float* zero_f, int64_t n_zero_f, double* zero_d, int32_t* zero_i)
 {
     const dim3 grid((unsigned)((H + 63) / 64), (unsigned)(Bp / 32));   // Bp is a multiple of 32
     hipLaunchKernelGGL(k_transpose_h, grid, dim3(256), 0, s, h, hT, B, H, Bp, zero_f, zero_f ? n_zero_f : 0,
-                       zero_d);
+                       zero_d, zero_i);
 }
 
 void launch_fill_f32(float* p, int64_t n, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fill_zero<float>, dim3(fill_grid(n)), dim3(256), 0, s, p, n);
+}
+
+void launch_fill_f32_i32(float* p, int64_t n, int32_t* i, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_zero_f32_i32, dim3(fill_grid(n)), dim3(256), 0, s, p, n, i);
 }
 
 void launch_fill_f64(double* p, int64_t n, hipStream_t s)

@@ -51,7 +51,17 @@ struct DhArgs {
     float* part;          // nchunks x (ntiles*kDhRows) x H fp32 (deterministic flush)
     const uint8_t* W8;    // FP8-weight variants: L x F E4M3 codes in place of W
     const int32_t* wexp;  // K group exponents
+    // Report of the bounded accumulator hand-off (a wait that gave up):
+    // atomic flush: *status (cleared by an earlier kernel of the call) is set
+    // to 1; deterministic flush: every workgroup writes flags[blockIdx.x]
+    // (0 or 1) and the reduce kernel folds them into *status.
+    int32_t* status;
+    int32_t* flags;
+    int spins;            // bound of each turn wait (polls)
 };
+// Bound of the feature-gradient turn waits for the next launches (the
+// default, or a test's setting through haste_test_set_turn_spins).
+int turn_spins();
 
 struct FixedArgs {
     const uint16_t* hT;
@@ -88,15 +98,19 @@ inline int dh_tile_rows(int G, int F, int64_t H, bool from_labels)
 }
 // w8: weights as FP8 codes + group exponents (DH_FROM_LABELS only).
 bool launch_dh(int G, int F, int src, bool det, const DhArgs& a, hipStream_t s, bool w8 = false);
+// Also sets *status to the OR of flags[0, nflags) when status is non-null.
 void launch_dh_reduce(const float* part, float* dh, int64_t B, int64_t H, int nchunks, int rows_per_chunk,
-                      hipStream_t s);
+                      hipStream_t s, const int32_t* flags = nullptr, int nflags = 0, int32_t* status = nullptr);
 bool launch_fixed_fwd(int F, const FixedArgs& a, int grid, hipStream_t s);
 bool launch_fixed_bwd_w(int F, const FixedArgs& a, int grid, hipStream_t s);
 bool launch_fixed_bwd_h(int F, bool det, const FixedArgs& a, hipStream_t s);
-// h (B x H) -> hT (H x Bp, zero padded); optionally clears zero_f[0, n) and *zero_d
+// h (B x H) -> hT (H x Bp, zero padded); optionally clears zero_f[0, n), *zero_d and *zero_i
 void launch_transpose_h(const uint16_t* h, uint16_t* hT, int64_t B, int64_t H, int64_t Bp, hipStream_t s,
-                        float* zero_f = nullptr, int64_t n_zero_f = 0, double* zero_d = nullptr);
+                        float* zero_f = nullptr, int64_t n_zero_f = 0, double* zero_d = nullptr,
+                        int32_t* zero_i = nullptr);
 void launch_fill_f32(float* p, int64_t n, hipStream_t s);
+// clears p[0, n) and, when non-null, *i
+void launch_fill_f32_i32(float* p, int64_t n, int32_t* i, hipStream_t s);
 void launch_fill_f64(double* p, int64_t n, hipStream_t s);
 void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s);

@@ -43,6 +43,14 @@
  *     haste_workspace_size(op, ...) bytes, 256-byte aligned.
  *   - Calls that overlap on one workspace race; separate streams need
  *     separate workspaces.
+ *   - Status word: the calls that run the grouped feature gradient
+ *     (haste_bwd_h, haste_step and its variants, haste_joint_step) keep an
+ *     int32 in the first 4 bytes of their workspace.  The waves of a
+ *     feature-gradient workgroup take turns on a shared accumulator; every
+ *     wait for a turn is bounded, and a wait that gives up (which a correct
+ *     turn sequence never does) skips that wave's update and sets the word
+ *     to 1.  The call then still completes, but dh is invalid.  The word is
+ *     rewritten by every such call; read it with haste_workspace_status.
  */
 #ifndef HASTE_H
 #define HASTE_H
@@ -320,6 +328,21 @@ int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, i
  * increasing. */
 int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t B, int64_t L, int32_t* bad,
                           hipStream_t stream);
+
+/* Copies the status word (first 4 bytes of `workspace`, see the conventions
+ * above) of the last feature-gradient call on that workspace into *status
+ * (host memory) and synchronises `stream`: 0 = every accumulator hand-off
+ * completed, 1 = a bounded turn wait gave up and dh is invalid.  Unlike the
+ * other calls this one blocks.  HASTE_ERR_NULL / HASTE_ERR_WORKSPACE
+ * (misaligned) / HASTE_ERR_HIP (copy or synchronisation failed). */
+int haste_workspace_status(const void* workspace, int32_t* status, hipStream_t stream);
+
+/* Test hook, not for production use: sets the bound (number of polls) of
+ * every feature-gradient turn wait launched afterwards in this process, so
+ * that a test can force the give-up path on the GPU (0: every wait gives up
+ * at once; every kernel still runs to its end) and check that the status
+ * word reports it.  A negative value restores the default bound. */
+void haste_test_set_turn_spins(int spins);
 
 /* Static text for a haste_status value. */
 const char* haste_status_string(int status);

@@ -10,3 +10,7 @@ for _p in (ROOT, os.path.join(ROOT, "tests")):
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload; takes tens of seconds")
+    # every feature-gradient call in the tests reads back its status word
+    # (a turn wait that gave up raises instead of leaving a wrong dh)
+    from group_shared_fixed_amd import binding
+    binding.CHECK_DH_STATUS = True

@@ -51,11 +51,24 @@ def test_workspace_size(L):
     # feature-major copy of h: H * round_up(B, 32) * 2 bytes, 256-aligned
     assert L.haste_workspace_size(0, 128, 768, 93748, 32, 64, 0) == 768 * 128 * 2
     assert L.haste_workspace_size(0, 100, 768, 10, 32, 64, 0) == 768 * 128 * 2
-    assert L.haste_workspace_size(2, 128, 768, 10, 32, 64, 0) == 0           # atomic dh needs none
+    # atomic dh: only the 256-byte status word
+    assert L.haste_workspace_size(2, 128, 768, 10, 32, 64, 0) == 256
+    # deterministic dh: status word, one hand-off flag per workgroup, the partials
+    # (32-row tiles at G = 32, F = 64: 4 batch tiles x 64 label chunks)
     det = L.haste_workspace_size(2, 128, 768, 10, 32, 64, 1)
-    assert det > 0 and det % 256 == 0
+    assert det == 256 + 1024 + 64 * 4 * 32 * 768 * 4
     assert L.haste_workspace_size(4, 128, 768, 10, 32, 64, 1) == 768 * 128 * 2 + det
+    assert L.haste_workspace_size(4, 128, 768, 10, 32, 64, 0) == 256 + 768 * 128 * 2
+    # the G = 1 baseline's feature gradient has no turn waits, so no status word
+    assert L.haste_workspace_size(7, 128, 768, 10, 1, 64, 0) == 0
     assert L.haste_workspace_size(99, 128, 768, 10, 32, 64, 0) == 0
+
+
+def test_workspace_status_rejects(L):
+    out = ctypes.c_int32(0)
+    assert L.haste_workspace_status(None, ctypes.byref(out), None) == NULL
+    assert L.haste_workspace_status(P(0x100000), None, None) == NULL
+    assert L.haste_workspace_status(P(0x100010), ctypes.byref(out), None) == WS
 
 
 def _fwd(L, h=A, idx=A, W=A, Z=A, B=128, H=768, K=100, G=32, F=64, ws=A, wsb=1 << 30):
