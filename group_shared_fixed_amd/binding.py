@@ -20,7 +20,7 @@ STATUS = {
     -4: "HASTE_ERR_ALIGN", -5: "HASTE_ERR_WORKSPACE", -6: "HASTE_ERR_INDEX", -7: "HASTE_ERR_HIP",
 }
 OP = {"fwd": 0, "bwd_w": 1, "bwd_h": 2, "fwd_bce": 3, "step": 4, "fixed_fwd": 5, "fixed_bwd_w": 6,
-      "fixed_bwd_h": 7}
+      "fixed_bwd_h": 7, "fwd_bce_bwd": 8}
 DH_MODE = {"atomic": 0, "det": 1, "deterministic": 1, 0: 0, 1: 1}
 
 # name -> (restype, argtypes); P = pointer, I = int64, S = size_t, F = float, M = int
@@ -33,6 +33,8 @@ SIGNATURES = {
     "haste_fwd_bce": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_step": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
     "haste_step_timed": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P, _P]),
+    "haste_bwd_h_workspace_size": (_S, [_I, _I, _I, _I, _I, _M]),
+    "haste_fwd_bce_bwd": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _M, _P, _S, _I, _I, _I, _I, _I, _P]),
     "haste_fixed_fwd": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "haste_fixed_bwd_w": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "haste_fixed_bwd_h": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _M, _P, _S, _P]),
@@ -262,6 +264,33 @@ def step(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want
     else:
         _check("haste_step_timed", lib().haste_step_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
     _check_dh("haste_step", ws, stream)
+    return out
+
+
+def bwd_h_workspace_size(B, H, K, G, F, mode="atomic") -> int:
+    return int(lib().haste_bwd_h_workspace_size(B, H, K, G, F, DH_MODE[mode]))
+
+
+def fwd_bce_bwd(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_loss=False, out=None, workspace=None,
+                stream=None):
+    """Fused forward + BCE + dW + dh (haste_fwd_bce_bwd, fp32 loss).
+    Returns dict(dW, dh, loss)."""
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    K, F = idx.shape
+    if out is None:
+        out = {
+            "dW": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "loss": torch.empty(4, dtype=torch.float32, device=h.device) if want_loss else None,
+        }
+    m = DH_MODE[mode]
+    ws, n = _workspace("fwd_bce_bwd", B, H, K, G, F, m, h.device, workspace)
+    _check("haste_fwd_bce_bwd", lib().haste_fwd_bce_bwd(
+        _ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]), _ptr(out["dh"]),
+        _ptr(out.get("loss")), m, _ptr(ws), ws.numel() if ws is not None else 0, B, H, K, G, F, _stream(h, stream)))
+    _check_dh("haste_fwd_bce_bwd", ws, stream)
     return out
 
 

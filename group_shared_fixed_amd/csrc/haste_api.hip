@@ -145,9 +145,15 @@ extern "C" {
 size_t haste_workspace_size(int op, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode)
 {
     (void)K;
-    (void)F;
-    if (op < HASTE_OP_FWD || op > HASTE_OP_FIXED_BWD_H || B < 1 || H < 1) return 0;
+    if (op < HASTE_OP_FWD || op > HASTE_OP_FWD_BCE_BWD || B < 1 || H < 1) return 0;
+    // the fused pass with an fp32 loss: the step's workspace plus its fp64 accumulator
+    if (op == HASTE_OP_FWD_BCE_BWD) return layout(HASTE_OP_STEP, B, H, G, F, dh_mode).total + 256;
     return layout(op, B, H, G, F, dh_mode).total;
+}
+
+size_t haste_bwd_h_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int mode)
+{
+    return haste_workspace_size(HASTE_OP_BWD_H, B, H, K, G, F, mode);
 }
 
 namespace {
@@ -351,6 +357,25 @@ int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, con
 {
     return haste_step_timed(h, idx, W, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode, workspace,
                             workspace_bytes, stream, nullptr);
+}
+
+int haste_fwd_bce_bwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                      const int32_t* y_col, float scale, float* dW, float* dh, float* loss, int mode,
+                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t K, int64_t G,
+                      int64_t F, hipStream_t stream)
+{
+    if (!W) return HASTE_ERR_NULL;
+    if (loss && !aligned16(loss)) return HASTE_ERR_ALIGN;
+    // shape and mode first, so that the workspace size below is meaningful
+    HASTE_TRY(check_shape(B, H, K, G, F, false));
+    if (mode != HASTE_DH_ATOMIC && mode != HASTE_DH_DETERMINISTIC) return HASTE_ERR_UNSUPPORTED;
+    const size_t step_ws = layout(HASTE_OP_STEP, B, H, G, F, mode).total;
+    HASTE_TRY(check_ws(workspace, workspace_bytes, step_ws + (loss ? 256 : 0)));
+    double* acc = loss ? (double*)((char*)workspace + step_ws) : nullptr;
+    HASTE_TRY(step_impl(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, dW, dh, nullptr, acc, B, H, K, G, F,
+                        mode, workspace, step_ws, stream, nullptr));
+    if (loss) launch_f64_to_f32(acc, loss, stream);
+    return hip_status();
 }
 
 int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* W, float* Z, int64_t B,

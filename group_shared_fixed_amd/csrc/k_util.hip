@@ -106,6 +106,17 @@ __global__ __launch_bounds__(256) void k_validate_labels(const int32_t* __restri
     if (!ok) atomicAdd(bad, 1);
 }
 
+// dst[0] = (float)src[0]: a loss accumulated in fp64, handed out as fp32.
+__global__ void k_f64_to_f32(const double* __restrict__ src, float* __restrict__ dst)
+{
+    if (threadIdx.x == 0) dst[0] = (float)src[0];
+}
+
+void launch_f64_to_f32(const double* src, float* dst, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_f64_to_f32, dim3(1), dim3(64), 0, s, src, dst);
+}
+
 static unsigned fill_grid(int64_t n)
 {
     int64_t g = (n + 255) / 256;

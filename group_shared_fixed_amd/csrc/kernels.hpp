@@ -112,6 +112,8 @@ void launch_fill_f32(float* p, int64_t n, hipStream_t s);
 // clears p[0, n) and, when non-null, *i
 void launch_fill_f32_i32(float* p, int64_t n, int32_t* i, hipStream_t s);
 void launch_fill_f64(double* p, int64_t n, hipStream_t s);
+// *dst = (float)*src
+void launch_f64_to_f32(const double* src, float* dst, hipStream_t s);
 void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s);
 void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B, int64_t L, int32_t* bad,

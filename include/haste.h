@@ -91,7 +91,8 @@ typedef enum {
     HASTE_OP_STEP = 4,
     HASTE_OP_FIXED_FWD = 5,
     HASTE_OP_FIXED_BWD_W = 6,
-    HASTE_OP_FIXED_BWD_H = 7
+    HASTE_OP_FIXED_BWD_H = 7,
+    HASTE_OP_FWD_BCE_BWD = 8
 } haste_op;
 
 /* Workspace bytes `op` needs for this shape (K = L and G = 1 for the
@@ -120,6 +121,10 @@ int haste_bwd_h(const haste_bf16* dZ, const int32_t* idx, const haste_bf16* W, f
                 int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of haste_bwd_h for this shape and dh mode (the same as
+ * haste_workspace_size(HASTE_OP_BWD_H, ...)). */
+size_t haste_bwd_h_workspace_size(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int mode);
+
 /* Forward with the BCE-gradient epilogue: dZ = scale * (sigmoid(Z) - Y)
  * rounded to bf16 (objective of the "head-tail split" section; mean over
  * samples, sum over labels: pass scale = 1/B).  Z (nullable) also receives
@@ -140,6 +145,23 @@ int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
                float* dW, float* dh, float* Z, double* loss,
                int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The fused training pass with the argument order of the layer's interface
+ * table: forward, BCE gradient dZ = scale * (sigmoid(Z) - Y) kept on chip,
+ * dW = dZ^T H_k per group and dh as the split-K scatter of dZ_k W_k
+ * ("gather-once + dense MMA kernel" for the three products, "head-tail
+ * split" for the BCE objective it differentiates).  The same kernels and
+ * results as haste_step (dW and dh bitwise equal for the same mode and
+ * shape); loss (nullable) is 1 fp32 value, scale * sum [max(z,0) +
+ * log(1 + e^-|z|) - y z], summed in fp64 and rounded once.  mode is a
+ * haste_dh_mode.  Workspace: haste_workspace_size(HASTE_OP_FWD_BCE_BWD, ...)
+ * bytes (256 more than haste_step's, for the fp64 loss); its first 4 bytes
+ * are the status word.  Errors as haste_step. */
+int haste_fwd_bce_bwd(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+                      const int32_t* y_rowptr, const int32_t* y_col, float scale,
+                      float* dW, float* dh, float* loss, int mode,
+                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t K, int64_t G,
+                      int64_t F, hipStream_t stream);
 
 /* haste_step plus timing: when `events` is non-NULL, events[0..4] (created
  * by the caller) are recorded on `stream` at the phase boundaries of the

@@ -64,6 +64,38 @@ def test_workspace_size(L):
     assert L.haste_workspace_size(99, 128, 768, 10, 32, 64, 0) == 0
 
 
+def test_section_interface_names(L):
+    """haste_bwd_h_workspace_size and the fused pass's workspace op."""
+    for mode in (0, 1):
+        for (B, H, K, G, F) in ((128, 768, 93748, 32, 64), (256, 768, 41888, 16, 128), (50, 1024, 9, 64, 32)):
+            assert L.haste_bwd_h_workspace_size(B, H, K, G, F, mode) == L.haste_workspace_size(2, B, H, K, G, F, mode)
+            assert L.haste_workspace_size(8, B, H, K, G, F, mode) == L.haste_workspace_size(4, B, H, K, G, F, mode) + 256
+
+
+def _fbb(L, h=A, idx=A, W=A, rp=A, col=A, scale=0.5, dW=A, dh=A, loss=A, mode=1, ws=A, wsb=1 << 30,
+         B=128, H=768, K=100, G=32, F=64):
+    return L.haste_fwd_bce_bwd(h, idx, W, rp, col, scale, dW, dh, loss, mode, ws, wsb, B, H, K, G, F, None)
+
+
+def test_fwd_bce_bwd_rejects(L):
+    assert _fbb(L, h=None) == NULL
+    assert _fbb(L, W=None) == NULL
+    assert _fbb(L, dW=None) == NULL
+    assert _fbb(L, dh=None) == NULL
+    assert _fbb(L, rp=None) == NULL
+    assert _fbb(L, B=0) == DIM
+    assert _fbb(L, scale=0.0) == DIM
+    assert _fbb(L, G=8) == UNSUP
+    assert _fbb(L, B=257) == UNSUP                   # label cursors cover 256 rows
+    assert _fbb(L, mode=2) == UNSUP
+    assert _fbb(L, loss=MIS) == ALIGN
+    assert _fbb(L, dW=MIS) == ALIGN
+    assert _fbb(L, ws=None) == WS
+    need = L.haste_workspace_size(8, 128, 768, 100, 32, 64, 1)
+    assert _fbb(L, wsb=need - 256) == WS              # the fp64 loss accumulator is missing
+    assert _fbb(L, ws=P(0x100010)) == WS
+
+
 def test_workspace_status_rejects(L):
     out = ctypes.c_int32(0)
     assert L.haste_workspace_status(None, ctypes.byref(out), None) == NULL

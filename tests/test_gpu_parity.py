@@ -250,6 +250,29 @@ def test_all_ones_integer_exact(G, F):
         assert_exact(to_host(hs.bwd_h(dZ, idx, W, G, H, mode=mode)), np.tile(G * cnt, (B, 1)), f"dh[{mode}]")
 
 
+@pytest.mark.parametrize("mode", ["atomic", "det"])
+@pytest.mark.parametrize("name", ["tiny_4k", "g32_f64_many_b128", "g16_f128_many_b130", "g64_f64_h96_b33",
+                                  "g32_f64_h1024"])
+def test_fwd_bce_bwd(name, mode):
+    """haste_fwd_bce_bwd (the interface table's argument order, fp32 loss):
+    dW and dh against the oracle, bitwise equal to haste_step's in
+    deterministic mode, the loss within 1e-5 of the oracle's."""
+    d = case(name)
+    say(f"  fwd_bce_bwd[{mode}] {name} {CASES[name]}")
+    h, idx, W, _, rp, col = dev_inputs(d)
+    out = hs.fwd_bce_bwd(h, idx, W, rp, col, d["scale"], d["G"], mode=mode, want_loss=True)
+    ref = O.oracle_step(d["h"], d["idx"], d["W"], d["y_rowptr"], d["y_col"], d["scale"], d["G"])
+    dW, dh = to_host(out["dW"]), to_host(out["dh"])
+    assert_parity(dW, ref["dW"], "dW")
+    assert_parity(dh, ref["dh"], f"dh[{mode}]")
+    lg = float(to_host(out["loss"])[0])
+    assert abs(lg - ref["loss"]) <= 1e-5 * abs(ref["loss"]), (lg, ref["loss"])
+    if mode == "det":
+        st = hs.step(h, idx, W, rp, col, d["scale"], d["G"], mode="det")
+        assert (to_host(st["dW"]).view(np.uint32) == dW.view(np.uint32)).all()
+        assert (to_host(st["dh"]).view(np.uint32) == dh.view(np.uint32)).all()
+
+
 def test_deterministic_mode_repeats_bitwise():
     d = case("g32_f64_b77")
     h, idx, W, dZ, rp, col = dev_inputs(d)
