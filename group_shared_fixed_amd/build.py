@@ -57,7 +57,7 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lrocblas",
-           "-Wl,-rpath,/opt/rocm/lib"]
+           "-Wl,-rpath,/opt/rocm/lib", f"-Wl,--version-script={os.path.join(CSRC, 'exports.map')}"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     if verbose:
