@@ -6,6 +6,7 @@ include/haste.h; `binding` is a thin ctypes layer over it.
 
 from . import binding  # noqa: F401
 from .binding import (  # noqa: F401
+    HandoffError,
     HasteError,
     bwd_h,
     bwd_w,
@@ -14,6 +15,9 @@ from .binding import (  # noqa: F401
     fixed_fwd,
     fwd,
     fwd_bce,
+    fwd_bce_bwd,
+    bwd_h_workspace_size,
+    workspace_status,
     fwd_w8,
     group_greedy,
     head_step,
