@@ -151,8 +151,10 @@ int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
  * dW = dZ^T H_k per group and dh as the split-K scatter of dZ_k W_k
  * ("gather-once + dense MMA kernel" for the three products, "head-tail
  * split" for the BCE objective it differentiates).  The same kernels and
- * results as haste_step (dW and dh bitwise equal for the same mode and
- * shape); loss (nullable) is 1 fp32 value, scale * sum [max(z,0) +
+ * results as haste_step (dW and dh bitwise equal to haste_step's with the
+ * same mode, shape and loss request: with a loss the forward epilogue forms
+ * the sigmoid from e^-|z|, which moves the last bits of dZ); loss
+ * (nullable) is 1 fp32 value, scale * sum [max(z,0) +
  * log(1 + e^-|z|) - y z], summed in fp64 and rounded once.  mode is a
  * haste_dh_mode.  Workspace: haste_workspace_size(HASTE_OP_FWD_BCE_BWD, ...)
  * bytes (256 more than haste_step's, for the fp64 loss); its first 4 bytes
