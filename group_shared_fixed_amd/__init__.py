@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     rewire,
     rewire_workspace_size,
     step,
+    step_noalloc,
     step_w8,
     quantize_w8,
     validate_idx,

@@ -34,6 +34,7 @@ SIGNATURES = {
     "haste_step": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
     "haste_step_timed": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P, _P]),
     "haste_bwd_h_workspace_size": (_S, [_I, _I, _I, _I, _I, _M]),
+    "haste_step_noalloc": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P]),
     "haste_fwd_bce_bwd": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _M, _P, _S, _I, _I, _I, _I, _I, _P]),
     "haste_fixed_fwd": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "haste_fixed_bwd_w": (_M, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
@@ -291,6 +292,27 @@ def fwd_bce_bwd(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_loss=F
         _ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]), _ptr(out["dh"]),
         _ptr(out.get("loss")), m, _ptr(ws), ws.numel() if ws is not None else 0, B, H, K, G, F, _stream(h, stream)))
     _check_dh("haste_fwd_bce_bwd", ws, stream)
+    return out
+
+
+def step_noalloc(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want_loss=False, out=None,
+                 stream=None):
+    """haste_step without a workspace (the library's per-GPU scratch array).
+    Returns dict(dW, dh, Z, loss)."""
+    torch = _torch()
+    _bits(h); _bits(W); _i32(idx); _i32(y_rowptr); _i32(y_col)
+    B, H = h.shape
+    K, F = idx.shape
+    if out is None:
+        out = {
+            "dW": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
+            "Z": torch.empty(B, K * G, dtype=torch.float32, device=h.device) if want_Z else None,
+            "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
+        }
+    _check("haste_step_noalloc", lib().haste_step_noalloc(
+        _ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]), _ptr(out["dh"]),
+        _ptr(out.get("Z")), _ptr(out.get("loss")), B, H, K, G, F, DH_MODE[mode], _stream(h, stream)))
     return out
 
 

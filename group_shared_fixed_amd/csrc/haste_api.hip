@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -272,11 +273,10 @@ int haste_fwd_bce(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, 
 
 namespace {
 
-// The fused step from bf16 weights (W) or FP8 codes and group exponents (W8, wexp).
-int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
-              const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
-              double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
-              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+// Host-side checks of the fused step (everything but the workspace).
+int step_check(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
+               const int32_t* y_rowptr, const int32_t* y_col, float scale, const float* dW, const float* dh,
+               const float* Z, const double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode)
 {
     const bool w8 = W8 != nullptr;
     if (!h || !idx || !y_rowptr || !y_col || !dW || !dh || (w8 ? !wexp : !W)) return HASTE_ERR_NULL;
@@ -288,6 +288,17 @@ int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, cons
     if (!aligned16(h) || !aligned16(idx) || !aligned16(y_rowptr) || !aligned16(y_col) || !aligned16(dW) ||
         !aligned16(dh) || (Z && !aligned16(Z)) || (loss && !aligned16(loss)))
         return HASTE_ERR_ALIGN;
+    return HASTE_OK;
+}
+
+// The fused step from bf16 weights (W) or FP8 codes and group exponents (W8, wexp).
+int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
+              const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
+              double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    const bool w8 = W8 != nullptr;
+    HASTE_TRY(step_check(h, idx, W, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode));
     const Layout l = layout(HASTE_OP_STEP, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
@@ -348,6 +359,61 @@ int haste_step_w8(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, co
 {
     return haste_step_w8_timed(h, idx, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
                                workspace, workspace_bytes, stream, nullptr);
+}
+
+namespace {
+
+// Device scratch of haste_step_noalloc: hT, the status word, the hand-off
+// flags and the deterministic dh partials of one fused pass (the loss
+// accumulator, dW, dh and Z are the caller's).  32 MiB covers every supported
+// shape with B <= 256 and H <= 768 in both dh modes (the Amazon-3M-shaped
+// pass in deterministic mode takes 25.4 MB); larger needs are refused.  Each
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// only the address hipGetSymbolAddress returns for the current device is
+// passed to kernels.
+constexpr size_t kNoAllocScratchBytes = 32ull << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current).
+int scratch_for_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return HASTE_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return HASTE_ERR_HIP;
+        }
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return HASTE_OK;
+}
+
+}  // namespace
+
+int haste_step_noalloc(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                       const int32_t* y_col, float scale, float* dW, float* dh, float* Z, double* loss, int64_t B,
+                       int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, hipStream_t stream)
+{
+    HASTE_TRY(step_check(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F,
+                         dh_mode));
+    const size_t need = layout(HASTE_OP_STEP, B, H, G, F, dh_mode).total;
+    if (need > kNoAllocScratchBytes) return HASTE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    HASTE_TRY(scratch_for_current_device(&ws));
+    return step_impl(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
+                     ws, kNoAllocScratchBytes, stream, nullptr);
 }
 
 int haste_step(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,

@@ -165,6 +165,27 @@ int haste_fwd_bce_bwd(const haste_bf16* h, const int32_t* idx, const haste_bf16*
                       void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t K, int64_t G,
                       int64_t F, hipStream_t stream);
 
+/* haste_step for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same pass,
+ * kernels and results (bitwise haste_step's in deterministic mode), with the
+ * workspace replaced by a 32 MiB device array inside the library, one per
+ * GPU, held until the process ends.  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.  Shapes whose workspace
+ * (haste_workspace_size(HASTE_OP_STEP, ...)) exceeds 32 MiB are refused with
+ * HASTE_ERR_WORKSPACE before any HIP call (every supported shape with
+ * H <= 768 fits; H = 1024 with large B in deterministic mode does not).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller.  The array keeps the last call's contents; every call rewrites or
+ * clears what it reads.  Its status word is not exposed; callers that need
+ * the checked path use haste_step.  Other arguments and errors as
+ * haste_step (HASTE_ERR_HIP also when the array's address cannot be
+ * obtained). */
+int haste_step_noalloc(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+                       const int32_t* y_rowptr, const int32_t* y_col, float scale,
+                       float* dW, float* dh, float* Z, double* loss,
+                       int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, hipStream_t stream);
+
 /* haste_step plus timing: when `events` is non-NULL, events[0..4] (created
  * by the caller) are recorded on `stream` at the phase boundaries of the
  * pass: [0] start, [1] after the feature-major copy of h and output
