@@ -182,6 +182,145 @@ def time_call(fn, reps, stream_handle, ev):
     return ev.ms(0, 1) / reps
 
 
+def calibrate(dev, seconds=1.0):
+    """What this GPU delivers to plain library kernels, measured in-process:
+    an fp32 copy of 1 GiB (torch elementwise kernel: read + write bytes per
+    second) and a dense bf16 GEMM of 8192^3 (torch.matmul, hipBLASLt).  They
+    are the measured second denominators next to the spec peaks.  The GEMM
+    runs for about `seconds`: a cold GPU otherwise spends its first few dozen
+    steps below its working clock (measured: the on-chip-bound feature-
+    gradient kernel 446 -> 397 us over its first 30 steps after an idle
+    period, the HBM-bound forward 307 -> 298 us; 300 ms of copies did not
+    remove it, one second of GEMMs did)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    e0.record()
+    for _ in range(20):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 0
+    e0.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            torch.matmul(a, b, out=c)
+        reps += 10
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(copy_gbs, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+            "copy": "torch.mul(src, 1.0, out=dst), fp32, 1 GiB in + 1 GiB out",
+            "gemm": f"torch.matmul bf16 {n}^3 (hipBLASLt)"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Run in a child process with OMP_NUM_THREADS=1: the oracle step on the
+# 4k-label workload (whole) and on a slice of the 670K-shaped one.
+_SINGLE_THREAD_SNIPPET = r"""
+import json, sys, time
+import numpy as np
+sys.path.insert(0, ROOT)
+from oracle import oracle as O
+from synthetic import get_workload, make_inputs
+res = {"threads": O.num_threads()}
+for name, ngroups in (("tiny_4k", None), ("amazon670k_shaped", 1024)):
+    w = get_workload(name)
+    d = make_inputs(w, dZ=False)
+    K = w.K if ngroups is None else ngroups
+    lo, hi = 0, K * w.G
+    rp, cols = [0], []
+    for b in range(w.B):
+        c = d["y_col"][d["y_rowptr"][b]:d["y_rowptr"][b + 1]]
+        c = c[(c >= lo) & (c < hi)] - lo
+        cols.append(c)
+        rp.append(rp[-1] + c.size)
+    t0 = time.perf_counter()
+    O.oracle_step(d["h"], np.ascontiguousarray(d["idx"][:K]), np.ascontiguousarray(d["W"][:hi]),
+                  np.array(rp, np.int32), np.concatenate(cols).astype(np.int32), 1.0 / w.B, w.G)
+    el = time.perf_counter() - t0
+    res[name] = {"groups": K, "of": w.K, "seconds": round(el, 3),
+                 "seconds_per_step": round(el * w.K / K, 2), "samples_per_s": round(w.B / (el * w.K / K), 4)}
+print(json.dumps(res))
+"""
+
+
+def cpu_single_thread(timeout=120):
+    """Single-threaded oracle step timings (child process, OMP_NUM_THREADS=1)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = f"ROOT = {ROOT!r}\n" + _SINGLE_THREAD_SNIPPET
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=timeout)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else {"error": r.stderr[-300:]}
+    except (subprocess.TimeoutExpired, ValueError, IndexError) as e:
+        return {"error": str(e)[:300]}
+
+
+def dense_point(w, d, dev, sh, ev, reps=10):
+    """FLOPs-matched dense context: this library's fused step with H = F and
+    every index set [0, F) (a dense bottleneck layer of the same useful
+    FLOPs), and the three products of that dense layer as library GEMMs
+    (torch.matmul on bf16, hipBLASLt; bf16 outputs, so they write half the
+    bytes of the fp32 dW)."""
+    import numpy as np
+    import torch
+
+    import group_shared_fixed_amd as hs
+    B, K, G, F, L = w.B, w.K, w.G, w.F, w.L
+    hF = bf16_dev(np.ascontiguousarray(d["h"][:, :F]), dev)
+    W = bf16_dev(d["W"], dev)
+    idxF = torch.arange(F, dtype=torch.int32, device=dev).repeat(K, 1).contiguous()
+    rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+    out = {"dW": torch.empty(L, F, dtype=torch.float32, device=dev),
+           "dh": torch.empty(B, F, dtype=torch.float32, device=dev), "Z": None, "loss": None}
+    ws = torch.empty(hs.workspace_size("step", B, F, K, G, F, "det"), dtype=torch.uint8, device=dev)
+    ours = 1e3 * time_call(lambda: hs.step(hF, idxF, W, rp, col, 1.0 / B, G, mode="det", out=out, workspace=ws),
+                           reps, sh, ev)
+    del out, ws, idxF
+    WT = W.t().contiguous()                       # F x L
+    dZ = bf16_dev(d["dZ"], dev) if "dZ" in d else torch.randn(B, L, device=dev).to(torch.bfloat16)
+    dZT = dZ.t().contiguous()                     # L x B
+    Z = torch.empty(B, L, dtype=torch.bfloat16, device=dev)
+    dWl = torch.empty(L, F, dtype=torch.bfloat16, device=dev)
+    dhl = torch.empty(B, F, dtype=torch.bfloat16, device=dev)
+    t_f = 1e3 * time_call(lambda: torch.matmul(hF, WT, out=Z), reps, sh, ev)
+    t_w = 1e3 * time_call(lambda: torch.matmul(dZT, hF, out=dWl), reps, sh, ev)
+    t_h = 1e3 * time_call(lambda: torch.matmul(dZ, W, out=dhl), reps, sh, ev)
+    del WT, dZT, Z, dWl, dhl, dZ, W, hF
+    torch.cuda.empty_cache()
+    return {"ours_step_dense_us": round(ours, 2),
+            "library_gemms_us": {"fwd": round(t_f, 2), "dW": round(t_w, 2), "dh": round(t_h, 2),
+                                 "sum": round(t_f + t_w + t_h, 2)},
+            "what": f"haste_step at H = F = {F} with every I_k = [0, {F}); the dense layer's three products "
+                    f"(B x F x L each) as torch.matmul bf16 GEMMs"}
+
+
 def cpu_baseline(w, d, seconds):
     """The oracle (as is) on consecutive group slices, all batch rows, until
     `seconds` of wall time are spent; extrapolated to the whole step."""
@@ -211,7 +350,7 @@ def cpu_baseline(w, d, seconds):
     return {"value": round(B / t_full, 3), "unit": "samples/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"fp64 oracle step (fwd+BCE+dW+dh) on label groups [0, {done}) of {K}, all {B} samples; "
                       f"{el:.1f} s wall, extrapolated x{K / done:.2f} to the full step",
-            "seconds_per_step": round(t_full, 3)}
+            "seconds_per_step": round(t_full, 3), "cpu_model": cpu_model()}
 
 
 def sweep_g(args):
@@ -693,6 +832,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip unfused calls and the G=1 baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the FLOPs-matched dense point")
+    ap.add_argument("--no-calibrate", action="store_true",
+                    help="skip the copy / GEMM calibration before the warm-up steps")
     ap.add_argument("--report", default=None, help="also write the JSON line to this file")
     ap.add_argument("--counter-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a few steps plus a plain 1 GiB copy, no JSON line")
@@ -769,6 +911,12 @@ def main():
         log("[bench] counter run done (3 steps, 2 copies of 1 GiB)")
         return
 
+    machine = None
+    if not args.no_calibrate:
+        log("[bench] calibrating (copy, dense bf16 GEMM)")
+        machine = calibrate(dev)
+        log(f"[bench] copy {machine['copy_gbs']} GB/s, bf16 GEMM {machine['bf16_gemm_tflops']} TFLOP/s")
+
     nev = 5 * args.steps
     ev = HipEvents(nev + 2)
 
@@ -809,9 +957,13 @@ def main():
 
     def roof(kernel, label, nbytes, us):
         ach = nbytes / (us * 1e-6) / 1e9
-        return {"kernel": label, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
-                "algorithmic_bytes": nbytes, "avg_us": round(us, 2)}
+        r = {"kernel": label, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
+             "algorithmic_bytes": nbytes, "avg_us": round(us, 2)}
+        if machine:
+            r["peak_measured"] = machine["copy_gbs"]
+            r["frac_measured"] = round(ach / machine["copy_gbs"], 4)
+        return r
 
     ra = roof("k_group_fwd", "k_group_fwd<STEP_DW> (forward + BCE + dW)", bytes_a, ph["fwd_bce_dw_us"])
     rb = roof("k_group_dh", "k_group_dh32 / k_group_dh, from labels (feature gradient, logits recomputed)", bytes_b,
@@ -840,6 +992,9 @@ def main():
         "roofline_other": other,
         "kernels_us": {k: round(v, 2) for k, v in ph.items()},
     }
+    if machine:
+        res["machine"] = machine
+        res["pct_measured_gemm"] = round(100 * useful_tflops / machine["bf16_gemm_tflops"], 2)
     log(f"[bench] step {ms_step:.3f} ms  phases {res['kernels_us']}")
 
     if not args.no_extra:
@@ -873,16 +1028,31 @@ def main():
         extra["speedup_fwd_vs_G1"] = round(extra["fixed_fwd_us"] / extra["fwd_us"], 2)
         extra["speedup_bwd_vs_G1"] = round((extra["fixed_bwd_w_us"] + extra["fixed_bwd_h_atomic_us"]) /
                                            (extra["bwd_w_us"] + extra["bwd_h_atomic_us"]), 2)
-        bytes_fwd = L * F * 2 + K * F * 4 + B * H * 2 + B * L * 4
-        bytes_bwh = B * L * 2 + L * F * 2 + K * F * 4 + B * H * 4
-        extra["fwd_hbm_frac"] = round(bytes_fwd / (extra["fwd_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-        extra["bwd_h_atomic_hbm_frac"] = round(bytes_bwh / (extra["bwd_h_atomic_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        # every call against its own HBM floor (compulsory bytes once at 8 TB/s)
+        floors = {
+            "fwd": L * F * 2 + K * F * 4 + B * H * 2 + B * L * 4,
+            "bwd_w": B * L * 2 + K * F * 4 + B * H * 2 + L * F * 4,
+            "bwd_h_atomic": B * L * 2 + L * F * 2 + K * F * 4 + B * H * 4,
+            "bwd_h_det": B * L * 2 + L * F * 2 + K * F * 4 + B * H * 4,
+            "fixed_fwd": L * F * 4 + L * F * 2 + B * H * 2 + B * L * 4,
+            "fixed_bwd_w": L * F * 4 + B * L * 2 + B * H * 2 + L * F * 4,
+            "fixed_bwd_h_atomic": L * F * 4 + L * F * 2 + B * L * 2 + B * H * 4,
+        }
+        for name, nbytes in floors.items():
+            extra[name + "_hbm_frac"] = round(nbytes / (extra[name + "_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         res["extra"] = extra
-        del Z
+        del Z, dW, dh, dZ, idx1
+        torch.cuda.empty_cache()
+        if not args.no_dense:
+            log("[bench] FLOPs-matched dense point")
+            res["dense_flops_matched"] = dense_point(w, d, dev, sh, ev)
+            res["dense_flops_matched"]["grouped_step_us"] = round(ph["step_events_us"], 2)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+        log("[bench] timing the CPU oracle on one thread")
+        res["cpu_baseline"]["single_thread"] = cpu_single_thread()
     ev.close()
     line = json.dumps(res)
     print(line, flush=True)

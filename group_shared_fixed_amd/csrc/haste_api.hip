@@ -57,11 +57,11 @@ Layout layout(int op, int64_t B, int64_t H, int64_t G, int64_t F, int dh_mode)
 {
     Layout l{};
     l.Bp = round_up(B, 32);
-    // grouped dh kernels pick their tile height by shape; the G = 1 baseline uses 16 rows.
+    // grouped dh kernels pick their tile height by shape; the G = 1 baseline uses 32 rows.
     // About two workgroups per CU for 16-row tiles, one for 32-row tiles; the
     // chunk count is a multiple of the 8 XCDs.
     l.rows = (op == HASTE_OP_BWD_H || op == HASTE_OP_STEP) ? dh_tile_rows((int)G, (int)F, H, op == HASTE_OP_STEP)
-                                                           : kDhRows;
+             : (op == HASTE_OP_FIXED_BWD_H ? 32 : kDhRows);
     l.ntiles = (int)((B + l.rows - 1) / l.rows);
     const int target = l.rows == 32 ? 256 : 512;
     int nc = (target / l.ntiles) / 8 * 8;
@@ -106,6 +106,10 @@ int check_shape(int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, bool fixe
     if (H > 1024) return HASTE_ERR_UNSUPPORTED;
     if (K > kMaxLabels / G) return HASTE_ERR_UNSUPPORTED;
     if (B > (1 << 24)) return HASTE_ERR_UNSUPPORTED;
+    // the gathers address the feature-major copy hT (H x Bp bf16) with 32-bit
+    // byte offsets, and its transpose kernel runs Bp / 32 workgroups along y
+    const int64_t Bp = round_up(B, 32);
+    if (2 * H * Bp >= (1LL << 31) || Bp / 32 > 65535) return HASTE_ERR_UNSUPPORTED;
     return HASTE_OK;
 }
 
@@ -456,7 +460,7 @@ int haste_fixed_fwd(const haste_bf16* h, const int32_t* idx1, const haste_bf16* 
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FixedArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.W = W; a.L = L; a.Z = Z;
-    if (!launch_fixed_fwd((int)F, a, 1024, stream)) return HASTE_ERR_UNSUPPORTED;
+    if (!launch_fixed_fwd((int)F, a, 768, stream)) return HASTE_ERR_UNSUPPORTED;
     return hip_status();
 }
 
@@ -472,7 +476,7 @@ int haste_fixed_bwd_w(const haste_bf16* h, const int32_t* idx1, const haste_bf16
     launch_transpose_h(h, hT, B, H, l.Bp, stream);
     FixedArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.H = H; a.idx1 = idx1; a.L = L; a.dZ = dZ; a.dW = dW;
-    if (!launch_fixed_bwd_w((int)F, a, 1024, stream)) return HASTE_ERR_UNSUPPORTED;
+    if (!launch_fixed_bwd_w((int)F, a, 768, stream)) return HASTE_ERR_UNSUPPORTED;
     return hip_status();
 }
 

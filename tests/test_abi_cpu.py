@@ -96,6 +96,14 @@ def test_fwd_bce_bwd_rejects(L):
     assert _fbb(L, ws=P(0x100010)) == WS
 
 
+def test_hT_offsets_stay_32_bit(L):
+    """Shapes whose feature-major copy of h would pass 2^31 bytes (32-bit
+    gather offsets) or need more than 65535 transpose workgroups are refused."""
+    assert _fwd(L, B=1 << 20, H=1024) == UNSUP                   # exactly 2^31 bytes
+    assert _fwd(L, B=(1 << 21) + 32, H=64, F=64) == UNSUP        # Bp / 32 > 65535
+    assert L.haste_bwd_w(A, A, A, A, 1 << 20, 1024, 100, 32, 64, A, 1 << 40, None) == UNSUP
+
+
 def test_workspace_status_rejects(L):
     out = ctypes.c_int32(0)
     assert L.haste_workspace_status(None, ctypes.byref(out), None) == NULL
