@@ -20,6 +20,58 @@ def _int_emb(L, H, seed, lo=-2, hi=3):
     return bf16_bits(np.random.default_rng(seed).integers(lo, hi, size=(L, H)).astype(np.float32))
 
 
+def assert_assign_valid(a, S, eps, what):
+    """Every assignment takes a centre whose score is within eps of the row's
+    best (the oracle's pick up to a near tie)."""
+    rows = np.arange(S.shape[0])
+    gap = S.max(axis=1) - S[rows, a]
+    bad = np.nonzero(gap > eps)[0]
+    assert bad.size == 0, f"{what}: {bad.size} assignments miss the best score by > {eps}, first {bad[:5]}"
+
+
+def assert_greedy_valid(E, a, C, G, perm, clusters, eps):
+    """Replays the greedy rule on the given clusters with the GPU's own picks:
+    within a cluster the groups come in order, each lists its members in
+    increasing id, its seed is the lowest-id member not yet grouped (exact),
+    and each of the other G - 1 members is an ungrouped member of the cluster
+    whose similarity with the seed is within eps of the (G - 1)-th largest
+    among the ungrouped candidates (the oracle's pick up to a near tie).  The
+    leftovers of all clusters follow the greedy groups in (cluster, id) order
+    when every cluster is replayed."""
+    Ef = O._bf16_f64(E)
+    L = E.shape[0]
+    sizes = np.bincount(a, minlength=C)
+    n_c = sizes // G
+    gbase = np.concatenate([[0], np.cumsum(n_c)[:-1]]).astype(np.int64)
+    near = 0
+    leftovers = {}
+    for c in clusters:
+        members = np.nonzero(a == c)[0]
+        free = np.ones(L, bool)
+        for k in range(int(n_c[c])):
+            g = perm[(gbase[c] + k) * G:(gbase[c] + k + 1) * G]
+            assert list(g) == sorted(g), f"cluster {c} group {k} not in increasing id"
+            assert (a[g] == c).all(), f"cluster {c} group {k} takes a label of another cluster"
+            assert free[g].all(), f"cluster {c} group {k} reuses a grouped label"
+            cand = members[free[members]]
+            seed = cand[0]
+            assert seed in g, f"cluster {c} group {k}: seed {seed} missing"
+            others = cand[1:]
+            sim = Ef[others] @ Ef[seed]
+            t = np.sort(sim)[::-1][G - 2]
+            picked = np.isin(others, g)
+            assert picked.sum() == G - 1
+            worst = sim[picked].min()
+            assert worst >= t - eps, f"cluster {c} group {k}: a pick {t - worst:.3e} below the (G-1)-th best"
+            near += int(worst < t)
+            free[g] = False
+        leftovers[c] = members[free[members]]
+    if len(clusters) == C:
+        rest = np.concatenate([leftovers[c] for c in range(C)])
+        assert np.array_equal(perm[int(n_c.sum()) * G:], rest), "leftovers not in (cluster, id) order"
+    return near
+
+
 @pytest.mark.parametrize("L,C,H", [(3000, 37, 64), (513, 5, 8), (4096, 300, 128)])
 def test_kmeans_assign_integer_exact(L, C, H):
     E = _int_emb(L, H, 90 + C)
@@ -68,8 +120,8 @@ def test_kmeans_update_steps():
         Mc0, v0 = to_host(Mc).astype(np.float64), to_host(v).astype(np.int64)
         a, _ = hs.kmeans_assign(Ed, Mb, rows=to_dev_i32(b))
         a_h = to_host(a)
-        ra, _ = O.oracle_kmeans_assign(np.ascontiguousarray(E[b]), to_host(Mb))
-        assert (a_h == ra).mean() > 0.999, "batch assignments"
+        Sb = O._bf16_f64(E[b]) @ O._bf16_f64(to_host(Mb)).T
+        assert_assign_valid(a_h, Sb, 1e-5, f"batch assignments of step {it}")
         hs.kmeans_update(Ed, to_dev_i32(b), a, Mc, Mb, v)
         want, want_v = O.oracle_kmeans_update(E, b, a_h, Mc0, v0)
         got = to_host(Mc).astype(np.float64)
@@ -82,10 +134,19 @@ def test_kmeans_update_steps():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("L,C,H,G", [(2048, 13, 64, 16), (1536, 7, 32, 32), (4096, 40, 128, 64), (960, 1, 16, 16)])
-def test_group_greedy_integer_exact(L, C, H, G):
+@pytest.mark.parametrize("L,C,H,G,big", [(2048, 13, 64, 16, 0), (1536, 7, 32, 32, 0), (4096, 40, 128, 64, 0),
+                                         (960, 1, 16, 16, 0),
+                                         # clusters past 1,024 members keep their per-member
+                                         # state in the workspace instead of LDS
+                                         (4096, 3, 32, 16, 1), (6144, 4, 64, 32, 1), (8192, 2, 32, 64, 1),
+                                         (2048, 1, 16, 32, 1)])
+def test_group_greedy_integer_exact(L, C, H, G, big):
     E = _int_emb(L, H, 94 + G, -1, 2)
-    a = np.random.default_rng(95 + C).integers(0, C, size=L).astype(np.int32)
+    rng = np.random.default_rng(95 + C)
+    a = rng.integers(0, C, size=L).astype(np.int32)
+    if big:
+        a[rng.random(L) < 0.7] = 0                 # cluster 0 holds ~70 % of the labels
+        assert (a == 0).sum() > 1024
     perm = to_host(hs.group_greedy(to_dev_bf16(E), to_dev_i32(a), C, G))
     want = O.oracle_group_greedy(E, a, C, G)
     assert sorted(perm.tolist()) == list(range(L)), "not a permutation"
@@ -106,11 +167,8 @@ def test_group_greedy_unit_vectors_and_repeat():
     want = O.oracle_group_greedy(E, a, C, G)
     same = np.mean([(p1[k * G:(k + 1) * G] == want[k * G:(k + 1) * G]).all() for k in range(L // G)])
     say(f"    {100 * same:.2f} % of groups identical to the oracle's")
-    assert same >= 0.99
-    n_greedy = sum(int((a == c).sum()) // G for c in range(C))
-    for k in range(n_greedy):
-        g = p1[k * G:(k + 1) * G]
-        assert len(set(a[g].tolist())) == 1 and list(g) == sorted(g)
+    near = assert_greedy_valid(E, a, C, G, p1, list(range(C)), 1e-4)
+    say(f"    every group valid; {near} decided within a near tie")
 
 
 @pytest.mark.slow
@@ -148,7 +206,7 @@ def test_grouping_fullsize_sampled():
         g = perm[k * G:(k + 1) * G]
         assert len(set(a[g].tolist())) == 1 and list(g) == sorted(g), f"group {k}"
     agree = 0
-    cl = [c for c in rng.choice(C, size=40, replace=False) if n_c[c] > 0]
+    cl = [int(c) for c in rng.choice(C, size=40, replace=False) if n_c[c] > 0]
     for c in cl:
         members = np.nonzero(a == c)[0]
         pad = (-members.size) % G                  # a second, padding cluster keeps L % G == 0
@@ -159,4 +217,5 @@ def test_grouping_fullsize_sampled():
         got = perm[gbase[c] * G:(gbase[c] + n_c[c]) * G]
         agree += int(np.array_equal(got, want))
     say(f"    {agree}/{len(cl)} sampled clusters identical to the oracle's groups")
-    assert agree >= len(cl) - 1
+    near = assert_greedy_valid(E, a, C, G, perm, cl, 1e-4)
+    say(f"    every sampled cluster's groups valid; {near} picks decided within a near tie")
