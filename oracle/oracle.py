@@ -396,3 +396,57 @@ def oracle_group_greedy(E, a, C, G):
     for i in range(0, len(leftovers), G):
         groups.append(leftovers[i:i + G])
     return np.array([x for g in groups for x in g], dtype=np.int32)
+
+
+# ------------------------------------------------------------ label embeddings
+#
+# HASTE notes, "group-shared fixed fan-in": the grouping works on label
+# embeddings, a label's embedding being the normalized mean of the encoder
+# features of the samples that have the label as a positive.  Over a
+# dataset given as batches of features h (B x H bf16) and 0/1 labels (CSR,
+# ids in [0, L)), the oracle keeps per label the fp64 sum of those features
+# and the number of positives; the direction of the mean is the direction
+# of the sum.
+
+def oracle_label_emb_accumulate(S, n, h, y_rowptr, y_col):
+    """Adds one batch in place: for every sample b and every positive label
+    l of b, S[l] += h[b] and n[l] += 1.  S: L x H fp64, n: L int64.
+    Returns (S, n)."""
+    hf = _bf16_f64(h)
+    rp = np.asarray(y_rowptr, dtype=np.int64)
+    col = np.asarray(y_col, dtype=np.int64)
+    for b in range(hf.shape[0]):
+        for p in range(rp[b], rp[b + 1]):
+            S[col[p]] += hf[b]
+            n[col[p]] += 1
+    return S, n
+
+
+def f64_to_bf16_bits(x):
+    """Round fp64 values to the nearest bf16, ties to even (directly, without
+    an fp32 step); returns the 16-bit patterns."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                               # x = m 2^e, 0.5 <= |m| < 1
+    q = np.rint(np.ldexp(m, 8))                      # 8 significant bits, ties to even
+    r = np.ldexp(q, e - 8).astype(np.float32)        # exact in fp32
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def oracle_label_emb_finalize(S, n):
+    """e_l = S_l / |S_l|, rounded to bf16 (L x H bits); 0 for a label without
+    positives or with a zero sum."""
+    S = np.asarray(S, dtype=np.float64)
+    norm = np.sqrt((S * S).sum(axis=1))
+    ok = (np.asarray(n) > 0) & (norm > 0)
+    E = np.zeros_like(S)
+    E[ok] = S[ok] / norm[ok, None]
+    return f64_to_bf16_bits(E)
+
+
+def oracle_label_emb(batches, L, H):
+    """Embeddings from a list of (h, y_rowptr, y_col) batches: (E bits, S, n)."""
+    S = np.zeros((L, H), dtype=np.float64)
+    n = np.zeros(L, dtype=np.int64)
+    for h, rp, col in batches:
+        oracle_label_emb_accumulate(S, n, h, rp, col)
+    return oracle_label_emb_finalize(S, n), S, n

@@ -669,6 +669,98 @@ def pin_group_greedy(lib):
         assert sum(1 for x in rest if a2[x] == c) == int((a2 == c).sum()) % G, f"leftovers of cluster {c}"
 
 
+def _csr(rows):
+    rp = np.zeros(len(rows) + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    col = np.array([x for r in rows for x in r], np.int32)
+    return rp, col
+
+
+def pin_label_emb_hand_example(lib):
+    """One-hot features: sample features e_0, e_0, e_1, e_2 (H = 4); label 0 is
+    positive for samples 0, 1, 2 -> sum (2, 1, 0, 0) -> (2, 1, 0, 0) / sqrt 5;
+    label 1 for sample 3 only -> e_2; label 2 for none -> 0; label 3 for
+    samples 2 and 3 -> (0, 1, 1, 0) / sqrt 2."""
+    H, L = 4, 4
+    hf = np.zeros((4, H), np.float32)
+    hf[0, 0] = hf[1, 0] = hf[2, 1] = hf[3, 2] = 1.0
+    rp, col = _csr([[0], [0], [0, 3], [1, 3]])
+    E, S, n = O.oracle_label_emb([(bf16_bits(hf), rp, col)], L, H)
+    want = np.array([[2, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 0], [0, 1, 1, 0]], np.float64)
+    _close(S, want, what="sums")
+    assert n.tolist() == [3, 1, 0, 2]
+    r5, r2 = 1 / np.sqrt(5), 1 / np.sqrt(2)
+    want_e = np.array([[2 * r5, r5, 0, 0], [0, 0, 1, 0], [0, 0, 0, 0], [0, r2, r2, 0]])
+    # bf16 keeps 8 significant bits
+    _close(_f(E), want_e, rtol=2 ** -8, atol=0, what="embeddings")
+    assert (E[2] == 0).all()
+
+
+def pin_label_emb_dense_product(lib):
+    """The sums are Y^T h for the dense 0/1 label matrix Y (a matrix product,
+    per batch, added over batches); the counts its column sums; every
+    embedding of a label with positives has unit norm up to bf16 rounding and
+    points along its sum."""
+    rng = np.random.default_rng(41)
+    L, H = 30, 24
+    batches, Ssum, nsum = [], np.zeros((L, H)), np.zeros(L)
+    for B in (17, 9, 1):
+        h = bf16_bits(rng.normal(size=(B, H)).astype(np.float32))
+        rows = [sorted(rng.choice(L - 3, size=rng.integers(0, 6), replace=False).tolist()) for _ in range(B)]
+        rp, col = _csr(rows)
+        Y = np.zeros((B, L))
+        for b, r in enumerate(rows):
+            Y[b, r] = 1.0
+        Ssum += Y.T @ _f(h)
+        nsum += Y.sum(axis=0)
+        batches.append((h, rp, col))
+    E, S, n = O.oracle_label_emb(batches, L, H)
+    _close(S, Ssum, what="sums vs Y^T h")
+    assert (n == nsum).all()
+    Ef = _f(E)
+    has = nsum > 0
+    assert (Ef[~has] == 0).all(), "labels without positives must get 0"
+    norms = np.linalg.norm(Ef[has], axis=1)
+    assert np.all(np.abs(norms - 1) < 2 ** -7), norms
+    cos = (Ef[has] * S[has]).sum(axis=1) / (norms * np.linalg.norm(S[has], axis=1))
+    assert np.all(cos > 1 - 2 ** -12)
+
+
+def pin_label_emb_invariances(lib):
+    """Splitting a batch, scaling every feature by 2 (exact in bf16) or adding
+    a copy of every sample leaves the embeddings bit for bit; sums scale and
+    counts double as they must."""
+    rng = np.random.default_rng(42)
+    L, H, B = 20, 16, 24
+    h = bf16_bits(rng.normal(size=(B, H)).astype(np.float32))
+    rows = [sorted(rng.choice(L, size=rng.integers(0, 5), replace=False).tolist()) for _ in range(B)]
+    rp, col = _csr(rows)
+    E1, S1, n1 = O.oracle_label_emb([(h, rp, col)], L, H)
+    parts = []
+    for lo, hi in ((0, 7), (7, 8), (8, B)):
+        r2, c2 = _csr(rows[lo:hi])
+        parts.append((np.ascontiguousarray(h[lo:hi]), r2, c2))
+    E2, S2, n2 = O.oracle_label_emb(parts, L, H)
+    assert (E1 == E2).all() and (n1 == n2).all()
+    _close(S1, S2, what="split batches")
+    h2 = bf16_bits((2 * _f(h)).astype(np.float32))
+    E3, S3, _ = O.oracle_label_emb([(h2, rp, col)], L, H)
+    assert (E3 == E1).all()
+    _close(S3, 2 * S1, what="doubled features")
+    E4, S4, n4 = O.oracle_label_emb([(h, rp, col), (h, rp, col)], L, H)
+    assert (E4 == E1).all() and (n4 == 2 * n1).all()
+    _close(S4, 2 * S1, what="repeated batch")
+    one = np.flatnonzero(n1 == 1)
+    for l in one[:5]:
+        b = [i for i, r in enumerate(rows) if l in r][0]
+        u = _f(h[b]) / np.linalg.norm(_f(h[b]))
+        assert (E1[l] == O.f64_to_bf16_bits(u)).all(), "a single positive gives its own direction"
+    # direct rounding: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> 1 (even);
+    # 1 + 3 * 2^-8 rounds up to 1 + 2^-6 ... checked on the bit patterns
+    r = O.f64_to_bf16_bits(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -9), 0.0]))
+    assert r.tolist() == [0x3F80, 0x3F82, 0xBF80, 0x0000], [hex(x) for x in r]
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -693,4 +785,7 @@ ALL_PINS = [
     pin_kmeans_assign_brute_force,
     pin_kmeans_update,
     pin_group_greedy,
+    pin_label_emb_hand_example,
+    pin_label_emb_dense_product,
+    pin_label_emb_invariances,
 ]

@@ -110,6 +110,12 @@ PY_MUTANTS = {
     "group_farthest": ("key=lambda i: (-sims[i], rest[i])", "key=lambda i: (sims[i], rest[i])"),
     "group_unsorted_members": ("            chosen = sorted([seed] + [rest[i] for i in order])",
                                "            chosen = [seed] + [rest[i] for i in order]"),
+    "emb_mean_not_normalized": ("    E[ok] = S[ok] / norm[ok, None]", "    E[ok] = S[ok] / np.asarray(n)[ok, None]"),
+    "emb_drops_last_positive": ("        for p in range(rp[b], rp[b + 1]):\n            S[col[p]] += hf[b]",
+                                "        for p in range(rp[b], rp[b + 1] - 1):\n            S[col[p]] += hf[b]"),
+    "emb_entry_as_sample": ("            S[col[p]] += hf[b]", "            S[col[p]] += hf[p % hf.shape[0]]"),
+    "emb_round_up": ("    q = np.rint(np.ldexp(m, 8))", "    q = np.ceil(np.ldexp(m, 8))"),
+    "emb_zero_rows_kept": ("    ok = (np.asarray(n) > 0) & (norm > 0)", "    ok = norm >= 0"),
     "rewire_grown_keep_old_weight": (
         "            if c in kept:\n                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]",
         "            W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept.get(c, f_new)]"),
@@ -135,7 +141,8 @@ def test_head_mutant_is_caught(name, monkeypatch):
         monkeypatch.setattr(O, "oracle_joint_step", mod.oracle_joint_step)
         for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire", "e4m3_decode", "e4m3_encode",
                    "w8_group_exponent", "oracle_quantize_w8", "oracle_dequantize_w8", "oracle_kmeans_assign",
-                   "oracle_kmeans_update", "oracle_group_greedy"):
+                   "oracle_kmeans_update", "oracle_group_greedy", "oracle_label_emb_accumulate",
+                   "f64_to_bf16_bits", "oracle_label_emb_finalize", "oracle_label_emb"):
             monkeypatch.setattr(O, fn, getattr(mod, fn))
         failed = _pins_fail(lib)
     assert failed, f"mutant {name} passes every pin"
