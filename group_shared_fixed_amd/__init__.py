@@ -27,6 +27,8 @@ from .binding import (  # noqa: F401
     kmeans_assign,
     kmeans_init,
     kmeans_update,
+    label_emb_accumulate,
+    label_emb_finalize,
     rewire,
     rewire_workspace_size,
     step,

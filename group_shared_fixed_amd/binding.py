@@ -56,6 +56,9 @@ SIGNATURES = {
     "haste_kmeans_update": (_M, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
     "haste_group_workspace_size": (_S, [_I, _I]),
     "haste_group_greedy": (_M, [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P]),
+    "haste_label_emb_workspace_size": (_S, [_I]),
+    "haste_label_emb_accumulate": (_M, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P]),
+    "haste_label_emb_finalize": (_M, [_P, _P, _I, _I, _P, _P]),
     "haste_rewire_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "haste_rewire": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
@@ -540,6 +543,32 @@ def group_greedy(E, assign, C, G, workspace=None, stream=None):
     _check("haste_group_greedy", lib().haste_group_greedy(_ptr(E), _ptr(assign), L, C, H, G, _ptr(perm), _ptr(ws),
                                                            ws.numel(), _stream(E, stream)))
     return perm
+
+
+def label_emb_accumulate(h, y_rowptr, y_col, S, counts, nnz=None, workspace=None, stream=None):
+    """Adds one batch into the per-label feature sums S (L x H fp32) and
+    positive counts (L int32), in place.  nnz defaults to y_col.numel()."""
+    _bits(h); _i32(y_rowptr); _i32(y_col); _i32(counts)
+    B, H = h.shape
+    L = S.shape[0]
+    n = int(y_col.numel() if nnz is None else nnz)
+    ws = _ws(int(lib().haste_label_emb_workspace_size(n)), h.device, workspace)
+    _check("haste_label_emb_accumulate", lib().haste_label_emb_accumulate(
+        _ptr(h), _ptr(y_rowptr), _ptr(y_col), n, B, H, L, _ptr(S), _ptr(counts), _ptr(ws), ws.numel(),
+        _stream(h, stream)))
+    return S, counts
+
+
+def label_emb_finalize(S, counts, E=None, stream=None):
+    """E (L x H bf16) = the directions of the per-label sums (0 without positives)."""
+    torch = _torch()
+    _i32(counts)
+    L, H = S.shape
+    if E is None:
+        E = torch.empty(L, H, dtype=torch.bfloat16, device=S.device)
+    _check("haste_label_emb_finalize", lib().haste_label_emb_finalize(_ptr(S), _ptr(counts), L, H, _ptr(E),
+                                                                       _stream(S, stream)))
+    return E
 
 
 def rewire_workspace_size(B, H, K, G, F) -> int:

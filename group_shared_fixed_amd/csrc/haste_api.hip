@@ -821,6 +821,39 @@ int haste_group_greedy(const haste_bf16* E, const int32_t* assign, int64_t L, in
 
 void haste_test_set_turn_spins(int spins) { g_turn_spins.store(spins < 0 ? kTurnSpins : spins); }
 
+size_t haste_label_emb_workspace_size(int64_t nnz)
+{
+    if (nnz < 0) return 0;
+    return align256((size_t)group_sort_size(nnz) * 8) + align256((size_t)nnz * 4);
+}
+
+int haste_label_emb_accumulate(const haste_bf16* h, const int32_t* y_rowptr, const int32_t* y_col, int64_t nnz,
+                               int64_t B, int64_t H, int64_t L, float* S, int32_t* counts, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    if (!h || !y_rowptr || !S || !counts || (nnz > 0 && !y_col)) return HASTE_ERR_NULL;
+    if (B < 1 || nnz < 0) return HASTE_ERR_DIM;
+    HASTE_TRY(check_emb(L, 1, H));
+    if (nnz > ((int64_t)1 << 30) || B > ((int64_t)1 << 30)) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(y_rowptr) || (y_col && !aligned16(y_col)) || !aligned16(S) || !aligned16(counts))
+        return HASTE_ERR_ALIGN;
+    HASTE_TRY(check_ws(workspace, workspace_bytes, haste_label_emb_workspace_size(nnz)));
+    uint64_t* keys = (uint64_t*)workspace;
+    int32_t* sample = (int32_t*)((char*)workspace + align256((size_t)group_sort_size(nnz) * 8));
+    run_label_emb_accumulate(h, y_rowptr, y_col, nnz, B, H, S, counts, keys, sample, stream);
+    return hip_status();
+}
+
+int haste_label_emb_finalize(const float* S, const int32_t* counts, int64_t L, int64_t H, haste_bf16* E,
+                             hipStream_t stream)
+{
+    if (!S || !counts || !E) return HASTE_ERR_NULL;
+    HASTE_TRY(check_emb(L, 1, H));
+    if (!aligned16(S) || !aligned16(counts) || !aligned16(E)) return HASTE_ERR_ALIGN;
+    run_label_emb_finalize(S, counts, L, H, E, stream);
+    return hip_status();
+}
+
 int haste_workspace_status(const void* workspace, int32_t* status, hipStream_t stream)
 {
     if (!workspace || !status) return HASTE_ERR_NULL;

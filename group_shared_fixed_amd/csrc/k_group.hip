@@ -446,6 +446,8 @@ void sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t s)
 
 int64_t group_sort_size(int64_t n) { return sort_size(n); }
 
+void group_sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t s) { sort_keys(seg, n, keys, s); }
+
 int64_t kmeans_chunk_rows(int64_t n_rows, int64_t C)
 {
     int64_t lc = ((int64_t)256 << 20) / (4 * ((C + 3) / 4 * 4));

@@ -164,6 +164,15 @@ bool launch_rewire_select(int G, int F, const int32_t* idx, const uint16_t* W, c
 // Label grouping (mini-batch spherical k-means and greedy groups).
 // Keys sorted for a segment list of n entries take group_sort_size(n) x 8 bytes.
 int64_t group_sort_size(int64_t n);
+// keys[i] = seg[i] << 32 | i for i < n, sorted ascending (padding keys, all
+// ones, to group_sort_size(n) at the end).
+void group_sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t s);
+// Label embeddings: one batch added into the fp32 per-label sums and counts
+// (keys: group_sort_size(nnz) entries, sample: nnz entries), and the bf16
+// directions of the sums.
+void run_label_emb_accumulate(const uint16_t* h, const int32_t* rowptr, const int32_t* col, int64_t nnz, int64_t B,
+                              int64_t H, float* S, int32_t* counts, uint64_t* keys, int32_t* sample, hipStream_t s);
+void run_label_emb_finalize(const float* S, const int32_t* counts, int64_t L, int64_t H, uint16_t* E, hipStream_t s);
 // Rows per product chunk of the k-means assignment (scores chunk x C fp32).
 int64_t kmeans_chunk_rows(int64_t n_rows, int64_t C);
 bool run_kmeans_assign(const uint16_t* E, const int32_t* rows, int64_t n_rows, const uint16_t* M, int64_t C,

@@ -330,6 +330,28 @@ size_t haste_group_workspace_size(int64_t L, int64_t C);
 int haste_group_greedy(const haste_bf16* E, const int32_t* assign, int64_t L, int64_t C, int64_t H, int64_t G,
                        int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Label embeddings for the grouping ("group-shared fixed fan-in" section: a
+ * label's embedding is the normalized mean of the encoder features of the
+ * samples it is positive for).  S (L x H fp32) and counts (L int32) are the
+ * caller's running per-label feature sums and positive counts, zeroed by the
+ * caller before the first batch.  haste_label_emb_accumulate adds one batch:
+ * for every sample b (features h, B x H bf16) and each positive label l of b
+ * (CSR y_rowptr[B + 1] and y_col[nnz], ids in [0, L); nnz = y_rowptr[B],
+ * passed by the caller), S[l] += h[b] and counts[l] += 1.  A label's
+ * contributions from one batch are summed in sample order and added to S
+ * once (no atomics), so S repeats bit for bit for the same batch sequence.
+ * haste_label_emb_finalize: E (L x H bf16) = S_l / |S_l| rounded to nearest
+ * bf16, and 0 for labels without positives.  8 <= H <= 1024 with H % 8 == 0,
+ * L <= 2^30, nnz <= 2^30, B <= 2^30.  Workspace of the accumulation:
+ * haste_label_emb_workspace_size(nnz) bytes (sort keys and the entries'
+ * sample ids), 256-byte aligned. */
+size_t haste_label_emb_workspace_size(int64_t nnz);
+int haste_label_emb_accumulate(const haste_bf16* h, const int32_t* y_rowptr, const int32_t* y_col, int64_t nnz,
+                               int64_t B, int64_t H, int64_t L, float* S, int32_t* counts, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+int haste_label_emb_finalize(const float* S, const int32_t* counts, int64_t L, int64_t H, haste_bf16* E,
+                             hipStream_t stream);
+
 /* Group-level rewiring of the index sets: the discrete phase of the dynamic
  * sparse training ("loss / training strategy" section: every so many steps
  * the group-level I_k are reselected RigL-style with |I_k| = F kept; the

@@ -104,6 +104,26 @@ def test_hT_offsets_stay_32_bit(L):
     assert L.haste_bwd_w(A, A, A, A, 1 << 20, 1024, 100, 32, 64, A, 1 << 40, None) == UNSUP
 
 
+def test_label_emb_rejects(L):
+    def acc(h=A, rp=A, col=A, nnz=10, B=4, H=64, Lb=100, S=A, n=A, ws=A, wsb=1 << 30):
+        return L.haste_label_emb_accumulate(h, rp, col, nnz, B, H, Lb, S, n, ws, wsb, None)
+    assert acc(h=None) == NULL
+    assert acc(col=None) == NULL
+    assert acc(S=None) == NULL
+    assert acc(B=0) == DIM
+    assert acc(nnz=-1) == DIM
+    assert acc(H=60) == UNSUP                      # H % 8
+    assert acc(H=2048) == UNSUP
+    assert acc(S=MIS) == ALIGN
+    assert acc(ws=None) == WS
+    assert acc(wsb=16) == WS
+    assert L.haste_label_emb_workspace_size(5000) == 8192 * 8 + 20224
+    assert L.haste_label_emb_finalize(None, A, 10, 64, A, None) == NULL
+    assert L.haste_label_emb_finalize(A, A, 10, 12, A, None) == UNSUP
+    assert L.haste_label_emb_finalize(A, A, 0, 64, A, None) == DIM
+    assert L.haste_label_emb_finalize(A, A, 10, 64, MIS, None) == ALIGN
+
+
 def test_workspace_status_rejects(L):
     out = ctypes.c_int32(0)
     assert L.haste_workspace_status(None, ctypes.byref(out), None) == NULL
