@@ -689,7 +689,7 @@ def grouping_bench(args):
                    "step": "kmeans_init + iters x (assign batch + update) + full assign + group_greedy"},
         "phases_ms": {"minibatch_assign": round(step_assign, 3), "minibatch_update": round(step_update, 3),
                       "full_assign": round(full_assign, 2), "greedy": round(greedy, 2)},
-        "roofline": {"kernel": "full assignment (rocBLAS bf16 products in label chunks + k_row_argmax)",
+        "roofline": {"kernel": "full assignment (k_assign: fused matrix-core scores + arg-max)",
                      "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "algorithmic_flops": flops_full,
                      "avg_us": round(1e3 * full_assign, 1)},

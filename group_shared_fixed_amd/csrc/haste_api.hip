@@ -709,13 +709,14 @@ int check_emb(int64_t L, int64_t C, int64_t H)
 }
 
 struct KmAssignLayout {
-    size_t gather, scores, blas, total;
+    size_t keys, xpack, mpack, total;
     KmAssignLayout(int64_t n_rows, int64_t C, int64_t H, bool rows)
     {
-        gather = 0;
-        scores = rows ? align256((size_t)n_rows * (size_t)H * 2) : 0;
-        blas = scores + align256((size_t)kmeans_chunk_rows(n_rows, C) * (size_t)((C + 3) / 4 * 4) * 4);
-        total = blas + kHeadBlasWorkspace;
+        const int64_t Hp = kmeans_assign_width(H);
+        keys = 0;
+        xpack = keys + align256((size_t)n_rows * 8);
+        mpack = xpack + ((rows || Hp != H) ? align256((size_t)n_rows * (size_t)Hp * 2) : 0);
+        total = mpack + (Hp != H ? align256((size_t)C * (size_t)Hp * 2) : 0);
     }
 };
 
@@ -753,12 +754,12 @@ int haste_kmeans_assign(const haste_bf16* E, const int32_t* rows, int64_t n_rows
     if (!aligned16(E) || !aligned16(M) || !aligned16(assign) || (rows && !aligned16(rows)) ||
         (score && !aligned16(score)))
         return HASTE_ERR_ALIGN;
+    if (kmeans_assign_tiles(n_rows, C) > ((int64_t)1 << 31)) return HASTE_ERR_UNSUPPORTED;
     const KmAssignLayout l(n_rows, C, H, rows != nullptr);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     char* w = (char*)workspace;
-    if (!run_kmeans_assign(E, rows, n_rows, M, C, H, assign, score, (uint16_t*)(w + l.gather), (float*)(w + l.scores),
-                           w + l.blas, kHeadBlasWorkspace, stream))
-        return HASTE_ERR_HIP;
+    run_kmeans_assign(E, rows, n_rows, M, C, H, assign, score, (uint64_t*)(w + l.keys), (uint16_t*)(w + l.xpack),
+                      (uint16_t*)(w + l.mpack), stream);
     return hip_status();
 }
 

@@ -5,8 +5,8 @@
 // coarse clusters, then, inside each cluster, greedy groups of a seed and
 // its G - 1 nearest neighbours.  Similarity is the dot product of bf16
 // embeddings (the cosine for unit vectors).
-//   assignment: the largest dot product, the lowest centre on ties (a
-//     rocBLAS product in label chunks and k_row_argmax);
+//   assignment: the largest dot product, the lowest centre on ties (the
+//     fused matrix-core kernel of k_assign.hip);
 //   update: Sculley's mini-batch step (a centre becomes the running mean of
 //     everything assigned to it so far) and projection onto the unit sphere,
 //     summing each centre's batch members in batch order;
@@ -16,81 +16,10 @@
 //     concatenated in (cluster, id) order and cut into groups of G.
 // Every step is deterministic: sorts are by (segment, index) keys, sums run
 // in a fixed order, and comparisons break ties by index.
-#include "blas.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace haste {
-
-// out[i] = E[rows[i]] (H bf16, H % 8 == 0), 16-byte pieces.
-__global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict__ E, const int32_t* __restrict__ rows,
-                                                     int64_t n, int64_t H, uint16_t* __restrict__ out)
-{
-    const int64_t pieces = H / 8;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n * pieces; t += (int64_t)gridDim.x * 256) {
-        const int64_t i = t / pieces, p = t % pieces;
-        *reinterpret_cast<u32x4_t*>(out + i * H + 8 * p) = ldg16(E + (int64_t)rows[i] * H + 8 * p);
-    }
-}
-
-// One block per row of S (n x C, row stride ldS, a multiple of 4): the
-// largest value and its column, the lowest column among equal maxima.
-// Threads read 16-byte pieces (columns rise within a thread, so a strict
-// comparison keeps the lowest), then the block reduces with the same rule.
-__global__ __launch_bounds__(256) void k_row_argmax(const float* __restrict__ S, int64_t n, int64_t C, int64_t ldS,
-                                                    int32_t* __restrict__ a, float* __restrict__ smax)
-{
-    __shared__ float sv[4];
-    __shared__ int sc[4];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int64_t row = blockIdx.x;
-    const float* r = S + row * ldS;
-    float bv = -INFINITY;
-    int bc = 0x7fffffff;
-    const int64_t C4 = C / 4;
-#pragma unroll 4
-    for (int64_t i = t; i < C4; i += 256) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(r + 4 * i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (v[e] > bv) {
-                bv = v[e];
-                bc = (int)(4 * i + e);
-            }
-        }
-    }
-    for (int64_t c = 4 * C4 + t; c < C; c += 256) {
-        if (r[c] > bv) {
-            bv = r[c];
-            bc = (int)c;
-        }
-    }
-    auto better = [](float ov, int oc, float v, int c) { return oc != 0x7fffffff && (c == 0x7fffffff || ov > v || (ov == v && oc < c)); };
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oc = __shfl_xor(bc, o, 64);
-        if (better(ov, oc, bv, bc)) {
-            bv = ov;
-            bc = oc;
-        }
-    }
-    if (lane == 0) {
-        sv[w] = bv;
-        sc[w] = bc;
-    }
-    __syncthreads();
-    if (t == 0) {
-        for (int u = 1; u < 4; ++u) {
-            if (better(sv[u], sc[u], bv, bc)) {
-                bv = sv[u];
-                bc = sc[u];
-            }
-        }
-        a[row] = bc == 0x7fffffff ? 0 : bc;
-        if (smax) smax[row] = bv;
-    }
-}
 
 // keys[i] = seg[i] << 32 | i for i < n, all ones for n <= i < N.
 __global__ __launch_bounds__(256) void k_make_keys(const int32_t* __restrict__ seg, int64_t n, int64_t N,
@@ -447,39 +376,6 @@ void sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t s)
 int64_t group_sort_size(int64_t n) { return sort_size(n); }
 
 void group_sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t s) { sort_keys(seg, n, keys, s); }
-
-int64_t kmeans_chunk_rows(int64_t n_rows, int64_t C)
-{
-    int64_t lc = ((int64_t)256 << 20) / (4 * ((C + 3) / 4 * 4));
-    lc = lc / 64 * 64;
-    if (lc < 64) lc = 64;
-    return lc < n_rows ? lc : n_rows;
-}
-
-bool run_kmeans_assign(const uint16_t* E, const int32_t* rows, int64_t n_rows, const uint16_t* M, int64_t C,
-                       int64_t H, int32_t* a, float* smax, uint16_t* gather, float* scores, void* blas_ws,
-                       size_t blas_ws_bytes, hipStream_t s)
-{
-    rocblas_handle bh = blas_handle(s, blas_ws, blas_ws_bytes);
-    if (!bh) return false;
-    const uint16_t* X = E;
-    if (rows) {
-        hipLaunchKernelGGL(k_gather_rows, dim3(grid_for(n_rows * (H / 8), 256)), dim3(256), 0, s, E, rows, n_rows, H,
-                           gather);
-        X = gather;
-    }
-    const int64_t lc = kmeans_chunk_rows(n_rows, C);
-    const int64_t ldS = (C + 3) / 4 * 4;          // 16-byte aligned score rows
-    for (int64_t r0 = 0; r0 < n_rows; r0 += lc) {
-        const int64_t nr = (r0 + lc <= n_rows) ? lc : n_rows - r0;
-        // scores (nr x C, row stride ldS) = X[r0 .. r0 + nr) M^T
-        if (gemm_rm(bh, false, true, nr, C, H, X + r0 * H, H, M, H, 0.f, scores, ldS) != rocblas_status_success)
-            return false;
-        hipLaunchKernelGGL(k_row_argmax, dim3((unsigned)nr), dim3(256), 0, s, scores, nr, C, ldS, a + r0,
-                           smax ? smax + r0 : nullptr);
-    }
-    return true;
-}
 
 void run_kmeans_init(const uint16_t* E, const int32_t* init, int64_t C, int64_t H, float* Mc, uint16_t* Mb,
                      int32_t* v, hipStream_t s)

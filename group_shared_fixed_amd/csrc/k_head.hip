@@ -515,10 +515,17 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
               bool accumulate_dh, uint16_t* dzcat, uint16_t* hcat, float* dhcat, uint16_t* hT, void* blas_ws,
               size_t blas_ws_bytes, hipStream_t stream)
 {
-    rocblas_handle bh = blas_handle(stream, blas_ws, blas_ws_bytes);
-    if (!bh) return false;
     const int64_t Bp = (B + 31) / 32 * 32;
+    const bool own_z = B <= 128 && H % kHzStage == 0 && L % 8 == 0;
     const bool own_dw = L % 8 == 0 && H % 4 == 0 && Bp <= 128;
+    const bool own_dh = L % 8 == 0 && H % 8 == 0;
+    // the rocBLAS handle (per thread and device, kept for the process) is
+    // created only when some product is not one of libhaste's own kernels
+    rocblas_handle bh = nullptr;
+    if (!(own_z && own_dw && own_dh)) {
+        bh = blas_handle(stream, blas_ws, blas_ws_bytes);
+        if (!bh) return false;
+    }
     if (own_dw) {
         launch_transpose_h(h, hT, B, H, Bp, stream);
     } else {
@@ -526,7 +533,7 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
         if (hipMemcpyAsync(hcat, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
         if (hipMemcpyAsync(hcat + B * H, h, hbytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) return false;
     }
-    if (B <= 128 && H % kHzStage == 0 && L % 8 == 0) {
+    if (own_z) {
         // Z and the BCE gradient in one kernel (Z stored only when asked for)
         hipLaunchKernelGGL(k_head_zbce, dim3((unsigned)((L + kHzLabels - 1) / kHzLabels)), dim3(256), 0, stream, h,
                            W, rowptr, col, scale, want_z ? zbuf : nullptr, dzcat, dzcat + B * L, loss, B, H, L);
@@ -545,7 +552,7 @@ bool run_head(const uint16_t* h, const uint16_t* W, const int32_t* rowptr, const
         return false;
     }
     const int64_t m = B * H;
-    if (L % 8 == 0 && H % 8 == 0) {
+    if (own_dh) {
         // per label chunk c: (hi + lo)[:, chunk c] W[chunk c, :] (B x H) on libhaste's kernel
         const int64_t S = head_dh_mfma_chunks(B, H, L), Lc = head_dh_mfma_chunk_len(B, H, L);
         const dim3 grid((unsigned)S, (unsigned)((H + 255) / 256), (unsigned)((B + 127) / 128));

@@ -173,11 +173,17 @@ void group_sort_keys(const int32_t* seg, int64_t n, uint64_t* keys, hipStream_t 
 void run_label_emb_accumulate(const uint16_t* h, const int32_t* rowptr, const int32_t* col, int64_t nnz, int64_t B,
                               int64_t H, float* S, int32_t* counts, uint64_t* keys, int32_t* sample, hipStream_t s);
 void run_label_emb_finalize(const float* S, const int32_t* counts, int64_t L, int64_t H, uint16_t* E, hipStream_t s);
-// Rows per product chunk of the k-means assignment (scores chunk x C fp32).
-int64_t kmeans_chunk_rows(int64_t n_rows, int64_t C);
-bool run_kmeans_assign(const uint16_t* E, const int32_t* rows, int64_t n_rows, const uint16_t* M, int64_t C,
-                       int64_t H, int32_t* a, float* smax, uint16_t* gather, float* scores, void* blas_ws,
-                       size_t blas_ws_bytes, hipStream_t s);
+// k-means assignment (k_assign.hip): a[i] = the centre with the largest dot
+// product with E[rows ? rows[i] : i] (the lowest on ties), smax[i]
+// (nullable) that product.  Scratch: keys, n_rows 64-bit words; xpack,
+// n_rows x kmeans_assign_width(H) bf16, used when rows is given or the width
+// differs from H; mpack, C x that width, used when it differs.  One
+// workgroup per (256-label, 256-centre) tile: kmeans_assign_tiles of them.
+int64_t kmeans_assign_tiles(int64_t n_rows, int64_t C);
+int64_t kmeans_assign_width(int64_t H);
+void run_kmeans_assign(const uint16_t* E, const int32_t* rows, int64_t n_rows, const uint16_t* M, int64_t C,
+                       int64_t H, int32_t* a, float* smax, uint64_t* keys, uint16_t* xpack, uint16_t* mpack,
+                       hipStream_t s);
 void run_kmeans_init(const uint16_t* E, const int32_t* init, int64_t C, int64_t H, float* Mc, uint16_t* Mb,
                      int32_t* v, hipStream_t s);
 void run_kmeans_update(const uint16_t* E, const int32_t* batch, const int32_t* a_batch, int64_t n, int64_t C,

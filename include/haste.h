@@ -25,7 +25,13 @@
  *   - All pointers except `workspace` arguments of size 0 and the optional
  *     outputs marked "nullable" are device pointers the caller allocated; the
  *     library never allocates or frees them, keeps no pointer after the call
- *     returns and keeps no state between calls.
+ *     returns and keeps no state between calls.  Two exceptions, both
+ *     process-lifetime and never freed: haste_step_noalloc's static scratch
+ *     array (below), and the rocBLAS handle (one per host thread and device,
+ *     created on first use; rocBLAS allocates inside it) that haste_head_step
+ *     and the joint step create only for head shapes outside their own
+ *     kernels (B > 128, H % 64 != 0 or L_head % 8 != 0).  No other call
+ *     touches rocBLAS.
  *   - Calls are asynchronous on `stream` (0 = default stream) and return
  *     before the GPU work finishes; outputs are valid after the stream
  *     synchronises.  Outputs are overwritten, never accumulated into.
@@ -296,9 +302,15 @@ int haste_step_w8_timed(const haste_bf16* h, const int32_t* idx, const uint8_t* 
  *
  * haste_kmeans_assign: assign[i] = argmax_c <E_r, M_c> (lowest c on ties)
  * for r = rows[i] (rows NULL: r = i, n_rows = L); score (nullable) gets
- * the maximum.  M: C x H bf16.  The products run on rocBLAS in label
- * chunks (fp32 accumulate), the arg-max is a libhaste kernel.  Workspace:
- * haste_kmeans_assign_workspace_size(n_rows, C, H, rows != NULL).
+ * the maximum.  M: C x H bf16; rows[] must hold ids in [0, L).  One
+ * fused matrix-core kernel computes the products (fp32 accumulate) tile by
+ * tile and keeps only each label's best (score, centre), so no score
+ * matrix is stored.  The number of 256 x 256 (label, centre) tiles must not
+ * exceed 2^31 (HASTE_ERR_UNSUPPORTED).  Workspace:
+ * haste_kmeans_assign_workspace_size(n_rows, C, H, rows != NULL): 8 bytes
+ * per row, plus, with Hp = H rounded up to 128, the gathered rows (n_rows x
+ * Hp bf16) when rows is given or Hp != H, and the centres (C x Hp bf16) when
+ * Hp != H.
  * haste_kmeans_init: centre c starts as E[init[c]]: Mc (C x H fp32), Mb
  * (its bf16 copy, the operand of the assignment) and counts[c] = 0.
  * haste_kmeans_update: one mini-batch step (Sculley's update) for the n

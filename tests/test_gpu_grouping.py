@@ -72,7 +72,7 @@ def assert_greedy_valid(E, a, C, G, perm, clusters, eps):
     return near
 
 
-@pytest.mark.parametrize("L,C,H", [(3000, 37, 64), (513, 5, 8), (4096, 300, 128)])
+@pytest.mark.parametrize("L,C,H", [(3000, 37, 64), (513, 5, 8), (4096, 300, 128), (2600, 700, 200)])
 def test_kmeans_assign_integer_exact(L, C, H):
     E = _int_emb(L, H, 90 + C)
     M = _int_emb(C, H, 91 + C)
