@@ -39,9 +39,12 @@ namespace haste {
 
 // Wide variants (weight-gradient tiles of G x 128 or 64 x F) need more than
 // 256 registers per lane; they run one workgroup per CU with up to 512.
+// The fused G = 16, F = 128 step fits two waves per SIMD (256 registers,
+// under 80 KB of LDS) without prefetching the next group's weights, and
+// gains more from the second wave's latency hiding than it loses.
 constexpr int fwd_min_blocks(int G, int F, int mode)
 {
-    return ((mode == STEP_DW && (F == 128 || G == 64)) || (G == 64 && F == 128)) ? 1 : 2;
+    return ((mode == STEP_DW && ((F == 128 && G > 16) || G == 64)) || (G == 64 && F == 128)) ? 1 : 2;
 }
 
 // Offset (16-bit elements) of (slot f, batch row b) in a wave's gathered tile
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     constexpr int NDZ = (32 * G / 8 + 63) / 64;    // 16-byte dZ pieces per lane per chunk (BWD_W)
     // Prefetch the next group's weights only when they are small; wide tiles
     // would push the wave past 256 registers (two waves per SIMD).
-    constexpr bool PF_W = FWD && (GT * KS <= 4);
+    constexpr bool PF_W = FWD && (GT * KS <= 4) && !(MODE == STEP_DW && G == 16 && F == 128);
     // Four-chunk groups run as two chunk pairs where the registers for a
     // second set of inputs are there (see the chunk loop); with per-chunk
     // outputs the pair's two chunks are staged in two buffers.
@@ -91,9 +94,14 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     constexpr bool ALIAS_WZ = DW && !DEFER_DW && STORE_Z;
     constexpr int WO_SIZE = DW ? (ALIAS_WZ && 32 * ZST > DW_ROWS * WST ? 32 * ZST : DW_ROWS * WST) : 4;
 
+    // W_k passes through LDS once per group, before the group's first chunk
+    // is written to the gathered tile: for G <= 32 it fits in that tile.
+    constexpr bool W_IN_H = (G <= 32);
+    // label bits of one batch row: the group's G labels
+    using MaskT = typename pick<(G <= 16), uint16_t, typename pick<(G <= 32), uint32_t, uint64_t>::type>::type;
     __shared__ __attribute__((aligned(16))) uint16_t sH[4][32 * F];
-    __shared__ __attribute__((aligned(16))) uint16_t sWk[4][FWD ? G * F : 8];
-    __shared__ uint64_t sM[4][LABELS ? kMaxLabelBatch : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sWk[4][FWD && !W_IN_H ? G * F : 8];
+    __shared__ MaskT sM[4][LABELS ? kMaxLabelBatch : 1];
     __shared__ __attribute__((aligned(16))) uint16_t sD[4][MODE == BWD_W ? 32 * DST : 2];
     __shared__ __attribute__((aligned(16))) float sWo[4][WO_SIZE];
     __shared__ __attribute__((aligned(16))) float sZo[4][ZB][STORE_Z && !ALIAS_WZ ? 32 * ZST : 4];
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
         if constexpr (FWD) {
             // this group's weights: through LDS into the matrix-core B layout
             // of the forward product (lane (label 16gt + r16, q): slots 32s + 8q ..)
-            uint16_t* wk = sWk[wv];
+            uint16_t* wk = W_IN_H ? tile : sWk[wv];
             if constexpr (!PF_W) {
                 if (k != k0) load_w(k, wraw);
             }
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
             if (anypos) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    sM[wv][lane + 64 * s] = m[s];
+                    sM[wv][lane + 64 * s] = (MaskT)m[s];
                 wave_sync();
             }
         }
