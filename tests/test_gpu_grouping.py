@@ -72,7 +72,9 @@ def assert_greedy_valid(E, a, C, G, perm, clusters, eps):
     return near
 
 
-@pytest.mark.parametrize("L,C,H", [(3000, 37, 64), (513, 5, 8), (4096, 300, 128), (2600, 700, 200)])
+@pytest.mark.parametrize("L,C,H", [(3000, 37, 64), (513, 5, 8), (4096, 300, 128), (2600, 700, 200),
+                                   # one label and one centre; H at its maximum; five centre tiles
+                                   (1, 1, 8), (300, 2, 1024), (5000, 1200, 128)])
 def test_kmeans_assign_integer_exact(L, C, H):
     E = _int_emb(L, H, 90 + C)
     M = _int_emb(C, H, 91 + C)
@@ -81,7 +83,7 @@ def test_kmeans_assign_integer_exact(L, C, H):
     ra, rs = O.oracle_kmeans_assign(E, M)
     assert (to_host(a) == ra).all(), "assignments differ"
     assert (to_host(s).astype(np.float64) == rs).all(), "scores differ"
-    rows = np.sort(np.random.default_rng(C).choice(L, size=L // 3, replace=False)).astype(np.int32)
+    rows = np.sort(np.random.default_rng(C).choice(L, size=max(L // 3, 1), replace=False)).astype(np.int32)
     a2, _ = hs.kmeans_assign(to_dev_bf16(E), to_dev_bf16(M), rows=to_dev_i32(rows))
     assert (to_host(a2) == ra[rows]).all(), "assignments of a row subset differ"
 
