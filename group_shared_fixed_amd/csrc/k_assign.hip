@@ -10,10 +10,10 @@
 //
 // Layout: the label rows X (n x H bf16) and the centres M (C x H bf16) are
 // both contiguous along the contraction, so a 16-byte piece of a row is
-// directly one lane's operand of a 16x16x32 matrix-core product.  A
+// directly one lane's operand of a 32x32x16 matrix-core product.  A
 // workgroup of four waves scores one tile of 256 labels x 256 centres; each
-// wave owns a 128 x 128 quarter, held as 64 accumulator tiles (256 fp32 per
-// lane, in the accumulation registers).
+// wave owns a 128 x 128 quarter, held as 16 accumulator tiles of 32 x 32
+// (256 fp32 per lane, in the accumulation registers).
 //
 // The contraction runs in LDS stages of 32 through a ring of four stage
 // buffers (32 KB each: both operands' 256 rows x 64 bytes).  The operands
@@ -27,8 +27,8 @@
 // no branches (past the end it repeats the last stage's moves into buffers
 // nobody reads): the compiler then adds no waits of its own beyond these.
 // Staged rows are 64 bytes; their 16-byte pieces are XOR-swizzled with
-// (row / 4) % 4, so the 16 rows a lane group reads in one operand fetch fall
-// in distinct banks.  H must be a multiple of 128 (four stages per loop
+// (row / 4) % 4, so the 16 rows that 16 consecutive lanes read in one
+// operand fetch fall in distinct banks.  H must be a multiple of 128 (four stages per loop
 // turn); other widths are zero-padded into a copy first.
 //
 // Tiles are dealt so that the workgroups resident on one XCD (workgroup ids
@@ -52,12 +52,6 @@ constexpr int kAsTile = 256;       // labels and centres per workgroup tile
 constexpr int kAsStage = 32;       // contraction per LDS stage
 constexpr int kAsWidth = 128;      // the kernel's H granularity (four stages)
 constexpr int kAsGroupRows = 8;    // label tiles per dealing group
-// Row stride (in (score, centre) pairs) of the epilogue's partials: 32
-// used, padded to 272 bytes, an odd number of 16-byte units, so that the 16
-// rows that 16 consecutive threads read in one 16-byte fetch fall in
-// distinct banks (the writes then conflict at most two ways).
-constexpr int kAsPartStride = 34;
-
 // Order-preserving image of an fp32 score in 32 unsigned bits (-0 and +0
 // map to the same value, so equal scores compare equal).
 __device__ __forceinline__ uint32_t score_order(float s)
@@ -93,6 +87,17 @@ __device__ __forceinline__ void bare_barrier()
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 32x32x16 bf16 matrix-core product, fp32 accumulate.  Lane l supplies A
+// row (l % 32) and B column (l % 32), contraction elements 8 (l / 32) .. + 8;
+// the result lands as: lane l holds column (l % 32), element e at row
+// 8 (e / 4) + 4 (l / 32) + e % 4.
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
 
 // keys[i] (pre-zeroed) = max over centres c of assign_key(<X_i, M_c>, c), X:
 // n x H bf16, M: C x H bf16, H % 128 == 0.  Grid: one workgroup per (label
@@ -152,34 +157,51 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     };
 
-    f32x4_t acc[8][8];
+    // 32x32x16 products: per wave 4 x 4 result tiles of 32 x 32, 16 fp32 per
+    // lane each.  (With 8 x 8 tiles of the 16x16x32 product the compiler
+    // renamed most accumulator chains inside the loop and copied them back
+    // at its end, ~700 accumulator moves per four stages, 25 % of the
+    // kernel's time; these 16 chains stay in place.)
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = zero4();
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x16_t{};
 
-    // operand fetch: lane (q, r16) reads tile row 16 x + r16, logical piece
-    // q, stored as piece q ^ (row / 4) % 4 = q ^ (r16 / 4)
-    const int pc = 8 * (q ^ (r16 >> 2));
+    // operand fetch: lane (h, r32) reads tile row 32 x + r32, logical piece
+    // 2 s + h of the stage (s = the 16-deep step), stored as piece
+    // (2 s + h) ^ (row / 4) % 4 = (2 s + h) ^ (r32 / 4) % 4
+    const int r32 = lane & 31, h = lane >> 5, rsw = (r32 >> 2) & 3;
     auto products = [&](const uint16_t* buf) {
-        const uint16_t* tA = buf + (128 * wr + r16) * kAsStage + pc;
-        const uint16_t* tB = buf + kHalf + (128 * wc + r16) * kAsStage + pc;
-        // A one row tile ahead of its products; the scheduling barriers keep
-        // that order (left alone, the compiler reads each A fragment into one
-        // register and waits for it)
-        u32x4_t bf[8], af[2];
-        af[0] = *reinterpret_cast<const u32x4_t*>(tA);
+        const uint16_t* tA = buf + (128 * wr + r32) * kAsStage;
+        const uint16_t* tB = buf + kHalf + (128 * wc + r32) * kAsStage;
+        u32x4_t af[2][4], bf[2][4];
+        auto rd = [&](int st16) {
+            const int pc = 8 * ((2 * st16 + h) ^ rsw);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) bf[ct] = *reinterpret_cast<const u32x4_t*>(tB + 16 * ct * kAsStage);
-        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+            for (int ct = 0; ct < 4; ++ct)
+                bf[st16][ct] = *reinterpret_cast<const u32x4_t*>(tB + 32 * ct * kAsStage + pc);
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            if (rt + 1 < 8) af[(rt + 1) & 1] = *reinterpret_cast<const u32x4_t*>(tA + 16 * (rt + 1) * kAsStage);
+            for (int rt = 0; rt < 4; ++rt)
+                af[st16][rt] = *reinterpret_cast<const u32x4_t*>(tA + 32 * rt * kAsStage + pc);
+        };
+        // the second step's fragments are read while the first step's
+        // products run (the scheduling barriers keep that interleave)
+        rd(0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        rd(1);
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = mfma16(af[rt & 1], bf[ct], acc[rt][ct]);
-            if (rt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        for (int st16 = 0; st16 < 2; ++st16)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = mfma32(af[st16][rt], bf[st16][ct], acc[rt][ct]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     };
     // stage st: this wave's moves of st done (those of st + 1 and st + 2,
     // 16 instructions, may be in flight), barrier, moves of st + 3 into the
@@ -204,38 +226,41 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     wait_vm<0>();              // the repeated moves past the end, into buffers reused below
     bare_barrier();
 
-    // lane (q, r16) holds the scores of rows 16 rt + 4 q + i, centres
-    // 16 ct + r16 of the wave's quarter.  Each lane keeps, per row, its best
-    // over ct (centres rise with ct, so a strict comparison keeps the
-    // lowest; centres past C only occur in the last centre tile) and writes
-    // it to slot 16 wc + r16 of the row; then thread t reduces row t over
-    // its 32 slots: the largest score, then the lowest centre holding it.
-    // Row r's slots sit in buffer r / 64, local row r % 64.
+    // Lane (h, r32) holds, for result tile (rt, ct), element e: row
+    // 32 rt + 8 (e / 4) + 4 h + e % 4, centre 32 ct + r32 of the wave's
+    // quarter.  Each lane keeps, per row, its best over ct (centres rise with
+    // ct, so a strict comparison keeps the lowest; centres past C only occur
+    // in the last centre tile) and writes it to slot 32 wc + r32 of the row;
+    // then thread t reduces row t over its 64 slots: the largest score, then
+    // the lowest centre holding it.  Row r's slots sit in buffer r / 64 (the
+    // whole ring), 512 bytes per row, pair s at s ^ 2 (r % 16), so that 16
+    // consecutive threads' 16-byte reads fall in distinct banks.
     auto part_rows = [&](int quarter) {
         uint16_t* p = quarter == 0 ? ring0 : quarter == 1 ? ring1 : quarter == 2 ? ring2 : ring3;
         return reinterpret_cast<f32x2_t*>(p);
     };
-    const int64_t cw = col0 + 128 * wc + r16;
+    const int cw = (int)col0 + 128 * wc + r32;      // C < 2^30
+    const int slot = 32 * wc + r32;
     auto lane_best = [&](bool ragged) {
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            f32x2_t* const part = part_rows(2 * wr + (rt >> 2));
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x2_t* const part = part_rows(2 * wr + (rt >> 1));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float bv = acc[rt][0][i];
+            for (int e = 0; e < 16; ++e) {
+                float bv = acc[rt][0][e];
                 int bc = 0;
                 if (ragged && cw >= C) bv = -INFINITY;
 #pragma unroll
-                for (int ct = 1; ct < 8; ++ct) {
-                    float v = acc[rt][ct][i];
-                    if (ragged && cw + 16 * ct >= C) v = -INFINITY;
+                for (int ct = 1; ct < 4; ++ct) {
+                    float v = acc[rt][ct][e];
+                    if (ragged && cw + 32 * ct >= C) v = -INFINITY;
                     if (v > bv) {
                         bv = v;
                         bc = ct;
                     }
                 }
-                const int lrow = (16 * rt + 4 * q + i) & 63;
-                part[lrow * kAsPartStride + 16 * wc + r16] = f32x2_t{bv, __int_as_float((int)cw + 16 * bc)};
+                const int lr = 32 * (rt & 1) + 8 * (e >> 2) + 4 * h + (e & 3);   // row within its buffer
+                part[lr * 64 + (slot ^ (2 * (lr & 15)))] = f32x2_t{bv, __int_as_float(cw + 32 * bc)};
             }
         }
     };
@@ -246,19 +271,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __syncthreads();
     const int64_t r = row0 + tid;
     if (r < n) {
-        const f32x4_t* pr = reinterpret_cast<const f32x4_t*>(part_rows(w) + (tid & 63) * kAsPartStride);
-        f32x4_t pv[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) pv[u] = pr[u];
+        const int lr = tid & 63;
+        const f32x2_t* pr = part_rows(w) + lr * 64;
+        // a running best over the 64 (score, centre) slots: the larger score,
+        // the lower centre on equal scores
         float m = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) m = fmaxf(m, fmaxf(pv[u][0], pv[u][2]));
         int bc = 0x7fffffff;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int c0 = pv[u][0] == m ? __float_as_int(pv[u][1]) : 0x7fffffff;
-            const int c1 = pv[u][2] == m ? __float_as_int(pv[u][3]) : 0x7fffffff;
-            bc = min(bc, min(c0, c1));
+        for (int u = 0; u < 32; ++u) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(pr + 2 * (u ^ (lr & 15)));
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                const float sv = v[e];
+                const int cv = __float_as_int(v[e + 1]);
+                const bool better = sv > m || (sv == m && cv < bc);
+                m = better ? sv : m;
+                bc = better ? cv : bc;
+            }
         }
         atomicMax(keys + r, assign_key(m, bc));
     }
