@@ -450,3 +450,42 @@ def oracle_label_emb(batches, L, H):
     for h, rp, col in batches:
         oracle_label_emb_accumulate(S, n, h, rp, col)
     return oracle_label_emb_finalize(S, n), S, n
+
+
+# ------------------------------------------------------------------ slot order
+#
+# HASTE notes, "group-shared fixed fan-in": a group is defined by its index
+# set I_k.  The slot f at which a column sits carries no meaning as long as
+# column f of W_k moves with it, since every product of the layer sums over
+# the slots.  The library can therefore store each group's slots in an order
+# chosen for its feature-gradient accumulator.  That accumulator keeps the
+# rows of feature column j in bank group (j >> 1) mod 8, and one of its
+# read-add-write instructions covers a run of 8 consecutive slots, so the
+# columns of a run should have distinct keys (j >> 1) mod 8.  The order,
+# group by group (F a multiple of 8, R = F / 8 runs):
+#   1. sort the F slots by key, equal keys in slot order;
+#   2. deal the sorted slots over the runs in turn: the p-th slot of the
+#      sorted list becomes new slot 8 (p mod R) + (p div R).
+# A key held by at most R slots then lands in distinct runs.
+
+def oracle_order_slots(idx, W=None, G=None):
+    """(idx_new, W_new, perm) with perm[k, s] the old slot of new slot s:
+    idx_new[k, s] = idx[k, perm[k, s]] and, when W (L x F bf16 bits, L = K G)
+    is given, W_new[k G + g, s] = W[k G + g, perm[k, s]] (else W_new is None)."""
+    idx = np.asarray(idx)
+    K, F = idx.shape
+    if F % 8 != 0:
+        raise ValueError("F must be a multiple of 8")
+    R = F // 8
+    perm = np.empty((K, F), dtype=np.int32)
+    for k in range(K):
+        keys = [(int(idx[k, f]) >> 1) & 7 for f in range(F)]
+        order = sorted(range(F), key=lambda f: (keys[f], f))
+        for p, f in enumerate(order):
+            perm[k, 8 * (p % R) + p // R] = f
+    idx_new = np.take_along_axis(idx, perm, axis=1).astype(np.int32)
+    W_new = None
+    if W is not None:
+        _check("W", W, np.uint16, (K * G, F))
+        W_new = np.take_along_axis(W, np.repeat(perm, G, axis=0), axis=1)
+    return idx_new, W_new, perm

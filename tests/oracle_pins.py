@@ -34,6 +34,10 @@ What pins what:
   k-means update                Sculley's per-sample rule (loops) == the closed form; full-batch
                                 steps from zero counts never lower the objective (Lloyd)
   greedy grouping               planted clumps recovered exactly; partition and leftover rules
+  slot order                    hand-worked rows (tests/golden); every row a permutation with W's
+                                columns moved along; repeated keys per run == the lower bound
+                                sum_v max(0, count_v - F/8), which brute force over all splits of
+                                16 slots into two runs confirms is the least possible
 """
 
 from __future__ import annotations
@@ -761,6 +765,48 @@ def pin_label_emb_invariances(lib):
     assert r.tolist() == [0x3F80, 0x3F82, 0xBF80, 0x0000], [hex(x) for x in r]
 
 
+def _run_repeats(row, F):
+    """Slots of each run of 8 whose bank key (j >> 1) mod 8 repeats an earlier
+    slot of the same run, summed over the runs."""
+    keys = [(int(j) >> 1) & 7 for j in row]
+    return sum(8 - len(set(keys[r:r + 8])) for r in range(0, F, 8))
+
+
+def pin_slot_order_hand_examples(lib):
+    with open(os.path.join(GOLDEN, "slot_order_hand_examples.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        idx = np.array([c["idx"]], np.int32)
+        idx_new, _, perm = O.oracle_order_slots(idx)
+        assert list(perm[0]) == c["perm"], f"slot order perm {list(perm[0])} vs {c['perm']}"
+        assert list(idx_new[0]) == c["idx_new"], f"slot order idx {list(idx_new[0])} vs {c['idx_new']}"
+
+
+def pin_slot_order_properties(lib):
+    rng = np.random.default_rng(21)
+    for F, H, G in ((16, 40, 3), (32, 256, 2), (64, 768, 4), (128, 768, 2), (128, 1024, 1)):
+        K = 40
+        idx = sorted_subsets(K, F, H, 9, F)
+        W = rng.integers(0, 1 << 16, size=(K * G, F), dtype=np.uint16)
+        idx_new, W_new, perm = O.oracle_order_slots(idx, W, G)
+        for k in range(K):
+            assert sorted(perm[k]) == list(range(F)), "slot order: not a permutation"
+            assert (idx_new[k] == idx[k][perm[k]]).all(), "slot order: index row not permuted by perm"
+            for g in range(G):
+                assert (W_new[k * G + g] == W[k * G + g][perm[k]]).all(), "slot order: W column left behind"
+            counts = np.bincount((idx[k] >> 1) & 7, minlength=8)
+            bound = int(np.maximum(counts - F // 8, 0).sum())
+            assert _run_repeats(idx_new[k], F) == bound, f"slot order F={F} k={k}: repeats above the bound"
+    # brute force: no split of 16 slots into two runs of 8 repeats fewer keys
+    import itertools
+    for seed in range(6):
+        row = sorted_subsets(1, 16, 48, 30 + seed, 16)[0]
+        best = min(_run_repeats([row[i] for i in a] + [row[i] for i in range(16) if i not in a], 16)
+                   for a in itertools.combinations(range(16), 8) if 0 in a)
+        idx_new, _, _ = O.oracle_order_slots(row[None, :])
+        assert _run_repeats(idx_new[0], 16) == best, f"slot order brute force seed {seed}"
+
+
 ALL_PINS = [
     pin_hand_example,
     pin_bce_hand_example,
@@ -788,4 +834,6 @@ ALL_PINS = [
     pin_label_emb_hand_example,
     pin_label_emb_dense_product,
     pin_label_emb_invariances,
+    pin_slot_order_hand_examples,
+    pin_slot_order_properties,
 ]

@@ -116,6 +116,13 @@ PY_MUTANTS = {
     "emb_entry_as_sample": ("            S[col[p]] += hf[b]", "            S[col[p]] += hf[p % hf.shape[0]]"),
     "emb_round_up": ("    q = np.rint(np.ldexp(m, 8))", "    q = np.ceil(np.ldexp(m, 8))"),
     "emb_zero_rows_kept": ("    ok = (np.asarray(n) > 0) & (norm > 0)", "    ok = norm >= 0"),
+    "slot_order_no_deal": ("            perm[k, 8 * (p % R) + p // R] = f", "            perm[k, p] = f"),
+    "slot_order_low_bits": ("        keys = [(int(idx[k, f]) >> 1) & 7 for f in range(F)]",
+                            "        keys = [int(idx[k, f]) & 7 for f in range(F)]"),
+    "slot_order_ties_reversed": ("key=lambda f: (keys[f], f))", "key=lambda f: (keys[f], -f))"),
+    "slot_order_inverse_perm": ("            perm[k, 8 * (p % R) + p // R] = f", "            perm[k, f] = 8 * (p % R) + p // R"),
+    "slot_order_weights_stay": ("        W_new = np.take_along_axis(W, np.repeat(perm, G, axis=0), axis=1)",
+                                "        W_new = W.copy()"),
     "rewire_grown_keep_old_weight": (
         "            if c in kept:\n                W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept[c]]",
         "            W_new[k * G:(k + 1) * G, f_new] = W[k * G:(k + 1) * G, kept.get(c, f_new)]"),
@@ -142,7 +149,7 @@ def test_head_mutant_is_caught(name, monkeypatch):
         for fn in ("oracle_rewire_scores", "oracle_rewire_select", "oracle_rewire", "e4m3_decode", "e4m3_encode",
                    "w8_group_exponent", "oracle_quantize_w8", "oracle_dequantize_w8", "oracle_kmeans_assign",
                    "oracle_kmeans_update", "oracle_group_greedy", "oracle_label_emb_accumulate",
-                   "f64_to_bf16_bits", "oracle_label_emb_finalize", "oracle_label_emb"):
+                   "f64_to_bf16_bits", "oracle_label_emb_finalize", "oracle_label_emb", "oracle_order_slots"):
             monkeypatch.setattr(O, fn, getattr(mod, fn))
         failed = _pins_fail(lib)
     assert failed, f"mutant {name} passes every pin"
