@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     kmeans_assign,
     kmeans_init,
     kmeans_update,
+    order_slots,
     label_emb_accumulate,
     label_emb_finalize,
     rewire,

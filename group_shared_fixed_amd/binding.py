@@ -62,6 +62,7 @@ SIGNATURES = {
     "haste_rewire_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "haste_rewire": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_rewire_timed": (_M, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P, _P]),
+    "haste_order_slots": (_M, [_P, _P, _P, _I, _I, _I, _P]),
     "haste_validate_idx": (_M, [_P, _I, _I, _I, _P, _P]),
     "haste_validate_labels": (_M, [_P, _P, _I, _I, _P, _P]),
     "haste_workspace_status": (_M, [_P, _P, _P]),
@@ -601,8 +602,25 @@ def rewire(h, dZ, idx, W, G, n_swap, idx_out=None, W_out=None, want_scores=False
     return {"idx": idx_out, "W": W_out, "grow": grow, "prune": prune}
 
 
+def order_slots(idx, W=None, G=None, perm=False, stream=None):
+    """Bank-balanced slot order of every group, in place on idx (K x F int32)
+    and, if given, the columns of W (K G x F bf16).  Returns the K x F uint8
+    tensor perm (perm[k, s] = old slot now at s) when perm is True, else None."""
+    torch = _torch()
+    _i32(idx)
+    K, F = idx.shape
+    if W is not None:
+        _bits(W)
+        if G is None or W.shape != (K * G, F):
+            raise ValueError("W must be K*G x F with G given")
+    Gv = G if G is not None else 32
+    p = torch.empty(K, F, dtype=torch.uint8, device=idx.device) if perm else None
+    _check("haste_order_slots", lib().haste_order_slots(_ptr(idx), _ptr(W), _ptr(p), K, Gv, F, _stream(idx, stream)))
+    return p
+
+
 def validate_idx(idx, H, stream=None) -> int:
-    """Number of index rows with an entry outside [0, H) or not increasing."""
+    """Number of index rows with an entry outside [0, H) or an entry twice."""
     torch = _torch()
     _i32(idx)
     bad = torch.empty(4, dtype=torch.int32, device=idx.device)

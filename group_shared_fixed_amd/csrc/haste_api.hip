@@ -509,6 +509,19 @@ int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, i
     return hip_status();
 }
 
+int haste_order_slots(int32_t* idx, haste_bf16* W, uint8_t* perm, int64_t K, int64_t G, int64_t F,
+                      hipStream_t stream)
+{
+    if (!idx) return HASTE_ERR_NULL;
+    if (K < 1 || G < 1 || F < 1) return HASTE_ERR_DIM;
+    if (G != 16 && G != 32 && G != 64) return HASTE_ERR_UNSUPPORTED;
+    if (F != 32 && F != 64 && F != 128) return HASTE_ERR_UNSUPPORTED;
+    if (K > kMaxLabels / G) return HASTE_ERR_UNSUPPORTED;
+    if (!aligned16(idx) || (W && !aligned16(W))) return HASTE_ERR_ALIGN;
+    launch_order_slots(idx, reinterpret_cast<uint16_t*>(W), perm, K, (int)G, (int)F, stream);
+    return hip_status();
+}
+
 int haste_validate_labels(const int32_t* y_rowptr, const int32_t* y_col, int64_t B, int64_t L, int32_t* bad,
                           hipStream_t stream)
 {

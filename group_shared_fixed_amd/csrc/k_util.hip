@@ -70,20 +70,25 @@ __global__ __launch_bounds__(256) void k_fill_zero_f32_i32(float* __restrict__ p
     if (zi && blockIdx.x == 0 && threadIdx.x == 0) *zi = 0;
 }
 
-// One thread per row: entries in [0, H) and strictly increasing.
+// One wave per row: entries in [0, H) and pairwise distinct.  The slots of a
+// row may come in any order (a group is defined by its index set); each lane
+// checks its own entries against every earlier entry of the row.
 __global__ __launch_bounds__(256) void k_validate_idx(const int32_t* __restrict__ idx, int64_t rows, int64_t F,
                                                       int64_t H, int32_t* bad)
 {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= rows) return;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;                   // whole wave
+    const int32_t* row = idx + r * F;
     bool ok = true;
-    int32_t prev = -1;
-    for (int64_t f = 0; f < F; ++f) {
-        const int32_t v = idx[r * F + f];
-        ok = ok && v > prev && v < H;
-        prev = v;
+    for (int64_t f0 = 0; f0 < F; f0 += 64) {
+        const int64_t f = f0 + lane;
+        const int32_t v = f < F ? row[f] : 0;
+        ok = ok && (f >= F || (v >= 0 && v < H));
+        for (int64_t e = 0; e < f0 + 64 && e < F; ++e)
+            ok = ok && !(e < f && f < F && row[e] == v);
     }
-    if (!ok) atomicAdd(bad, 1);
+    if (__any(!ok) && lane == 0) atomicAdd(bad, 1);
 }
 
 // One thread per sample: rowptr non-decreasing, ids in [0, L), strictly increasing.
@@ -153,8 +158,7 @@ void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s)
 
 void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_validate_idx, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, idx, rows, F, H,
-                       bad);
+    hipLaunchKernelGGL(k_validate_idx, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, idx, rows, F, H, bad);
 }
 
 void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B, int64_t L, int32_t* bad,
@@ -162,6 +166,89 @@ void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B
 {
     hipLaunchKernelGGL(k_validate_labels, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, rowptr, col, B, L,
                        bad);
+}
+
+
+// Bank-balanced slot order of each group (the layer's results do not depend
+// on the order of a group's slots as long as W_k's columns move with them).
+// The feature-gradient accumulator keeps feature column j's rows in bank group
+// (j >> 1) mod 8 and one read-add-write instruction covers a run of 8
+// consecutive slots.  Per group: sort the F slots by that key, equal keys in
+// slot order, and deal the sorted slots over the R = F / 8 runs in turn (the
+// p-th one becomes slot 8 (p mod R) + p div R).
+//
+// One wave per group; lane owns slots lane + 64 i.  A slot's place p in the
+// sorted list is the number of slots with a smaller key plus the number of
+// earlier slots with its key, counted from one ballot per key value.  The
+// wave reads its whole index row and each weight row before writing it, so
+// the permutation runs in place.
+template <int FPL>
+__global__ __launch_bounds__(256) void k_order_slots(int32_t* idx, uint16_t* W, uint8_t* perm, int64_t K, int G,
+                                                     int F)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (k >= K) return;                      // whole wave
+    const int R = F >> 3;
+    int col[FPL], key[FPL], dst[FPL];
+    uint64_t m[FPL][8];
+#pragma unroll
+    for (int i = 0; i < FPL; ++i) {
+        const int f = lane + 64 * i;
+        col[i] = f < F ? idx[k * F + f] : 0;
+        key[i] = f < F ? (col[i] >> 1) & 7 : 8;      // 8: no slot
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+            m[i][v] = __ballot(key[i] == v);
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < FPL; ++i) {
+        int p = 0;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            int all = 0, before = 0;
+#pragma unroll
+            for (int j = 0; j < FPL; ++j) {
+                all += __popcll(m[j][v]);
+                before += j < i ? __popcll(m[j][v]) : (j == i ? __popcll(m[j][v] & below) : 0);
+            }
+            p += v < key[i] ? all : (v == key[i] ? before : 0);
+        }
+        dst[i] = 8 * (p % R) + p / R;
+    }
+#pragma unroll
+    for (int i = 0; i < FPL; ++i) {
+        if (lane + 64 * i < F) {
+            idx[k * F + dst[i]] = col[i];
+            if (perm) perm[k * F + dst[i]] = (uint8_t)(lane + 64 * i);
+        }
+    }
+    if (!W) return;
+    // weight rows, eight at a time: all loads of a row precede its stores
+    uint16_t* Wk = W + k * G * F;
+    for (int g0 = 0; g0 < G; g0 += 8) {
+        uint16_t v[8][FPL];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int i = 0; i < FPL; ++i) {
+                const int f = lane + 64 * i;
+                v[r][i] = (g0 + r < G && f < F) ? Wk[(int64_t)(g0 + r) * F + f] : (uint16_t)0;
+            }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int i = 0; i < FPL; ++i)
+                if (g0 + r < G && lane + 64 * i < F) Wk[(int64_t)(g0 + r) * F + dst[i]] = v[r][i];
+    }
+}
+
+void launch_order_slots(int32_t* idx, uint16_t* W, uint8_t* perm, int64_t K, int G, int F, hipStream_t s)
+{
+    const dim3 grid((unsigned)((K + 3) / 4));
+    if (F <= 64) hipLaunchKernelGGL(k_order_slots<1>, grid, dim3(256), 0, s, idx, W, perm, K, G, F);
+    else hipLaunchKernelGGL(k_order_slots<2>, grid, dim3(256), 0, s, idx, W, perm, K, G, F);
 }
 
 }  // namespace haste

@@ -116,6 +116,8 @@ void launch_fill_f64(double* p, int64_t n, hipStream_t s);
 void launch_f64_to_f32(const double* src, float* dst, hipStream_t s);
 void launch_fill_i32(int32_t* p, int64_t n, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad, hipStream_t s);
+// Bank-balanced slot order of each group's index row and W_k's columns, in place (F <= 128).
+void launch_order_slots(int32_t* idx, uint16_t* W, uint8_t* perm, int64_t K, int G, int F, hipStream_t s);
 void launch_validate_labels(const int32_t* rowptr, const int32_t* col, int64_t B, int64_t L, int32_t* bad,
                             hipStream_t s);
 // Dense head pass (head-tail split): Z = h W^T (into zbuf when want_z; the

@@ -10,7 +10,8 @@
  *
  * Shapes and layouts (all row-major, contiguous):
  *   h    B x H  bf16   features (the encoder output feeding the layer)
- *   idx  K x F  int32  I_k = idx[k, :], entries in [0, H), strictly increasing
+ *   idx  K x F  int32  I_k = idx[k, :], entries in [0, H), pairwise distinct, in any
+ *                      order (haste_order_slots picks one that suits dh)
  *   W    L x F  bf16   W[l, f] multiplies h[:, idx[l / G, f]]
  *   Z    B x L  fp32   logits
  *   dZ   B x L  bf16   upstream gradient of the logits
@@ -39,7 +40,7 @@
  *     haste_status is returned without touching the GPU.  HASTE_ERR_HIP
  *     means a launch failed (hipGetLastError).  Faults inside kernels surface
  *     at the next synchronisation.  The hot calls do not re-validate index
- *     sets or labels: out-of-range or unsorted entries are undefined behaviour
+ *     sets or labels: out-of-range or repeated entries are undefined behaviour
  *     (use haste_validate_idx / haste_validate_labels).
  *   - Supported: G in {16, 32, 64} (G = 1 for the haste_fixed_* baseline),
  *     F in {32, 64, 128}, F <= H <= 1024, L = K*G < 2^31 - 64; label-consuming
@@ -397,8 +398,32 @@ int haste_rewire_timed(const haste_bf16* h, const haste_bf16* dZ, const int32_t*
                        int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, void* workspace,
                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
+/* Bank-balanced slot order, in place.  A group is its index set I_k ("group-
+ * shared fixed fan-in" section): the slot at which a column sits does not
+ * change any result of the layer as long as column f of W_k moves with it.
+ * This call reorders every group's slots for the feature-gradient kernels,
+ * whose accumulator holds feature column j's rows in bank group
+ * (j >> 1) mod 8 and whose read-add-write instructions each cover a run of 8
+ * consecutive slots: per group, the F slots are sorted by that key (equal
+ * keys keep their order) and dealt over the F / 8 runs in turn, the p-th
+ * sorted slot becoming slot 8 (p mod F/8) + p div F/8.  A key held by at most
+ * F / 8 slots of a group then falls in distinct runs (fewer bank conflicts in
+ * dh); nothing else depends on the order.
+ *   idx   K x F int32, permuted in place (device).
+ *   W     L x F bf16 (L = K G), its columns permuted with idx, in place;
+ *         NULL to reorder idx alone (e.g. before W is initialised).
+ *   perm  K x F uint8 output, perm[k, s] = the old slot now at slot s; NULL
+ *         to skip.  Apply it to any other per-slot state the caller keeps
+ *         (optimizer moments, FP8 weight codes).
+ * Rewiring (haste_rewire) writes sorted rows; order them again afterwards.
+ * G in {16, 32, 64}, F in {32, 64, 128}; pointers 16-byte aligned.
+ * Asynchronous on `stream`. */
+int haste_order_slots(int32_t* idx, haste_bf16* W, uint8_t* perm, int64_t K, int64_t G, int64_t F,
+                      hipStream_t stream);
+
 /* Count (into *bad, a device int32 the call zeroes first) the index rows
- * that have an entry outside [0, H) or are not strictly increasing. */
+ * that have an entry outside [0, H) or an entry twice (the order of a row's
+ * entries is free). */
 int haste_validate_idx(const int32_t* idx, int64_t rows, int64_t F, int64_t H, int32_t* bad,
                        hipStream_t stream);
 

@@ -182,6 +182,18 @@ def test_fixed_rejects(L):
     assert L.haste_fixed_bwd_h(A, A, A, A, 128, 768, 1000, 64, 1, None, 0, None) == WS
 
 
+def test_order_slots_rejects(L):
+    assert L.haste_order_slots(None, A, A, 10, 32, 64, None) == NULL
+    assert L.haste_order_slots(A, A, A, 0, 32, 64, None) == DIM
+    assert L.haste_order_slots(A, A, A, 10, 0, 64, None) == DIM
+    assert L.haste_order_slots(A, A, A, 10, 8, 64, None) == UNSUP
+    assert L.haste_order_slots(A, A, A, 10, 32, 48, None) == UNSUP
+    assert L.haste_order_slots(A, A, A, 10, 32, 256, None) == UNSUP
+    assert L.haste_order_slots(A, A, A, (2**31) // 32, 32, 64, None) == UNSUP
+    assert L.haste_order_slots(MIS, A, A, 10, 32, 64, None) == ALIGN
+    assert L.haste_order_slots(A, MIS, None, 10, 32, 64, None) == ALIGN
+
+
 def test_validate_rejects(L):
     assert L.haste_validate_idx(None, 10, 64, 768, A, None) == NULL
     assert L.haste_validate_idx(A, 0, 64, 768, A, None) == DIM

@@ -293,9 +293,17 @@ def test_validators():
     assert hs.validate_idx(to_dev_i32(idxn), H) == 0
     bad = idxn.copy()
     bad[3, 4] = H          # out of range
-    bad[10, 0], bad[10, 1] = bad[10, 1], bad[10, 0]   # unsorted
+    bad[10, 0], bad[10, 1] = bad[10, 1], bad[10, 0]   # unsorted: a valid set
     bad[20, 6] = bad[20, 5]                            # duplicate
+    bad[30, 7] = -1                                    # negative
     assert hs.validate_idx(to_dev_i32(bad), H) == 3
+    # F = 128 (two passes of a wave): a repeat across the passes, a shuffled row
+    idx2 = sorted_subsets(9, 128, 768, 6, 0)
+    idx2[4] = idx2[4][np.random.default_rng(3).permutation(128)]
+    assert hs.validate_idx(to_dev_i32(idx2), 768) == 0
+    idx2[2, 127] = idx2[2, 3]
+    idx2[7, 64] = idx2[7, 63]
+    assert hs.validate_idx(to_dev_i32(idx2), 768) == 2
     rp = np.array([0, 2, 2, 5], np.int32)
     col = np.array([1, 9, 0, 4, 7], np.int32)
     assert hs.validate_labels(to_dev_i32(rp), to_dev_i32(col), 10) == 0
