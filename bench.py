@@ -170,6 +170,19 @@ def i32_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
 
+def prepare_slots(hs, idx, W, G, args):
+    """Puts each group's slots in the bank-balanced order (haste_order_slots,
+    in place on idx and W's columns) unless --sorted-slots is given; the index
+    sets themselves are unchanged.  Runs once, before any timing.  Returns the
+    order's name for the JSON config."""
+    if getattr(args, "sorted_slots", False):
+        return "sorted (as drawn)"
+    hs.order_slots(idx, W, G)
+    import torch
+    torch.cuda.synchronize()
+    return "bank-balanced (haste_order_slots, applied once before timing)"
+
+
 def time_call(fn, reps, stream_handle, ev):
     """Average ms of fn() over reps, from events on the call's stream."""
     fn()
@@ -394,6 +407,7 @@ def sweep_g(args):
                                                                    workspace=ws), reps, sh, ev)
         else:
             idx = i32_dev(d["idx"], dev)
+            r["slot_order"] = prepare_slots(hs, idx, W, G, args)
             ws = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, "det")), dtype=torch.uint8,
                              device=dev)
             o = {"dW": dW, "dh": dh, "Z": None, "loss": None}
@@ -442,6 +456,7 @@ def joint_bench(args):
                       bf16_dev(d["W_head"], dev))
     yt = (i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev))
     yh = (i32_dev(d["yh_rowptr"], dev), i32_dev(d["yh_col"], dev))
+    slot_order = prepare_slots(hs, idx, Wt, G, args)
     s = 1.0 / B
     out = {"dW_tail": torch.empty(L, F, dtype=torch.float32, device=dev),
            "dW_head": torch.empty(Lh, H, dtype=torch.float32, device=dev),
@@ -489,7 +504,7 @@ def joint_bench(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "ht3m_joint_shaped", "L_head": Lh, "L_tail": L, "G": G, "K": K, "F": F, "H": H,
-                   "B": B, "positives_per_sample": w.m, "dh_mode": args.mode,
+                   "B": B, "positives_per_sample": w.m, "dh_mode": args.mode, "slot_order": slot_order,
                    "step": "haste_joint_step: tail haste_step, then the dense head (logits + BCE, dW and dh kernels)"},
         "useful_tflops": round((head_flops + tail_flops) / (ms_step * 1e-3) / 1e12, 2),
         "branches_us": {"tail_step": round(tail_us, 2), "head_step": round(head_us, 2)},
@@ -537,6 +552,7 @@ def w8_bench(args):
     d = make_inputs(w, dZ=False)
     h, idx, W = bf16_dev(d["h"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev)
     rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+    slot_order = prepare_slots(hs, idx, W, G, args)
     W8, wexp = hs.quantize_w8(W, G)
     # the bf16 weights the FP8 step computes with, for the side-by-side step
     Wq = torch.empty_like(W)
@@ -589,6 +605,7 @@ def w8_bench(args):
         "warmup": args.warmup, "ms_per_step": round(ms8, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 compute, fp8 e4m3 weights", "data": "synthetic",
         "config": {"workload": w.name, "L": L, "G": G, "K": K, "F": F, "H": H, "B": B, "dh_mode": args.mode,
+                   "slot_order": slot_order,
                    "step": "haste_step_w8: fused forward + BCE + dW + dh from E4M3 weights with group exponents"},
         "kernels_us": ph8,
         "bf16_step": {"ms_per_step": round(ms16, 4), "samples_per_s": round(B / (ms16 * 1e-3), 1),
@@ -852,6 +869,8 @@ def main():
     ap.add_argument("--grouping", action="store_true",
                     help="semantic label grouping (k-means + greedy groups) at 3M labels, one JSON line")
     ap.add_argument("--km-iters", type=int, default=20, help="with --grouping: mini-batch k-means steps")
+    ap.add_argument("--sorted-slots", action="store_true",
+                    help="keep each group's slots in the drawn (sorted) order instead of the bank-balanced order")
     ap.add_argument("--w8", action="store_true",
                     help="the fused step with FP8 (E4M3) weights next to the bf16 step, one JSON line")
     args = ap.parse_args()
@@ -892,6 +911,7 @@ def main():
 
     h, idx, W = bf16_dev(d["h"], dev), i32_dev(d["idx"], dev), bf16_dev(d["W"], dev)
     rp, col = i32_dev(d["y_rowptr"], dev), i32_dev(d["y_col"], dev)
+    slot_order = prepare_slots(hs, idx, W, G, args)
     s = 1.0 / B
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -983,7 +1003,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "L": L, "G": G, "K": K, "F": F, "H": H, "B": B,
-                   "positives_per_sample": w.m, "dh_mode": args.mode,
+                   "positives_per_sample": w.m, "dh_mode": args.mode, "slot_order": slot_order,
                    "step": "haste_step: fused forward + BCE gradient + dW + dh"},
         "useful_tflops": round(useful_tflops, 2),
         "pct_bf16_peak": round(100 * useful_tflops / BF16_PEAK_TFLOPS, 2),
