@@ -558,16 +558,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                 hv[hf][u] = ldg16(a.hT + ((uint32_t)gc[u] * (uint32_t)a.Bp +
                                           (uint32_t)(b0 + 16 * hf + 8 * (lane & 1))));
     };
-    // dZ half tile: piece pc = lane + 64 u is batch row b0 + 16 hf + pc / DCH, labels 8 (pc % DCH) ..
+    // dZ half tile.  Up to G = 32 a row's labels fit one contraction step,
+    // and lane (row r16, q) loads labels 8q .. +8 of batch row b0 + 16 hf +
+    // r16 straight into the A layout of P = dZ W_k (no pass through LDS;
+    // 345 -> 328 us for the given-dZ call at 3M).  At G = 64 (two steps)
+    // piece pc = lane + 64 u is batch row b0 + 16 hf + pc / DCH, labels
+    // 8 (pc % DCH) .., staged through the tile: each row's 128 bytes then
+    // come from 8 neighbouring lanes (the direct form measured 1 % slower).
+    constexpr bool DZ_DIRECT = (G <= 32);
+    static_assert(LAB || !DZ_DIRECT || (NDH == 1 && KSG == 1), "one dZ piece per half");
     auto load_dz = [&](int64_t kk, u32x4_t (&dv)[2][NDH]) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int u = 0; u < NDH; ++u) {
-                const int pc = lane + 64 * u;
-                const int64_t b = b0 + 16 * hf + pc / DCH;
                 dv[hf][u] = u32x4_t{0u, 0u, 0u, 0u};
-                if (pc < 16 * DCH && b < a.B) dv[hf][u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
+                if constexpr (DZ_DIRECT) {
+                    const int64_t b = b0 + 16 * hf + r16;
+                    if (q < DCH && b < a.B) dv[hf][u] = ldg16(a.dZ + b * L + kk * G + 8 * q);
+                } else {
+                    const int pc = lane + 64 * u;
+                    const int64_t b = b0 + 16 * hf + pc / DCH;
+                    if (pc < 16 * DCH && b < a.B) dv[hf][u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
+                }
             }
     };
 
@@ -637,9 +650,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         }
         u32x4_t ahi[2][KSG], alo[2][KSG];
         if constexpr (!LAB) {
-            // A of P = given dZ rows, one 16-row half at a time through the tile
+            // A of P = given dZ rows: as loaded, or one 16-row half at a time
+            // through the tile
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
+                if constexpr (DZ_DIRECT) {
+                    ahi[hf][0] = c.d[hf][0];
+                    alo[hf][0] = u32x4_t{0u, 0u, 0u, 0u};
+                    continue;
+                }
 #pragma unroll
                 for (int u = 0; u < NDH; ++u) {
                     const int pc = lane + 64 * u;
