@@ -173,14 +173,24 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
         for (int u = 0; u < NHP; ++u)
             hv[u] = ldg16(a.hT + ((uint32_t)gc[u] * (uint32_t)a.Bp + (uint32_t)(b0 + 8 * (lane & 1))));
     };
-    // dZ tile: piece pc = lane + 64 u is batch row b0 + pc / DCH, labels 8 (pc % DCH) .. +8
+    // dZ tile.  Up to G = 32, lane (row r16, q) loads labels 8q .. +8 of batch
+    // row b0 + r16 straight into the A layout of P = dZ W_k; at G = 64 piece
+    // pc = lane + 64 u is batch row b0 + pc / DCH, labels 8 (pc % DCH) .. +8,
+    // staged through the tile (as in the 32-row kernel).
+    constexpr bool DZ_DIRECT = (G <= 32);
+    static_assert(LAB || !DZ_DIRECT || (NDP == 1 && KSG == 1), "one dZ piece per lane");
     auto load_dz = [&](int64_t kk, u32x4_t (&dv)[NDP]) {
 #pragma unroll
         for (int u = 0; u < NDP; ++u) {
-            const int pc = lane + 64 * u;
-            const int64_t b = b0 + pc / DCH;
             dv[u] = u32x4_t{0u, 0u, 0u, 0u};
-            if (pc < 16 * DCH && b < a.B) dv[u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
+            if constexpr (DZ_DIRECT) {
+                const int64_t b = b0 + r16;
+                if (q < DCH && b < a.B) dv[u] = ldg16(a.dZ + b * L + kk * G + 8 * q);
+            } else {
+                const int pc = lane + 64 * u;
+                const int64_t b = b0 + pc / DCH;
+                if (pc < 16 * DCH && b < a.B) dv[u] = ldg16(a.dZ + b * L + kk * G + 8 * (pc % DCH));
+            }
         }
     };
 
@@ -243,7 +253,10 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
             for (int t = 0; t < NT; ++t)
                 p[t] = zero4();
             u32x4_t ahi[KSG], alo[KSG];
-            if constexpr (!LAB) {
+            if constexpr (!LAB && DZ_DIRECT) {
+                ahi[0] = c.d[0];
+                alo[0] = u32x4_t{0u, 0u, 0u, 0u};
+            } else if constexpr (!LAB) {
 #pragma unroll
                 for (int u = 0; u < NDP; ++u) {
                     const int pc = lane + 64 * u;
