@@ -58,7 +58,12 @@ def test_layer_on_ordered_slots_matches_oracle():
     base = {k: to_host(v) for k, v in hs.step(h, idx, W, rp, col, scale, G, mode="det", want_Z=True).items()
             if v is not None}
     perm = hs.order_slots(idx, W, G, perm=True)
-    idx_o, W_o, p = to_host(idx), to_host(W), to_host(perm).astype(np.int64)
+    # the reference orders the generator's arrays itself; the GPU's order must equal it
+    idx_o, W_o, p = O.oracle_order_slots(d["idx"], d["W"], G)
+    p = p.astype(np.int64)
+    assert_exact(to_host(idx), idx_o, "ordered idx")
+    assert_exact(to_host(W), W_o, "ordered W")
+    assert_exact(to_host(perm), p, "perm")
     ref = O.oracle_step(d["h"], idx_o, W_o, d["y_rowptr"], d["y_col"], scale, G)
     for mode in ("det", "atomic"):
         out = {k: to_host(v) for k, v in hs.step(h, idx, W, rp, col, scale, G, mode=mode).items() if v is not None}
