@@ -7,12 +7,13 @@
 // along the label dimension).
 //
 // Work split: a workgroup owns one chunk of consecutive groups and one tile
-// of kDhRows batch rows, and accumulates P_k = dZ_k[tile] W_k for its groups
-// into an LDS accumulator acc[kDhRows][H] (scatter-add into columns I_k).
+// of batch rows (16, or 32 in k_group_dh32), and accumulates
+// P_k = dZ_k[tile] W_k for its groups into an LDS accumulator acc[rows][H]
+// (scatter-add into columns I_k).
 // The workgroups of one chunk sit on one XCD (workgroup ids are dealt to the
 // XCDs round-robin), so the W_k they all read is fetched from HBM once and
-// served to the other batch tiles from that XCD's L2.  Each wave takes every
-// fourth group of the chunk.
+// served to the other batch tiles from that XCD's L2.  With NW waves per
+// workgroup, each wave takes every NW-th group of the chunk.
 //
 // dZ comes either from the caller (bf16) or is recomputed from the logits
 // of the tile (Z_k^T = W_k H_k^T on matrix cores) and the labels, as
