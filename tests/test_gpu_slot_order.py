@@ -89,3 +89,47 @@ def test_order_slots_full_size_sampled():
     assert_exact(got[rows], want, "3M idx sampled rows")
     assert_exact(gp[rows], wp, "3M perm sampled rows")
     assert hs.validate_idx(di, w.H) == 0
+
+
+def test_any_slot_order_every_call():
+    """Index rows in an arbitrary order (W's columns moved along): forward,
+    dW, dh (both modes) and the fused pass match the oracle on the same
+    permuted inputs, and rewiring yields the same sets and weights as it does
+    from sorted rows."""
+    B, H, K, G, F = 77, 300, 40, 32, 64
+    rng = np.random.default_rng(41)
+    idx = sorted_subsets(K, F, H, 12, 0)
+    W = normal_bf16(K * G * F, 0.5, 12, 2).reshape(K * G, F)
+    h = normal_bf16(B * H, 1.0, 12, 1).reshape(B, H)
+    dZ = normal_bf16(B * K * G, 1.0, 12, 3).reshape(B, K * G)
+    sig = np.stack([rng.permutation(F) for _ in range(K)])
+    idx_p = np.ascontiguousarray(np.take_along_axis(idx, sig, 1)).astype(np.int32)
+    W_p = np.ascontiguousarray(np.take_along_axis(W, np.repeat(sig, G, 0), 1))
+    # two distinct positive labels per sample, sorted (CSR)
+    col = np.concatenate([np.sort(rng.choice(K * G, 2, replace=False)) for _ in range(B)]).astype(np.int32)
+    rp = np.arange(0, 2 * B + 1, 2, dtype=np.int32)
+    dh_, dp = to_dev_bf16(h), to_dev_i32(idx_p)
+    dw_, dz_ = to_dev_bf16(W_p), to_dev_bf16(dZ)
+    assert hs.validate_idx(dp, H) == 0
+    assert_parity(to_host(hs.fwd(dh_, dp, dw_, G)), O.oracle_fwd(h, idx_p, W_p, G), "Z, shuffled slots")
+    assert_parity(to_host(hs.bwd_w(dh_, dp, dz_, G)), O.oracle_bwd_w(h, idx_p, dZ, G), "dW, shuffled slots")
+    ref_dh = O.oracle_bwd_h(dZ, idx_p, W_p, G, H)
+    for mode in ("det", "atomic"):
+        assert_parity(to_host(hs.bwd_h(dz_, dp, dw_, G, H, mode=mode)), ref_dh, f"dh {mode}, shuffled slots")
+    ref = O.oracle_step(h, idx_p, W_p, rp, col, 1.0 / B, G)
+    out = hs.step(dh_, dp, dw_, to_dev_i32(rp), to_dev_i32(col), 1.0 / B, G, mode="det")
+    assert_parity(to_host(out["dW"]), ref["dW"], "step dW, shuffled slots")
+    assert_parity(to_host(out["dh"]), ref["dh"], "step dh, shuffled slots")
+    # rewiring: small-integer inputs make every score exact, so the selection
+    # is the same whatever the order of the input row
+    hi = (rng.integers(-3, 4, size=(B, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    zi = (rng.integers(-3, 4, size=(B, K * G)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wi = (rng.integers(-3, 4, size=(K * G, F)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wi_p = np.ascontiguousarray(np.take_along_axis(wi, np.repeat(sig, G, 0), 1))
+    r_sorted = hs.rewire(to_dev_bf16(hi), to_dev_bf16(zi), to_dev_i32(idx), to_dev_bf16(wi), G, 9)
+    r_shuf = hs.rewire(to_dev_bf16(hi), to_dev_bf16(zi), to_dev_i32(idx_p), to_dev_bf16(wi_p), G, 9)
+    assert_exact(to_host(r_shuf["idx"]), to_host(r_sorted["idx"]), "rewired index rows")
+    assert_exact(to_host(r_shuf["W"]), to_host(r_sorted["W"]), "rewired weights")
+    want_idx, want_W, _, _ = O.oracle_rewire(hi, zi, idx_p, wi_p, 9, G)
+    assert_exact(to_host(r_shuf["idx"]), want_idx, "rewired index rows vs oracle")
+    assert_exact(to_host(r_shuf["W"]), want_W, "rewired weights vs oracle")
