@@ -1025,6 +1025,7 @@ def main():
         dW = torch.empty(L, F, dtype=torch.float32, device=dev)
         dh = torch.empty(B, H, dtype=torch.float32, device=dev)
         wsx = torch.empty(max(256, hs.workspace_size("step", B, H, K, G, F, "det")), dtype=torch.uint8, device=dev)
+        out16 = {"dW": torch.empty(L, F, dtype=torch.bfloat16, device=dev), "dh": dh, "Z": None, "loss": None}
         reps = 10
         calls = {
             "fwd": lambda: hs.fwd(h, idx, W, G, Z=Z, workspace=wsx),
@@ -1034,6 +1035,9 @@ def main():
             "step_other_mode": lambda: hs.step(h, idx, W, rp, col, s, G,
                                                mode="det" if args.mode == "atomic" else "atomic",
                                                out=out, workspace=wsx),
+            # the same step with dW stored as bf16 (haste_step_bf16dw): half the dW write
+            "step_bf16_dw": lambda: hs.step(h, idx, W, rp, col, s, G, mode=args.mode, out=out16, workspace=wsx,
+                                            dw_bf16=True),
             "fixed_fwd": lambda: hs.fixed_fwd(h, idx1, W, Z=Z, workspace=wsx),
             "fixed_bwd_w": lambda: hs.fixed_bwd_w(h, idx1, dZ, dW=dW, workspace=wsx),
             "fixed_bwd_h_atomic": lambda: hs.fixed_bwd_h(dZ, idx1, W, H, mode="atomic", dh=dh, workspace=wsx),
@@ -1045,6 +1049,14 @@ def main():
         extra["fwd_bce_us"] = round(1e3 * t_fwd_bce, 2)
         unf = extra["fwd_bce_us"] + extra["bwd_w_us"] + extra["bwd_h_atomic_us"]
         extra["unfused_step_us"] = round(unf, 2)
+        extra["step_bf16_dw_samples_per_s"] = round(B / (extra["step_bf16_dw_us"] * 1e-6), 1)
+        for i in range(args.steps):
+            hs.step(h, idx, W, rp, col, s, G, mode=args.mode, out=out16, workspace=wsx, dw_bf16=True,
+                    events=ev.block(5 * i, 5))
+        torch.cuda.synchronize()
+        extra["step_bf16_dw_kernels_us"] = {"fwd_bce_dw_us": round(1e3 * avg(1, 2), 2),
+                                            "dh_us": round(1e3 * avg(2, 3), 2)}
+        log(f"[bench] step_bf16_dw phases: {extra['step_bf16_dw_kernels_us']}")
         extra["speedup_fwd_vs_G1"] = round(extra["fixed_fwd_us"] / extra["fwd_us"], 2)
         extra["speedup_bwd_vs_G1"] = round((extra["fixed_bwd_w_us"] + extra["fixed_bwd_h_atomic_us"]) /
                                            (extra["bwd_w_us"] + extra["bwd_h_atomic_us"]), 2)
@@ -1061,7 +1073,7 @@ def main():
         for name, nbytes in floors.items():
             extra[name + "_hbm_frac"] = round(nbytes / (extra[name + "_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         res["extra"] = extra
-        del Z, dW, dh, dZ, idx1
+        del Z, dW, dh, dZ, idx1, out16
         torch.cuda.empty_cache()
         if not args.no_dense:
             log("[bench] FLOPs-matched dense point")

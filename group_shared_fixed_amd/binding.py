@@ -33,6 +33,7 @@ SIGNATURES = {
     "haste_fwd_bce": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "haste_step": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P]),
     "haste_step_timed": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P, _P]),
+    "haste_step_bf16dw": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P, _S, _P, _P]),
     "haste_bwd_h_workspace_size": (_S, [_I, _I, _I, _I, _I, _M]),
     "haste_step_noalloc": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _M, _P]),
     "haste_fwd_bce_bwd": (_M, [_P, _P, _P, _P, _P, _F, _P, _P, _P, _M, _P, _S, _I, _I, _I, _I, _I, _P]),
@@ -244,23 +245,35 @@ def fwd_bce(h, idx, W, y_rowptr, y_col, scale, G, want_Z=False, want_loss=False,
 
 
 def step(h, idx, W, y_rowptr, y_col, scale, G, mode="atomic", want_Z=False, want_loss=False, out=None,
-         workspace=None, stream=None, events=None):
+         workspace=None, stream=None, events=None, dw_bf16=False):
     """Fused forward + BCE + dW + dh.  Returns dict(dW, dh, Z, loss).
 
-    events: optional ctypes array of 5 hipEvent_t handles (haste_step_timed)."""
+    events: optional ctypes array of 5 hipEvent_t handles (haste_step_timed).
+    dw_bf16: store dW as bf16 (haste_step_bf16dw; no Z output)."""
     torch = _torch()
     _bits(h); _bits(W); _i32(idx); _i32(y_rowptr); _i32(y_col)
     B, H = h.shape
     K, F = idx.shape
+    if dw_bf16 and (want_Z or (out is not None and out.get("Z") is not None)):
+        raise ValueError("the bf16-dW pass has no logits output")
     if out is None:
         out = {
-            "dW": torch.empty(K * G, F, dtype=torch.float32, device=h.device),
+            "dW": torch.empty(K * G, F, dtype=torch.bfloat16 if dw_bf16 else torch.float32, device=h.device),
             "dh": torch.empty(B, H, dtype=torch.float32, device=h.device),
             "Z": torch.empty(B, K * G, dtype=torch.float32, device=h.device) if want_Z else None,
             "loss": torch.empty(2, dtype=torch.float64, device=h.device) if want_loss else None,
         }
     m = DH_MODE[mode]
     ws, n = _workspace("step", B, H, K, G, F, m, h.device, workspace)
+    if dw_bf16:
+        _bits(out["dW"])
+        ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
+        _check("haste_step_bf16dw", lib().haste_step_bf16dw(
+            _ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]), _ptr(out["dh"]),
+            _ptr(out.get("loss")), B, H, K, G, F, m, _ptr(ws), ws.numel() if ws is not None else 0,
+            _stream(h, stream), ev))
+        _check_dh("haste_step_bf16dw", ws, stream)
+        return out
     args = (_ptr(h), _ptr(idx), _ptr(W), _ptr(y_rowptr), _ptr(y_col), float(scale), _ptr(out["dW"]),
             _ptr(out["dh"]), _ptr(out.get("Z")), _ptr(out.get("loss")), B, H, K, G, F, m, _ptr(ws),
             ws.numel() if ws is not None else 0, _stream(h, stream))

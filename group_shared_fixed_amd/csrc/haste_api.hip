@@ -280,9 +280,16 @@ namespace {
 // Host-side checks of the fused step (everything but the workspace).
 int step_check(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
                const int32_t* y_rowptr, const int32_t* y_col, float scale, const float* dW, const float* dh,
-               const float* Z, const double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode)
+               const float* Z, const double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+               const uint16_t* dW16 = nullptr)
 {
     const bool w8 = W8 != nullptr;
+    if (dW16) {
+        // bf16 weight gradient: bf16 weights, no logits output
+        if (w8 || Z) return HASTE_ERR_UNSUPPORTED;
+        if (!aligned16(dW16)) return HASTE_ERR_ALIGN;
+        dW = reinterpret_cast<const float*>(dW16);   // present; checked with the others below
+    }
     if (!h || !idx || !y_rowptr || !y_col || !dW || !dh || (w8 ? !wexp : !W)) return HASTE_ERR_NULL;
     if (w8 ? (!aligned16(W8) || !aligned16(wexp)) : !aligned16(W)) return HASTE_ERR_ALIGN;
     HASTE_TRY(check_shape(B, H, K, G, F, false));
@@ -299,10 +306,11 @@ int step_check(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, con
 int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const uint8_t* W8, const int32_t* wexp,
               const int32_t* y_rowptr, const int32_t* y_col, float scale, float* dW, float* dh, float* Z,
               double* loss, int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
-              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+              size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, uint16_t* dW16 = nullptr)
 {
     const bool w8 = W8 != nullptr;
-    HASTE_TRY(step_check(h, idx, W, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode));
+    HASTE_TRY(step_check(h, idx, W, W8, wexp, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
+                         dW16));
     const Layout l = layout(HASTE_OP_STEP, B, H, G, F, dh_mode);
     HASTE_TRY(check_ws(workspace, workspace_bytes, l.total));
     const bool det = dh_mode == HASTE_DH_DETERMINISTIC;
@@ -318,7 +326,8 @@ int step_impl(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, cons
     mark(1);
     FwdArgs a{};
     a.hT = hT; a.Bp = l.Bp; a.B = B; a.idx = idx; a.W = W; a.W8 = W8; a.wexp = wexp; a.K = K;
-    a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dW = dW; a.loss = loss;
+    a.y_rowptr = y_rowptr; a.y_col = y_col; a.scale = scale; a.Z = Z; a.dW = dW16 ? nullptr : dW; a.loss = loss;
+    a.dW16 = dW16;
     if (!launch_fwd((int)G, (int)F, STEP_DW, loss != nullptr, a, fwd_grid(K), stream, w8))
         return HASTE_ERR_UNSUPPORTED;
     mark(2);
@@ -344,6 +353,16 @@ int haste_step_timed(const haste_bf16* h, const int32_t* idx, const haste_bf16* 
     if (!W) return HASTE_ERR_NULL;
     return step_impl(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, dW, dh, Z, loss, B, H, K, G, F, dh_mode,
                      workspace, workspace_bytes, stream, events);
+}
+
+int haste_step_bf16dw(const haste_bf16* h, const int32_t* idx, const haste_bf16* W, const int32_t* y_rowptr,
+                      const int32_t* y_col, float scale, haste_bf16* dW, float* dh, double* loss, int64_t B,
+                      int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events)
+{
+    if (!W || !dW) return HASTE_ERR_NULL;
+    return step_impl(h, idx, W, nullptr, nullptr, y_rowptr, y_col, scale, nullptr, dh, nullptr, loss, B, H, K, G, F,
+                     dh_mode, workspace, workspace_bytes, stream, events, reinterpret_cast<uint16_t*>(dW));
 }
 
 int haste_step_w8_timed(const haste_bf16* h, const int32_t* idx, const uint8_t* W8, const int32_t* wexp,

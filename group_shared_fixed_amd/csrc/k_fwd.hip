@@ -59,9 +59,12 @@ __device__ __forceinline__ int tile_off(int f, int b)
 // WQ: the weights come as FP8 E4M3 codes with one power-of-two scale per
 // group (a.W8, a.wexp); they are widened to exact bf16 values on their way
 // into LDS, so the arithmetic is that of the bf16 kernel on those values.
-template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ = false>
+// DWB (fused step only): the weight gradient is stored as bf16 (a.dW16), each
+// value the fp32 accumulator rounded to nearest even: half the dW bytes.
+template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ = false, bool DWB = false>
 __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(FwdArgs a)
 {
+    static_assert(!DWB || MODE == STEP_DW, "a bf16 weight gradient is an option of the fused step");
     constexpr int NT = F / 16;    // 16-slot tiles (gather units, dW columns)
     constexpr int KS = F / 32;    // contraction steps of the forward product
     constexpr int GT = G / 16;    // 16-label tiles
@@ -211,12 +214,14 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                     const int u = lane + 64 * pp;
                     const int g = u / (F / 4), cc = u % (F / 4);
                     if (u < G * F / 4) {
-                        float* dst = a.dW + (pend_dw * G + g) * F + 4 * cc;
+                        const int64_t o = (pend_dw * G + g) * F + 4 * cc;
                         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
                         // plain stores in the fused step (non-temporal ones
                         // measured 13 % slower there); the standalone call streams
-                        if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(dst) = v;
-                        else stg_stream(dst, v);
+                        if constexpr (DWB)
+                            *reinterpret_cast<u32x2_t*>(a.dW16 + o) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                        else if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(a.dW + o) = v;
+                        else stg_stream(a.dW + o, v);
                     }
                 }
                 pend_dw = -1;
@@ -668,10 +673,13 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
                         const int u = lane + 64 * pp;
                         const int g = u / (F / 4), cc = u % (F / 4);
                         if (u < 4 * F) {
-                            float* dst = a.dW + (k * G + 16 * gt + g) * F + 4 * cc;
+                            const int64_t o = (k * G + 16 * gt + g) * F + 4 * cc;
                             const f32x4_t v = *reinterpret_cast<const f32x4_t*>(so + g * WST + 4 * cc);
-                            if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(dst) = v;
-                            else stg_stream(dst, v);
+                            if constexpr (DWB)
+                                *reinterpret_cast<u32x2_t*>(a.dW16 + o) =
+                                    u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                            else if constexpr (MODE == STEP_DW) *reinterpret_cast<f32x4_t*>(a.dW + o) = v;
+                            else stg_stream(a.dW + o, v);
                         }
                     }
                     wave_sync();
@@ -693,10 +701,10 @@ __global__ __launch_bounds__(256, fwd_min_blocks(G, F, MODE)) void k_group_fwd(F
     }
 }
 
-template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ>
+template <int G, int F, int MODE, bool LOSS, bool WZ, bool WQ, bool DWB = false>
 static void go(const FwdArgs& a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_group_fwd<G, F, MODE, LOSS, WZ, WQ>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_group_fwd<G, F, MODE, LOSS, WZ, WQ, DWB>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int G, int F, int MODE, bool WQ>
@@ -715,12 +723,20 @@ template <int G, int F>
 static bool launch_gf(int mode, bool loss, const FwdArgs& a, int grid, hipStream_t s, bool w8)
 {
     const bool wz = a.Z != nullptr;
+    if (w8 && a.dW16) return false;   // the bf16 weight gradient comes with bf16 weights only
     if (w8) {
         switch (mode) {
         case FWD_Z: go<G, F, FWD_Z, false, false, true>(a, grid, s); return true;
         case STEP_DW: go_bce<G, F, STEP_DW, true>(loss, wz, a, grid, s); return true;
         }
         return false;
+    }
+    if (a.dW16) {
+        // the fused step with a bf16 weight gradient (no logits output)
+        if (mode != STEP_DW || wz) return false;
+        if (loss) go<G, F, STEP_DW, true, false, false, true>(a, grid, s);
+        else go<G, F, STEP_DW, false, false, false, true>(a, grid, s);
+        return true;
     }
     switch (mode) {
     case FWD_Z: go<G, F, FWD_Z, false, false, false>(a, grid, s); return true;

@@ -31,6 +31,7 @@ struct FwdArgs {
     float* Z;             // B x L fp32 (FWD_Z; optional otherwise)
     uint16_t* dZ;         // B x L bf16 (FWD_BCE output, BWD_W input)
     float* dW;            // L x F fp32 (STEP_DW)
+    uint16_t* dW16;       // L x F bf16 (STEP_DW with a bf16 weight gradient, dW then unused)
     double* loss;         // 1 double, accumulated (optional)
     const uint8_t* W8;    // L x F FP8 E4M3 codes (FP8-weight variants, in place of W)
     const int32_t* wexp;  // K group exponents: weight = decode(code) * 2^wexp[k]

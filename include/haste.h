@@ -193,6 +193,21 @@ int haste_step_noalloc(const haste_bf16* h, const int32_t* idx, const haste_bf16
                        float* dW, float* dh, float* Z, double* loss,
                        int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode, hipStream_t stream);
 
+/* haste_step with the weight gradient dW_k = dZ_k^T H_k (HASTE page, the
+ * "gather-once + dense MMA kernel" section) stored as bf16: dW is L x F
+ * bf16, each value the fp32 accumulator of haste_step's dW rounded to nearest even
+ * (bitwise that rounding of haste_step's result), so the pass writes half
+ * the dW bytes.  The contractions are unchanged (fp32 accumulation, dZ split
+ * into bf16 hi + lo parts for the matrix cores), as is dh (fp32); the loss
+ * is optional as in haste_step; there is no logits output.  `events` may be
+ * NULL, else as in haste_step_timed.  bf16 weights only.  Workspace as
+ * haste_workspace_size(HASTE_OP_STEP, ...).  Same errors as haste_step. */
+int haste_step_bf16dw(const haste_bf16* h, const int32_t* idx, const haste_bf16* W,
+                      const int32_t* y_rowptr, const int32_t* y_col, float scale,
+                      haste_bf16* dW, float* dh, double* loss,
+                      int64_t B, int64_t H, int64_t K, int64_t G, int64_t F, int dh_mode,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* haste_step plus timing: when `events` is non-NULL, events[0..4] (created
  * by the caller) are recorded on `stream` at the phase boundaries of the
  * pass: [0] start, [1] after the feature-major copy of h and output

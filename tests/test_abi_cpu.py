@@ -96,6 +96,27 @@ def test_fwd_bce_bwd_rejects(L):
     assert _fbb(L, ws=P(0x100010)) == WS
 
 
+def _sbf(L, h=A, idx=A, W=A, rp=A, col=A, scale=0.5, dW=A, dh=A, loss=None, mode=1, ws=A, wsb=1 << 30,
+         B=128, H=768, K=100, G=32, F=64):
+    return L.haste_step_bf16dw(h, idx, W, rp, col, scale, dW, dh, loss, B, H, K, G, F, mode, ws, wsb, None, None)
+
+
+def test_step_bf16dw_rejects(L):
+    assert _sbf(L, W=None) == NULL
+    assert _sbf(L, dW=None) == NULL
+    assert _sbf(L, dh=None) == NULL
+    assert _sbf(L, h=None) == NULL
+    assert _sbf(L, B=0) == DIM
+    assert _sbf(L, scale=-1.0) == DIM
+    assert _sbf(L, G=8) == UNSUP
+    assert _sbf(L, F=48) == UNSUP
+    assert _sbf(L, mode=2) == UNSUP
+    assert _sbf(L, dW=MIS) == ALIGN
+    assert _sbf(L, ws=None) == WS
+    need = L.haste_workspace_size(4, 128, 768, 100, 32, 64, 1)
+    assert _sbf(L, wsb=need - 256) == WS
+
+
 def test_hT_offsets_stay_32_bit(L):
     """Shapes whose feature-major copy of h would pass 2^31 bytes (32-bit
     gather offsets) or need more than 65535 transpose workgroups are refused."""
