@@ -812,8 +812,22 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     // the same cell.  Each 16-row half of the accumulator has its own turn
     // counter; waves take turns on a half in the fixed order (batch of RPT
     // rounds, wave), RPT groups per turn in round order, so one wave can
-    // update one half while the next updates the other.
-    auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&col)[NT]) {
+    // update one half while the next updates the other.  With RPT groups per
+    // turn the offsets are those of half 0, formed before the turn wait: rows
+    // 16 + 4q of a column sit at its rows 4q with quad index bit 2 flipped,
+    // i.e. at offset XOR 16.
+    auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&off)[NT]) {
+        f32x4_t v[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            v[t] = *reinterpret_cast<const f32x4_t*>(acc + (off[t] ^ (16 * hf)));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4_t*>(acc + (off[t] ^ (16 * hf))) = v[t] + p[hf][t];
+    };
+    // (F > 64, a turn per round: offsets formed inside the turn, which
+    // measured faster there than the shared form above)
+    auto rmw_col = [&](int hf, const f32x4_t (&p)[2][NT], const int (&col)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -821,6 +835,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q)) = v[t] + p[hf][t];
+    };
+    auto offs = [&](const int (&col)[NT], int (&off)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            off[t] = acc32_off(col[t], 4 * q);
     };
     static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
@@ -839,7 +858,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const bool got = wait_turn(&sTurn[hf], turn, a.spins);
-                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, c.col);
+                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw_col(hf, p, c.col);
                     if (!got) sLost = 1;
                     pass_turn(&sTurn[hf], turn);
                 }
@@ -850,16 +869,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         int cl[RPT][NT];
         // every round of the batch runs (past the last round it only issues
         // clamped loads), so every path reaches the hand-off with the same
-        // loads outstanding; a round's columns are kept before the round
-        // after it overwrites its input set
+        // loads outstanding; a round's accumulator offsets are formed before
+        // the round after it overwrites its input set
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             In& c = (r % 2 == 0) ? sa : sb;
             In& n = (r % 2 == 0) ? sb : sa;
             round(rd + r, c, n, p[r]);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                cl[r][t] = c.col[t];
+            offs(c.col, cl[r]);
         }
         const int turn = (int)(NWV * i) + wv;
 #pragma unroll
