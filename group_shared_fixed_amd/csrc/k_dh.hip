@@ -383,14 +383,25 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     // read-add-write (rows 4q .. 4q+3 of column col[t] are adjacent).  Inside
     // one wave the index set is duplicate-free, so no two lanes touch the same
     // cell, and a later read-add-write of the wave sees its earlier writes.
-    auto rmw = [&](const f32x4_t (&p)[NT], const int (&col)[NT]) {
+    auto rmw = [&](const f32x4_t (&p)[NT], const int (&off)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc_off(col[t], 4 * q));
+            v[t] = *reinterpret_cast<const f32x4_t*>(acc + off[t]);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4_t*>(acc + acc_off(col[t], 4 * q)) = v[t] + p[t];
+            *reinterpret_cast<f32x4_t*>(acc + off[t]) = v[t] + p[t];
+    };
+    // The accumulator offsets are formed before the turn wait and consumed
+    // there by an empty asm statement: otherwise the compiler sinks their
+    // arithmetic into the held turn, where every instruction delays the
+    // waves queued behind.
+    auto offs = [&](const int (&col)[NT], int (&off)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            off[t] = acc_off(col[t], 4 * q);
+            asm volatile("" ::"v"(off[t]));
+        }
     };
 
     // Rounds in batches of RPT: the wave computes P for its groups of the
@@ -399,8 +410,8 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
     // updated by one wave at a time and in a fixed group order.  Every round
     // of a batch runs (past the last round it only issues clamped loads), so
     // every path reaches the hand-off with the same loads in flight; a
-    // round's columns are kept before the round after it overwrites its
-    // input set.
+    // round's accumulator offsets are formed before the round after it
+    // overwrites its input set.
     static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
     for (int64_t i = 0; i < nbatch; ++i) {
@@ -413,9 +424,11 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 Stage& n = (r % 2 == 0) ? sb : sa;
                 f32x4_t p[NT];
                 round(rd + r, c, n, p);
+                int off[NT];
+                offs(c.col, off);
                 const int turn = (int)(4 * (rd + r)) + wv;
                 const bool got = wait_turn(&sTurn, turn, a.spins);
-                if (got && kc0 + 4 * (rd + r) + wv < kc1) rmw(p, c.col);
+                if (got && kc0 + 4 * (rd + r) + wv < kc1) rmw(p, off);
                 if (!got) sLost = 1;
                 pass_turn(&sTurn, turn);
             }
@@ -427,9 +440,7 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
                 Stage& c = (r % 2 == 0) ? sa : sb;
                 Stage& n = (r % 2 == 0) ? sb : sa;
                 round(rd + r, c, n, p[r]);
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    cl[r][t] = c.col[t];
+                offs(c.col, cl[r]);
             }
             const int turn = (int)(4 * i) + wv;
             const bool got = wait_turn(&sTurn, turn, a.spins);
@@ -812,10 +823,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     // the same cell.  Each 16-row half of the accumulator has its own turn
     // counter; waves take turns on a half in the fixed order (batch of RPT
     // rounds, wave), RPT groups per turn in round order, so one wave can
-    // update one half while the next updates the other.  With RPT groups per
-    // turn the offsets are those of half 0, formed before the turn wait: rows
-    // 16 + 4q of a column sit at its rows 4q with quad index bit 2 flipped,
-    // i.e. at offset XOR 16.
+    // update one half while the next updates the other.  The offsets are
+    // those of half 0, formed before the turn wait: rows 16 + 4q of a column
+    // sit at its rows 4q with quad index bit 2 flipped, i.e. at offset XOR 16.
     auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&off)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
@@ -825,21 +835,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4_t*>(acc + (off[t] ^ (16 * hf))) = v[t] + p[hf][t];
     };
-    // (F > 64, a turn per round: offsets formed inside the turn, which
-    // measured faster there than the shared form above)
-    auto rmw_col = [&](int hf, const f32x4_t (&p)[2][NT], const int (&col)[NT]) {
-        f32x4_t v[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            v[t] = *reinterpret_cast<const f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q));
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4_t*>(acc + acc32_off(col[t], 16 * hf + 4 * q)) = v[t] + p[hf][t];
-    };
     auto offs = [&](const int (&col)[NT], int (&off)[NT]) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) {
             off[t] = acc32_off(col[t], 4 * q);
+            asm volatile("" ::"v"(off[t]));
+        }
     };
     static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
@@ -854,11 +855,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                 In& n = (r % 2 == 0) ? sb : sa;
                 f32x4_t p[2][NT];
                 round(rd + r, c, n, p);
+                int off[NT];
+                offs(c.col, off);
                 const int turn = (int)(NWV * (rd + r)) + wv;
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const bool got = wait_turn(&sTurn[hf], turn, a.spins);
-                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw_col(hf, p, c.col);
+                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, off);
                     if (!got) sLost = 1;
                     pass_turn(&sTurn[hf], turn);
                 }
