@@ -701,6 +701,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                 wave_sync();
             }
         } else {
+            // labels of this lane's two rows for this group, taken first: the
+            // cursor walk is a loop and the label correction a rare branch,
+            // and each ends a scheduling region
+            uint64_t mrow[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                mrow[hf] = cur[hf].take(k * G, G, a.y_col);
             // B of Z^T = H^T read transposed, per 16-row half: lane (row r16, q)
             // gets slots 32s + 8q + e
             u32x4_t bz[2][KSF];
@@ -735,44 +742,59 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                     for (int hf = 0; hf < 2; ++hf)
                         zt[hf][gt] = mfma16(wa, bz[hf][s], zt[hf][gt]);
                 }
+            // With up to two label tiles both halves' epilogues run side by
+            // side (one sigmoid region, one correction branch, both splits):
+            // 670K dh 570 -> 552 us.  At G = 64 (four label tiles, 252
+            // registers) that measured slower (490 -> 499 us at 8.6M), so the
+            // halves there run one after the other.
+            constexpr bool JOINT = (GT <= 2);
+            constexpr int NH = JOINT ? 2 : 1;   // halves per pass
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                // labels of this row for this group
-                const uint64_t mrow = cur[hf].take(k * G, G, a.y_col);
-                const bool brow_ok = b0 + 16 * hf + r16 < a.B;
-                float dz[GT][4];
+            for (int h0 = 0; h0 < 2; h0 += NH) {
                 // s * sigmoid(z) = 1 / ((1 + e^-z) / s); e^-z = +inf gives 0
+                float dz[NH][GT][4];
 #pragma unroll
-                for (int gt = 0; gt < GT; ++gt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float t = __builtin_amdgcn_exp2f(-zt[hf][gt][i] * kLog2e);
-                        dz[gt][i] = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
-                    }
-                if (__any(mrow != 0) || !tile_full) {   // rare: positives or padding rows
+                for (int u = 0; u < NH; ++u)
 #pragma unroll
                     for (int gt = 0; gt < GT; ++gt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            float d = dz[gt][i];
-                            if ((mrow >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
-                            dz[gt][i] = brow_ok ? d : 0.f;
+                            const float t = __builtin_amdgcn_exp2f(-zt[h0 + u][gt][i] * kLog2e);
+                            dz[u][gt][i] = __builtin_amdgcn_rcpf(fmaf(t, inv_s, inv_s));
                         }
+                const uint64_t many = JOINT ? (mrow[0] | mrow[1]) : mrow[h0];
+                if (__any(many != 0) || !tile_full) {   // rare: positives or padding rows
+#pragma unroll
+                    for (int u = 0; u < NH; ++u) {
+                        const int hf = h0 + u;
+                        const bool brow_ok = b0 + 16 * hf + r16 < a.B;
+#pragma unroll
+                        for (int gt = 0; gt < GT; ++gt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                float d = dz[u][gt][i];
+                                if ((mrow[hf] >> (16 * gt + 4 * q + i)) & 1ull) d -= scale;
+                                dz[u][gt][i] = brow_ok ? d : 0.f;
+                            }
+                    }
                 }
                 // contraction element e of step s <-> label 32s + 16*(e/4) + 4q + e%4
 #pragma unroll
-                for (int s = 0; s < KSG; ++s) {
-                    const int g0 = 2 * s, g1 = 2 * s + 1;
-                    const float x0 = dz[g0][0], x1 = dz[g0][1], x2 = dz[g0][2], x3 = dz[g0][3];
-                    const float y0 = g1 < GT ? dz[g1 < GT ? g1 : 0][0] : 0.f;
-                    const float y1 = g1 < GT ? dz[g1 < GT ? g1 : 0][1] : 0.f;
-                    const float y2 = g1 < GT ? dz[g1 < GT ? g1 : 0][2] : 0.f;
-                    const float y3 = g1 < GT ? dz[g1 < GT ? g1 : 0][3] : 0.f;
-                    { const u32x2_t _p = split_pair(x0, x1); ahi[hf][s][0] = _p[0]; alo[hf][s][0] = _p[1]; }
-                    { const u32x2_t _p = split_pair(x2, x3); ahi[hf][s][1] = _p[0]; alo[hf][s][1] = _p[1]; }
-                    { const u32x2_t _p = split_pair(y0, y1); ahi[hf][s][2] = _p[0]; alo[hf][s][2] = _p[1]; }
-                    { const u32x2_t _p = split_pair(y2, y3); ahi[hf][s][3] = _p[0]; alo[hf][s][3] = _p[1]; }
-                }
+                for (int u = 0; u < NH; ++u)
+#pragma unroll
+                    for (int s = 0; s < KSG; ++s) {
+                        const int hf = h0 + u;
+                        const int g0 = 2 * s, g1 = 2 * s + 1;
+                        const float x0 = dz[u][g0][0], x1 = dz[u][g0][1], x2 = dz[u][g0][2], x3 = dz[u][g0][3];
+                        const float y0 = g1 < GT ? dz[u][g1 < GT ? g1 : 0][0] : 0.f;
+                        const float y1 = g1 < GT ? dz[u][g1 < GT ? g1 : 0][1] : 0.f;
+                        const float y2 = g1 < GT ? dz[u][g1 < GT ? g1 : 0][2] : 0.f;
+                        const float y3 = g1 < GT ? dz[u][g1 < GT ? g1 : 0][3] : 0.f;
+                        { const u32x2_t _p = split_pair(x0, x1); ahi[hf][s][0] = _p[0]; alo[hf][s][0] = _p[1]; }
+                        { const u32x2_t _p = split_pair(x2, x3); ahi[hf][s][1] = _p[0]; alo[hf][s][1] = _p[1]; }
+                        { const u32x2_t _p = split_pair(y0, y1); ahi[hf][s][2] = _p[0]; alo[hf][s][2] = _p[1]; }
+                        { const u32x2_t _p = split_pair(y2, y3); ahi[hf][s][3] = _p[0]; alo[hf][s][3] = _p[1]; }
+                    }
             }
         }
         // P = dZ_tile W_k with B = W_k read transposed (shared by both tiles):
