@@ -191,6 +191,26 @@ __device__ __forceinline__ int swz(int r, int nchunks)
     return s & (nchunks - 1);
 }
 
+// Visits the cells i = start, start + step, ... < rows * width of a row-major
+// rows x width tile as (row, column) pairs, with one division for the start
+// and additions after it (a per-element division by a run-time width costs
+// a long instruction sequence, and 64-bit ones far more).
+template <typename Fn>
+__device__ __forceinline__ void for_cells(int rows, int width, int start, int step, Fn&& fn)
+{
+    int r = start / width, j = start - r * width;
+    const int sr = step / width, sj = step - sr * width;
+    while (r < rows) {
+        fn(r, j);
+        r += sr;
+        j += sj;
+        if (j >= width) {
+            j -= width;
+            ++r;
+        }
+    }
+}
+
 // Walks one sample's sorted positive-label list (a CSR row of the 0/1 label
 // matrix) alongside groups visited in increasing order.  take(lo, G) returns
 // the G-bit mask of positives with ids in [lo, lo + G) and skips ids below lo.

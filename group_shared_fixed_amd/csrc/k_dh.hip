@@ -458,14 +458,12 @@ __global__ __launch_bounds__(256, 2) void k_group_dh(DhArgs a)
 
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
-        for (int64_t i = threadIdx.x; i < R * H; i += 256)
-            dst[i] = acc[acc_off((int)(i % H), (int)(i / H))];
+        for_cells(R, (int)H, threadIdx.x, 256, [&](int r, int j) { dst[(int64_t)r * H + j] = acc[acc_off(j, r)]; });
         if (threadIdx.x == 0) a.flags[blockIdx.x] = sLost;
     } else {
-        for (int64_t i = threadIdx.x; i < R * H; i += 256) {
-            const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc_off((int)(i % H), (int)(i / H))]);
-        }
+        for_cells(R, (int)H, threadIdx.x, 256, [&](int r, int j) {
+            if (b0 + r < a.B) unsafeAtomicAdd(&a.dh[(b0 + r) * H + j], acc[acc_off(j, r)]);
+        });
         if (threadIdx.x == 0 && sLost) *a.status = 1;
     }
 }
@@ -921,14 +919,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
-        for (int64_t i = threadIdx.x; i < R * H; i += NT_)
-            dst[i] = acc[acc32_off((int)(i % H), (int)(i / H))];
+        for_cells(R, (int)H, threadIdx.x, NT_, [&](int r, int j) { dst[(int64_t)r * H + j] = acc[acc32_off(j, r)]; });
         if (threadIdx.x == 0) a.flags[blockIdx.x] = sLost;
     } else {
-        for (int64_t i = threadIdx.x; i < R * H; i += NT_) {
-            const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[acc32_off((int)(i % H), (int)(i / H))]);
-        }
+        for_cells(R, (int)H, threadIdx.x, NT_, [&](int r, int j) {
+            if (b0 + r < a.B) unsafeAtomicAdd(&a.dh[(b0 + r) * H + j], acc[acc32_off(j, r)]);
+        });
         if (threadIdx.x == 0 && sLost) *a.status = 1;
     }
 }

@@ -387,13 +387,11 @@ __global__ __launch_bounds__(64 * kFixDhWaves, 1) void k_fixed_bwd_h(FixedArgs a
     __syncthreads();
     if constexpr (DET) {
         float* dst = a.part + ((int64_t)chunk * a.ntiles * R + b0) * H;
-        for (int64_t i = threadIdx.x; i < R * H; i += NTH)
-            dst[i] = acc[fix_acc_off((int)(i % H), (int)(i / H))];
+        for_cells(R, (int)H, threadIdx.x, NTH, [&](int r, int j) { dst[(int64_t)r * H + j] = acc[fix_acc_off(j, r)]; });
     } else {
-        for (int64_t i = threadIdx.x; i < R * H; i += NTH) {
-            const int64_t b = b0 + i / H;
-            if (b < a.B) unsafeAtomicAdd(&a.dh[b * H + (i % H)], acc[fix_acc_off((int)(i % H), (int)(i / H))]);
-        }
+        for_cells(R, (int)H, threadIdx.x, NTH, [&](int r, int j) {
+            if (b0 + r < a.B) unsafeAtomicAdd(&a.dh[(b0 + r) * H + j], acc[fix_acc_off(j, r)]);
+        });
     }
 }
 
