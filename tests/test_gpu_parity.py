@@ -180,8 +180,9 @@ def test_step_without_optional_outputs(name):
 
 # f64_h1024: the G = 1 dh accumulator (16 x (1024 + 4) fp32) passes the
 # default 64 KB of dynamic LDS
+# f32_h131: an odd H, so the accumulator flush wraps rows at every step
 FIXED = {"f32": (64, 256, 700, 32), "f64_b77": (77, 768, 333, 64), "f128_b256": (256, 768, 150, 128),
-         "f64_b1": (1, 96, 65, 64), "f64_h1024": (40, 1024, 200, 64)}
+         "f64_b1": (1, 96, 65, 64), "f64_h1024": (40, 1024, 200, 64), "f32_h131": (37, 131, 90, 32)}
 
 
 @pytest.mark.parametrize("mode", ["atomic", "det"])
