@@ -29,6 +29,8 @@
 // The turn waits are bounded; a wave whose wait gives up skips its update and
 // the workgroup reports it (DhArgs::status / DhArgs::flags), so a broken
 // hand-off is an error the caller sees, never a silent wrong result.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -499,13 +501,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     constexpr int DCH = G / 8;                   // 16-byte chunks of a dZ row
     constexpr int NDH = (16 * DCH + 63) / 64;    // dZ pieces per lane per 16-row half
     static_assert(G * F <= 4096 && F <= 128, "per-wave tiles sized for the 32-row workgroup");
-    static_assert(NWV * (G * F + (LAB ? F * 16 : 16 * G)) * 2 + 32 * 768 * 4 + 8 <= 160 * 1024,
+    static_assert(NWV * (G * F + (LAB ? F * 16 : 16 * G)) * 2 + 32 * 768 * 4 + 20 <= 160 * 1024,
                   "per-wave tiles and a 32 x 768 accumulator fit in LDS");
 
     extern __shared__ __attribute__((aligned(16))) float acc[];   // acc[j * 32 + row], quads swizzled
     __shared__ __attribute__((aligned(16))) uint16_t sW[NWV][G * F];
     __shared__ __attribute__((aligned(16))) uint16_t sT[NWV][LAB ? F * 16 : 16 * G];   // one 16-row half
-    __shared__ int sTurn[2];                  // accumulator hand-off counters, one per 16-row half
+    __shared__ int sTurn[4];                  // accumulator hand-off counters: per 16-row half, or per 8-row quarter (F > 64)
     __shared__ int sLost;                     // a turn wait gave up
 
     const int lane = threadIdx.x & 63;
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 
     for (int64_t i = threadIdx.x; i < R * H; i += NT_)
         acc[i] = 0.f;
-    if (threadIdx.x < 2) sTurn[threadIdx.x] = 0;
+    if (threadIdx.x < 4) sTurn[threadIdx.x] = 0;
     if (threadIdx.x == 0) sLost = 0;
 
     // each lane's A rows: b0 + r16 (tile 0) and b0 + 16 + r16 (tile 1)
@@ -846,6 +848,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     // update one half while the next updates the other.  The offsets are
     // those of half 0, formed before the turn wait: rows 16 + 4q of a column
     // sit at its rows 4q with quad index bit 2 flipped, i.e. at offset XOR 16.
+    // The offsets are consumed there by an empty asm statement: otherwise the
+    // compiler sinks their arithmetic into the held turns, where every
+    // instruction delays the waves queued behind.
     auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&off)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
@@ -862,6 +867,53 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             asm volatile("" ::"v"(off[t]));
         }
     };
+    // Wide tiles (F = 128: eight result tiles per half and round) hold a half
+    // twice as long per turn, and there the turns are split once more: four
+    // 8-row quarters, each with its own counter, so up to four waves update
+    // the accumulator at once.  quarters() pairs result tiles 2u and 2u + 1
+    // and swaps the upper 32 lanes of the first with the lower 32 of the
+    // second (v_permlane32_swap): tile 2u then holds rows 0 .. 7 and tile
+    // 2u + 1 rows 8 .. 15 of the pair's 32 columns, lane (r16, q) covering
+    // column slot 16 (2u + q / 2) + r16 and rows 8 qa + 4 (q % 2) .. +3, so
+    // every read-add-write instruction of a quarter has all 64 lanes.  The
+    // rows of quarter qt sit at those of quarter 0 with offset XOR 8 qt.
+    auto quarters = [&](f32x4_t (&p)[2][NT]) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int u = 0; u < NT / 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // The elements go in by value: __builtin_bit_cast of an
+                    // indexed vector element reads element 0 in this clang.
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[hf][2 * u][e]),
+                                                                     __float_as_uint(p[hf][2 * u + 1][e]), false, false);
+                    p[hf][2 * u][e] = __uint_as_float((uint32_t)sw[0]);
+                    p[hf][2 * u + 1][e] = __uint_as_float((uint32_t)sw[1]);
+                }
+    };
+    auto rmw_q = [&](auto QT, const f32x4_t (&p)[2][NT], const int (&off)[NT / 2]) {
+        constexpr int qt = decltype(QT)::value, hf = qt >> 1, qa = qt & 1;
+        f32x4_t v[NT / 2];
+#pragma unroll
+        for (int u = 0; u < NT / 2; ++u)
+            v[u] = *reinterpret_cast<const f32x4_t*>(acc + (off[u] ^ (8 * qt)));
+#pragma unroll
+        for (int u = 0; u < NT / 2; ++u)
+            *reinterpret_cast<f32x4_t*>(acc + (off[u] ^ (8 * qt))) = v[u] + p[hf][2 * u + qa];
+    };
+    auto offs_q = [&](const int (&col)[NT], int (&off)[NT / 2]) {
+        // (the lane's column is blended from both values: a select between
+        // the two array elements would take their address and move the whole
+        // input set out of registers)
+        const int lo = -(int)(q < 2);
+#pragma unroll
+        for (int u = 0; u < NT / 2; ++u) {
+            const int c0 = col[2 * u], c1 = col[2 * u + 1];
+            off[u] = acc32_off((c0 & lo) | (c1 & ~lo), 4 * (q & 1));
+            asm volatile("" ::"v"(off[u]));
+        }
+    };
     static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
     for (int64_t i = 0; i < nbatch; ++i) {
@@ -869,22 +921,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         if constexpr (F > 64) {
             // wide tiles (P of both halves is 2 F / 16 result tiles): each
             // round's P goes into the accumulator at once, a turn per round
+            // and quarter
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 In& c = (r % 2 == 0) ? sa : sb;
                 In& n = (r % 2 == 0) ? sb : sa;
                 f32x4_t p[2][NT];
                 round(rd + r, c, n, p);
-                int off[NT];
-                offs(c.col, off);
+                quarters(p);
+                int off[NT / 2];
+                offs_q(c.col, off);
                 const int turn = (int)(NWV * (rd + r)) + wv;
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const bool got = wait_turn(&sTurn[hf], turn, a.spins);
-                    if (got && kc0 + NWV * (rd + r) + wv < kc1) rmw(hf, p, off);
+                const bool live = kc0 + NWV * (rd + r) + wv < kc1;
+                auto chain = [&](auto QT) {
+                    constexpr int qt = decltype(QT)::value;
+                    const bool got = wait_turn(&sTurn[qt], turn, a.spins);
+                    if (got && live) rmw_q(QT, p, off);
                     if (!got) sLost = 1;
-                    pass_turn(&sTurn[hf], turn);
-                }
+                    pass_turn(&sTurn[qt], turn);
+                };
+                chain(std::integral_constant<int, 0>{});
+                chain(std::integral_constant<int, 1>{});
+                chain(std::integral_constant<int, 2>{});
+                chain(std::integral_constant<int, 3>{});
             }
             continue;
         }
@@ -992,7 +1051,7 @@ static void launch_kern(dim3 grid, dim3 blk, size_t lds, hipStream_t s, const Dh
 // gathered tile of F = 128).
 constexpr int dh32_waves(int G, int F, int src)
 {
-    const int n = (160 * 1024 - 32 * 768 * 4 - 8) / ((G * F + (src == DH_FROM_LABELS ? F * 16 : 16 * G)) * 2);
+    const int n = (160 * 1024 - 32 * 768 * 4 - 20) / ((G * F + (src == DH_FROM_LABELS ? F * 16 : 16 * G)) * 2);
     return n < 8 ? n : 8;
 }
 
