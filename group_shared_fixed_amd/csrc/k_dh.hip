@@ -482,10 +482,11 @@ __device__ __forceinline__ int acc32_off(int j, int r)
 // group for both 16-row matrix-core tiles, so the W_k staging, its
 // transposed operand reads, the index loads and the accumulator addressing
 // serve twice the rows.  One workgroup per CU (accumulator 32 x H fp32 plus
-// per-wave tiles); used when G*F <= 2048, F <= 64 and H <= 768.  A wave
-// takes its turn on the accumulator once per RPT rounds (RPT groups per
-// turn): four when dZ is given (the turn hand-offs bound that kernel, and
-// its per-group registers are few), two when the logits are recomputed.
+// per-wave tiles); used when G*F <= 2048 (or G = 64 with F = 64) and
+// H <= 768.  With F <= 64 a wave takes its turn on the accumulator once per
+// RPT rounds (RPT groups per turn): four when dZ is given (the turn
+// hand-offs bound that kernel, and its per-group registers are few), two
+// when the logits are recomputed; with F = 128 once per round.
 template <int G, int F, int SRC, bool DET, int NWV, int RPT, bool WQ = false>
 __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
 {

@@ -84,12 +84,10 @@ bool launch_fwd(int G, int F, int mode, bool loss, const FwdArgs& a, int grid, h
 // Whether the 32-row feature-gradient kernel exists for (G, F) and the dZ
 // source: its per-wave tiles, for at least six waves, and a 32 x 768
 // accumulator fit in LDS without spilling registers (G F <= 2048, or G = 64
-// with F = 64).  With a given dZ it is built for F <= 64 only (at F = 128
-// the 16-row kernel is faster: its P tiles leave room for two groups per
-// accumulator turn).
-constexpr bool dh32_fits(int G, int F, bool from_labels)
+// with F = 64), for either dZ source.
+constexpr bool dh32_fits(int G, int F, bool /*from_labels*/)
 {
-    return (G * F <= 2048 || (G * F == 4096 && F == 64)) && (F <= 64 || from_labels);
+    return (G * F <= 2048 || (G * F == 4096 && F == 64));
 }
 // Batch rows per feature-gradient workgroup: 32 (six to eight waves, one
 // workgroup per CU) where that kernel exists and H <= 768, else 16.
