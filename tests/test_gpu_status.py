@@ -13,8 +13,10 @@ from synthetic import normal_bf16, sorted_subsets, zipf_labels
 
 pytestmark = pytest.mark.gpu
 
-# (B, H, K, G, F): the 32-row kernel (G = 32, F = 64) and the 16-row one (H > 768)
-SHAPES = [(77, 768, 900, 32, 64), (50, 1024, 300, 16, 64)]
+# (B, H, K, G, F): the 32-row kernel with a turn counter per 16-row half
+# (G = 32, F = 64) and per 8-row quarter (G = 16, F = 128), and the 16-row
+# kernel (H > 768)
+SHAPES = [(77, 768, 900, 32, 64), (45, 640, 400, 16, 128), (50, 1024, 300, 16, 64)]
 
 
 def inputs(B, H, K, G, F, seed):
