@@ -916,6 +916,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
         }
     };
     static_assert(RPT % 2 == 0, "rounds alternate between the two input sets");
+    // Let the prologue's loads land here (vmcnt(0); the other counters are
+    // left alone): the compiler's wait insertion otherwise carries some of
+    // them as possibly outstanding into the loop and waits for them inside
+    // the held turns, whose scratch registers they were loaded into.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     const int64_t nbatch = (nrounds + RPT - 1) / RPT;
     for (int64_t i = 0; i < nbatch; ++i) {
         const int64_t rd = RPT * i;
