@@ -502,10 +502,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     constexpr int DCH = G / 8;                   // 16-byte chunks of a dZ row
     constexpr int NDH = (16 * DCH + 63) / 64;    // dZ pieces per lane per 16-row half
     static_assert(G * F <= 4096 && F <= 128, "per-wave tiles sized for the 32-row workgroup");
-    static_assert(NWV * (G * F + (LAB ? F * 16 : 16 * G)) * 2 + 32 * 768 * 4 + 20 <= 160 * 1024,
+    static_assert(NWV * (G * F + (LAB ? F * 16 : 16 * G)) * 2 + 32 * 768 * 4 + 160 <= 160 * 1024,
                   "per-wave tiles and a 32 x 768 accumulator fit in LDS");
 
-    extern __shared__ __attribute__((aligned(16))) float acc[];   // acc[j * 32 + row], quads swizzled
+    extern __shared__ __attribute__((aligned(128))) float acc[];  // acc[j * 32 + row], quads swizzled;
+                                                                  // 128-byte aligned for the address flips below
     __shared__ __attribute__((aligned(16))) uint16_t sW[NWV][G * F];
     __shared__ __attribute__((aligned(16))) uint16_t sT[NWV][LAB ? F * 16 : 16 * G];   // one 16-row half
     __shared__ int sTurn[4];                  // accumulator hand-off counters: per 16-row half, or per 8-row quarter (F > 64)
@@ -847,24 +848,30 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
     // counter; waves take turns on a half in the fixed order (batch of RPT
     // rounds, wave), RPT groups per turn in round order, so one wave can
     // update one half while the next updates the other.  The offsets are
-    // those of half 0, formed before the turn wait: rows 16 + 4q of a column
-    // sit at its rows 4q with quad index bit 2 flipped, i.e. at offset XOR 16.
-    // The offsets are consumed there by an empty asm statement: otherwise the
-    // compiler sinks their arithmetic into the held turns, where every
-    // instruction delays the waves queued behind.
-    auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const int (&off)[NT]) {
+    // the LDS byte addresses of half 0, formed before the turn wait: rows
+    // 16 + 4q of a column sit at its rows 4q with quad index bit 2 flipped,
+    // i.e. at float offset XOR 16, byte address XOR 64 (the accumulator
+    // starts on a 128-byte boundary, so the flip never carries into the
+    // base).  The addresses are consumed there by an empty asm statement:
+    // otherwise the compiler sinks their arithmetic into the held turns,
+    // where every instruction delays the waves queued behind; as finished
+    // byte addresses the turn of half 0 starts with its LDS reads.
+    using lds_f4 = __attribute__((address_space(3))) f32x4_t;
+    const uint32_t accb = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)acc;
+    auto cell = [](uint32_t ad) { return (lds_f4*)(size_t)ad; };
+    auto rmw = [&](int hf, const f32x4_t (&p)[2][NT], const uint32_t (&off)[NT]) {
         f32x4_t v[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            v[t] = *reinterpret_cast<const f32x4_t*>(acc + (off[t] ^ (16 * hf)));
+            v[t] = *cell(off[t] ^ (64u * hf));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4_t*>(acc + (off[t] ^ (16 * hf))) = v[t] + p[hf][t];
+            *cell(off[t] ^ (64u * hf)) = v[t] + p[hf][t];
     };
-    auto offs = [&](const int (&col)[NT], int (&off)[NT]) {
+    auto offs = [&](const int (&col)[NT], uint32_t (&off)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            off[t] = acc32_off(col[t], 4 * q);
+            off[t] = accb + 4u * (uint32_t)acc32_off(col[t], 4 * q);
             asm volatile("" ::"v"(off[t]));
         }
     };
@@ -954,7 +961,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             continue;
         }
         f32x4_t p[RPT][2][NT];
-        int cl[RPT][NT];
+        uint32_t cl[RPT][NT];
         // every round of the batch runs (past the last round it only issues
         // clamped loads), so every path reaches the hand-off with the same
         // loads outstanding; a round's accumulator offsets are formed before
@@ -1052,12 +1059,14 @@ static void launch_kern(dim3 grid, dim3 blk, size_t lds, hipStream_t s, const Dh
     hipLaunchKernelGGL(Kern, grid, blk, lds, s, a);
 }
 
-// Waves of the 32-row kernel: eight, or seven where eight sets of per-wave
-// tiles and the 32 x H accumulator would not fit in LDS (G F = 2048 with the
-// gathered tile of F = 128).
+// Waves of the 32-row kernel: eight, or fewer where eight sets of per-wave
+// tiles and the 32 x H accumulator would not fit in LDS (seven at G F = 2048
+// with the gathered tile of F = 128, six at G = 64, F = 64).  160 bytes cover
+// the hand-off counters (20) and the accumulator's 128-byte alignment (up to
+// 124 bytes of padding after the static arrays).
 constexpr int dh32_waves(int G, int F, int src)
 {
-    const int n = (160 * 1024 - 32 * 768 * 4 - 20) / ((G * F + (src == DH_FROM_LABELS ? F * 16 : 16 * G)) * 2);
+    const int n = (160 * 1024 - 32 * 768 * 4 - 160) / ((G * F + (src == DH_FROM_LABELS ? F * 16 : 16 * G)) * 2);
     return n < 8 ? n : 8;
 }
 
