@@ -22,7 +22,9 @@
 // Reduction of the per-workgroup accumulators:
 //   atomic:        fp32 atomic adds into dh (order of the adds varies);
 //   deterministic: the waves of a workgroup add their P_k into acc in a
-//                  fixed order (turns handed on through a counter in LDS),
+//                  fixed order (turns handed on through counters in LDS:
+//                  one in k_group_dh; in k_group_dh32 one per 16-row half
+//                  of the accumulator, or per 8-row quarter at F = 128),
 //                  each workgroup writes its accumulator to its own slice of
 //                  a partials buffer, and a second kernel sums the slices in
 //                  chunk order: bitwise reproducible for a fixed shape.
