@@ -175,12 +175,16 @@ __device__ __forceinline__ bool wait_turn(const int* t, int v, int spins)
     return got;
 }
 
-__device__ __forceinline__ void pass_turn(int* t, int v)
+// pass_turn_to stores a successor value the caller formed ahead of the turn
+// (in a vector register), so the held turn ends with the store itself.
+__device__ __forceinline__ void pass_turn_to(int* t, int next)
 {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __hip_atomic_store(t, v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(t, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __builtin_amdgcn_s_setprio(0);
 }
+
+__device__ __forceinline__ void pass_turn(int* t, int v) { pass_turn_to(t, v + 1); }
 
 // XOR swizzle of 16-byte chunks inside a row of an LDS tile so that the
 // transposing 2-byte writes and the 16-byte matrix-operand reads of one

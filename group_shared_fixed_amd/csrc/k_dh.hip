@@ -976,6 +976,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             offs(c.col, cl[r]);
         }
         const int turn = (int)(NWV * i) + wv;
+        int nxt = turn + 1;   // the counters' next value, in a vector register before the turns
+        asm volatile("" : "+v"(nxt));
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const bool got = wait_turn(&sTurn[hf], turn, a.spins);
@@ -986,7 +988,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
             } else {
                 sLost = 1;
             }
-            pass_turn(&sTurn[hf], turn);
+            pass_turn_to(&sTurn[hf], nxt);
         }
     }
     __syncthreads();
