@@ -947,13 +947,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_group_dh32(DhArgs a)
                 int off[NT / 2];
                 offs_q(c.col, off);
                 const int turn = (int)(NWV * (rd + r)) + wv;
+                int nxt = turn + 1;
+                asm volatile("" : "+v"(nxt));
                 const bool live = kc0 + NWV * (rd + r) + wv < kc1;
                 auto chain = [&](auto QT) {
                     constexpr int qt = decltype(QT)::value;
                     const bool got = wait_turn(&sTurn[qt], turn, a.spins);
                     if (got && live) rmw_q(QT, p, off);
                     if (!got) sLost = 1;
-                    pass_turn(&sTurn[qt], turn);
+                    pass_turn_to(&sTurn[qt], nxt);
                 };
                 chain(std::integral_constant<int, 0>{});
                 chain(std::integral_constant<int, 1>{});
